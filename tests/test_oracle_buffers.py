@@ -1,0 +1,304 @@
+"""Buffer-level pins of the oracle: the library's semantics on host arrays.
+
+The buffer functions (commit, verify, fused replay+verify) are checked against
+the item-level recurrence (itself pinned in test_oracle_pins.py) through
+properties the pages state: the RecoverSSM identity (a commit of the verify's
+own records rebuilds the recurrence state), fused = commit followed by verify,
+the deferred protocol's end-to-end claim (fused over a prior window's records
+continues the recurrence), and the no-op rules (null slot, record row < 0,
+n = 0, slots nobody names).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+K = V = 128
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        return W.bits(t)
+    return t.detach().cpu().contiguous().numpy().copy()
+
+
+def _bf(bits):
+    return oracle.bf16_to_f64(bits)
+
+
+def _item_inputs(win, b, h, T, a_log, dtb, lb):
+    """Double-precision per-item inputs from a window (decays, normalised keys
+    and beta computed by the oracle's own pinned scalar steps)."""
+    q = _bf(_np(win.q))[b * T:(b + 1) * T, h]
+    kr = _bf(_np(win.k))[b * T:(b + 1) * T, h]
+    v = _bf(_np(win.v))[b * T:(b + 1) * T, h]
+    g = _bf(_np(win.raw_g))[b * T:(b + 1) * T, h]
+    rb = _bf(_np(win.raw_beta))[b * T:(b + 1) * T, h]
+    kn = np.stack([oracle.knorm(kr[t]) for t in range(T)])
+    d = np.array([[oracle.decay(g[t, c], a_log[h], dtb[h, c], lb) for c in range(K)]
+                  for t in range(T)])
+    beta = np.array([oracle.sigmoid(x) for x in rb])
+    return q, kn, v, d, beta
+
+
+def _case(seed=11, H=2, B=3, T=4, RQ=4, slots=6, **kw):
+    c = W.small_fused_case(seed, H, B, T, RQ, slots, **kw)
+    return c
+
+
+def _run_verify(c, H, B, T, RQ, fused, state=None, corr=None, kg=None, pending=None,
+                win=None, rows="given"):
+    state = _np(c["state"]) if state is None else state
+    corr = _np(c["corr"]) if corr is None else corr
+    kg = _np(c["kg"]) if kg is None else kg
+    win = c["window"] if win is None else win
+    out = np.full((B * T, H * V), 0x7FFF, dtype=np.uint16)  # a sentinel pattern
+    args = dict(heads=H, tokens=T, batch=B, q=_np(win.q), k=_np(win.k), v=_np(win.v),
+                raw_g=_np(win.raw_g), raw_beta=_np(win.raw_beta),
+                a_log=_np(c["a_log"])[0], dt_bias=_np(c["dt_bias"])[0],
+                lower_bound=W.LOWER_BOUND, state=state, state_slot_stride=H * V * K,
+                state_indices=_np(c["state_indices"]), corr=corr, kg=kg,
+                record_tokens=RQ, out=out,
+                record_rows=_np(c["record_rows"]) if rows == "given" else rows)
+    if fused:
+        oracle.fused_replay_verify(pending=_np(c["pending"]) if pending is None else pending,
+                                   **args)
+    else:
+        oracle.verify(**args)
+    return state, corr, kg, out
+
+
+def test_verify_writes_records_and_not_state():
+    H, B, T, RQ = 2, 3, 4, 6
+    c = _case(H=H, B=B, T=T, RQ=RQ, no_record_rows=(2,))
+    s0 = _np(c["state"])
+    corr0, kg0 = _np(c["corr"]), _np(c["kg"])
+    state, corr, kg, out = _run_verify(c, H, B, T, RQ, fused=False)
+    assert np.array_equal(state, s0)  # the checkpoint is never written
+    rows = _np(c["record_rows"])
+    win = c["window"]
+    k_bits, g_bits = _np(win.k), _np(win.raw_g)
+    for b in range(B):
+        r = rows[b]
+        if r < 0:
+            continue
+        for h in range(H):
+            for t in range(T):
+                tok = b * T + t
+                assert np.array_equal(kg[r, h, t, :K], k_bits[tok, h])
+                assert np.array_equal(kg[r, h, t, K:], g_bits[tok, h])
+            # tokens past T in the record keep their old contents
+            assert np.array_equal(kg[r, h, T:], kg0[r, h, T:])
+            assert np.array_equal(corr[r, h, T:], corr0[r, h, T:])
+    # the row with record row -1 wrote nothing, but produced outputs
+    written = {int(r) for r in rows if r >= 0}
+    for r in range(corr.shape[0]):
+        if r not in written:
+            assert np.array_equal(corr[r], corr0[r]) and np.array_equal(kg[r], kg0[r])
+    assert not np.any(out == 0x7FFF)
+
+
+def test_verify_matches_item_recurrence():
+    H, B, T, RQ = 2, 2, 5, 5
+    c = _case(seed=12, H=H, B=B, T=T, RQ=RQ, slots=4)
+    state, corr, kg, out = _run_verify(c, H, B, T, RQ, fused=False)
+    a_log, dtb = _np(c["a_log"])[0], _np(c["dt_bias"])[0]
+    slots, rows = _np(c["state_indices"]), _np(c["record_rows"])
+    for b in range(B):
+        for h in range(H):
+            S0 = state.reshape(-1, H, V, K)[slots[b], h].astype(np.float64)
+            q, kn, v, d, beta = _item_inputs(c["window"], b, h, T, a_log, dtb, W.LOWER_BOUND)
+            o, u, _ = oracle.verify_seq(S0, q, kn, v, d, beta)
+            assert np.array_equal(out[b * T:(b + 1) * T, h * V:(h + 1) * V], oracle.round_bf16(o))
+            assert np.array_equal(corr[rows[b], h, :T], u.astype(np.float32))
+
+
+def test_null_slot_rows_output_zero_and_touch_nothing():
+    H, B, T, RQ = 2, 3, 3, 4
+    c = _case(seed=13, H=H, B=B, T=T, RQ=RQ, null_rows=(1,))
+    s0, corr0, kg0 = _np(c["state"]), _np(c["corr"]), _np(c["kg"])
+    for fused in (False, True):
+        state, corr, kg, out = _run_verify(c, H, B, T, RQ, fused=fused, state=s0.copy(),
+                                           corr=corr0.copy(), kg=kg0.copy())
+        assert np.all(out[T:2 * T] == 0)
+        r = _np(c["record_rows"])[1]
+        assert np.array_equal(corr[r], corr0[r]) and np.array_equal(kg[r], kg0[r])
+
+
+def test_commit_buffer_rules_and_identity():
+    """Verify writes the records; the commit of n of them (FP32 state, source =
+    destination) equals the recurrence after n tokens (RecoverSSM identity,
+    through FP32-stored corrections); n = 0 and null rows write nothing; a slot
+    nobody names is unchanged."""
+    H, B, T, RQ = 2, 3, 4, 4
+    c = _case(seed=14, H=H, B=B, T=T, RQ=RQ, slots=6)
+    s0 = _np(c["state"])
+    state, corr, kg, out = _run_verify(c, H, B, T, RQ, fused=False, state=s0.copy())
+    slots, rows = _np(c["state_indices"]), _np(c["record_rows"])
+    lens = np.array([3, 0, 4], np.int32)
+    st = state.copy()
+    oracle.commit(heads=H, window=RQ, batch=B, state_bf16=False, state_layers=[st],
+                  state_slot_strides=[H * V * K], corr_layers=[corr],
+                  corr_row_strides=[H * RQ * V], kg_layers=[kg],
+                  kg_row_strides=[H * RQ * 2 * K], a_log=_np(c["a_log"]),
+                  dt_bias=_np(c["dt_bias"]), sources=slots, commit_lens=lens,
+                  destinations=slots, record_rows=rows, lower_bound=W.LOWER_BOUND)
+    pages0 = s0.reshape(-1, H, V, K)
+    pages = st.reshape(-1, H, V, K)
+    a_log, dtb = _np(c["a_log"])[0], _np(c["dt_bias"])[0]
+    for b in range(B):
+        for h in range(H):
+            if lens[b] == 0:
+                assert np.array_equal(pages[slots[b], h], pages0[slots[b], h])
+                continue
+            q, kn, v, d, beta = _item_inputs(c["window"], b, h, T, a_log, dtb, W.LOWER_BOUND)
+            n = int(lens[b])
+            _, _, Sn = oracle.verify_seq(pages0[slots[b], h].astype(np.float64), q[:n],
+                                         kn[:n], v[:n], d[:n], beta[:n])
+            assert np.allclose(pages[slots[b], h], Sn, rtol=1e-5, atol=1e-6)
+    others = set(range(6)) - set(int(s) for s in slots)
+    for s in others:
+        assert np.array_equal(pages[s], pages0[s])
+
+
+def test_commit_align_boundary_and_bf16():
+    """Align: the boundary slot gets the commit of min(m, n) tokens, the
+    destination that of n; both BF16, rounded once from FP64 (commit page,
+    module docstring and KdaCommit.kernel)."""
+    H, B, Q = 2, 3, 8
+    g = W._gen(21)
+    corr, kgr = W.draw_records(g, B, H, Q)
+    corr, kgr = _np(corr), _np(kgr)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    a_log, dtb = _np(a_log), _np(dtb)
+    S = 10
+    stride = H * V * K + 64
+    pool = W.bits(W.draw_state(5, S * stride, torch.bfloat16))
+    src = np.array([1, 2, 3], np.int32)
+    dst = np.array([4, 5, 6], np.int32)
+    bnd = np.array([7, 0, 8], np.int32)
+    lens = np.array([6, 5, 3], np.int32)
+    blen = np.array([2, 3, 7], np.int32)  # row 2: m > n -> S_n
+    st = pool.copy()
+    oracle.commit(heads=H, window=Q, batch=B, state_bf16=True, state_layers=[st],
+                  state_slot_strides=[stride], corr_layers=[corr],
+                  corr_row_strides=[H * Q * V], kg_layers=[kgr],
+                  kg_row_strides=[H * Q * 2 * K], a_log=a_log, dt_bias=dtb, sources=src,
+                  commit_lens=lens, destinations=dst, boundaries=bnd, boundary_lens=blen,
+                  lower_bound=W.LOWER_BOUND)
+
+    def page(arr, slot, h):
+        return arr[slot * stride + h * V * K: slot * stride + (h + 1) * V * K].reshape(V, K)
+
+    for b in range(B):
+        for h in range(H):
+            S0 = _bf(page(pool, src[b], h))
+            kn = np.stack([oracle.knorm(_bf(kgr[b, h, t, :K])) for t in range(Q)])
+            d = np.array([[oracle.decay(x, a_log[0, h], dtb[0, h, c], W.LOWER_BOUND)
+                           for c, x in enumerate(_bf(kgr[b, h, t, K:]))] for t in range(Q)])
+            u = corr[b, h].astype(np.float64)
+            n = int(lens[b])
+            want = oracle.round_bf16(oracle.commit_closed(S0, u, kn, d, n))
+            assert np.array_equal(page(st, dst[b], h), want)
+            if bnd[b] > 0:
+                m = min(int(blen[b]), n)
+                want_b = oracle.round_bf16(oracle.commit_closed(S0, u, kn, d, m))
+                assert np.array_equal(page(st, bnd[b], h), want_b)
+            # the source page is unchanged (source != destination)
+            assert np.array_equal(page(st, src[b], h), page(pool, src[b], h))
+    assert np.array_equal(page(st, 9, 0), page(pool, 9, 0))  # unnamed slot
+
+
+def test_fused_equals_commit_then_verify():
+    """fused(S0, records, pending) = commit(pending of the records) in place,
+    then verify, with the records rewritten (fused page, module docstring)."""
+    H, B, T, RQ = 2, 4, 3, 5
+    c = _case(seed=15, H=H, B=B, T=T, RQ=RQ, slots=8, null_rows=(3,), no_record_rows=(2,))
+    s0, corr0, kg0 = _np(c["state"]), _np(c["corr"]), _np(c["kg"])
+    pending = np.array([2, 0, 4, 5], np.int32)  # row with rec=-1 ignores its pending
+    rows = _np(c["record_rows"])
+    pend_by_row = np.zeros(B, np.int32)
+    for b in range(B):
+        if rows[b] >= 0:
+            pend_by_row[rows[b]] = pending[b]
+    st_f, corr_f, kg_f, out_f = _run_verify(c, H, B, T, RQ, True, state=s0.copy(),
+                                            corr=corr0.copy(), kg=kg0.copy(),
+                                            pending=pend_by_row)
+    # composition: commit with lens = pending (0 for rec < 0), then verify
+    slots = _np(c["state_indices"])
+    lens = np.array([pend_by_row[rows[b]] if rows[b] >= 0 else 0 for b in range(B)], np.int32)
+    st_c = s0.copy()
+    oracle.commit(heads=H, window=RQ, batch=B, state_bf16=False, state_layers=[st_c],
+                  state_slot_strides=[H * V * K], corr_layers=[corr0],
+                  corr_row_strides=[H * RQ * V], kg_layers=[kg0],
+                  kg_row_strides=[H * RQ * 2 * K], a_log=_np(c["a_log"]),
+                  dt_bias=_np(c["dt_bias"]), sources=slots, commit_lens=lens,
+                  destinations=slots, record_rows=rows, lower_bound=W.LOWER_BOUND)
+    st_v, corr_v, kg_v, out_v = _run_verify(c, H, B, T, RQ, False, state=st_c.copy(),
+                                            corr=corr0.copy(), kg=kg0.copy())
+    assert np.array_equal(st_f, st_c)  # the same FP32 rounding of S_n
+    assert np.array_equal(kg_f, kg_v)
+    assert np.allclose(corr_f, corr_v, rtol=1e-6, atol=1e-7)
+    diff = np.abs(out_f.view(np.int16).astype(np.int32) - out_v.view(np.int16).astype(np.int32))
+    assert diff.max() <= 1
+    # n = 0 items keep their page bit for bit
+    pages0 = s0.reshape(-1, H, V, K)
+    pages = st_f.reshape(-1, H, V, K)
+    assert np.array_equal(pages[slots[1]], pages0[slots[1]])
+    assert np.array_equal(pages[slots[2]], pages0[slots[2]])  # rec < 0: no replay
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 4])
+def test_deferred_protocol_continues_the_recurrence(n):
+    """Verify a prior window (records written), defer n accepted tokens, then
+    fused-verify a new window: its outputs equal the stock recurrence run over
+    the first n prior tokens followed by the new window, from the original
+    checkpoint (fused page, module docstring; kernels page, defer step)."""
+    H, B, T, RQ = 2, 2, 4, 4
+    c = _case(seed=16, H=H, B=B, T=T, RQ=RQ, slots=4)
+    prior = W.draw_window(W._gen(99), B, T, H)
+    s0 = _np(c["state"])
+    state, corr, kg, _ = _run_verify(c, H, B, T, RQ, False, state=s0.copy(), win=prior)
+    slots, rows = _np(c["state_indices"]), _np(c["record_rows"])
+    pending = np.zeros(B, np.int32)
+    lens = np.full(B, n, np.int32)
+    oracle.defer(slots, lens, rows, pending)
+    assert np.all(lens == 0)
+    state, corr, kg, out = _run_verify(c, H, B, T, RQ, True, state=state, corr=corr, kg=kg,
+                                       pending=pending)
+    a_log, dtb = _np(c["a_log"])[0], _np(c["dt_bias"])[0]
+    for b in range(B):
+        for h in range(H):
+            p = _item_inputs(prior, b, h, T, a_log, dtb, W.LOWER_BOUND)
+            x = _item_inputs(c["window"], b, h, T, a_log, dtb, W.LOWER_BOUND)
+            seq = [np.concatenate([p[i][:n], x[i]]) for i in range(5)]
+            S0 = s0.reshape(-1, H, V, K)[slots[b], h].astype(np.float64)
+            o, _, _ = oracle.verify_seq(S0, *seq)
+            got = out[b * T:(b + 1) * T, h * V:(h + 1) * V]
+            want = oracle.round_bf16(o[n:])
+            diff = np.abs(got.view(np.int16).astype(np.int32) - want.view(np.int16).astype(np.int32))
+            assert diff.max() <= 1  # FP32-stored corrections, then one BF16 rounding
+
+
+def test_fused_pending_clamped_to_record_capacity():
+    """A pending count above the records' capacity replays RQ tokens; a negative
+    one replays none (fused page, KdaFused.kernel: n clamped to [0, RQ])."""
+    H, B, T, RQ = 1, 2, 2, 3
+    c = _case(seed=17, H=H, B=B, T=T, RQ=RQ, slots=4)
+    s0, corr0, kg0 = _np(c["state"]), _np(c["corr"]), _np(c["kg"])
+    rows = _np(c["record_rows"])
+
+    def run(p0, p1):
+        pend = np.zeros(B, np.int32)
+        pend[rows[0]], pend[rows[1]] = p0, p1
+        return _run_verify(c, H, B, T, RQ, True, state=s0.copy(), corr=corr0.copy(),
+                           kg=kg0.copy(), pending=pend)
+
+    hi = run(RQ + 5, -4)
+    ref = run(RQ, 0)
+    for a, b in zip(hi, ref):
+        assert np.array_equal(a, b)
+    mid = run(RQ - 1, 1)
+    assert not np.array_equal(mid[0], ref[0])  # the clamp point matters

@@ -1,0 +1,219 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) KDA gated delta-rule state-update library
+ * (libkda.so): the bounded gate decay, the RecoverSSM commit, the stock verify,
+ * the fused replay+verify, and the two plan steps of deferred RecoverSSM.
+ *
+ * Sources are the vLLM API pages on Kimi-K3 KDA, cited by page title:
+ *   [commit page]  vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.commit
+ *   [kernels page] vllm.models.kimi_k3.nvidia.specialized_decode.recoverssm.kernels
+ *   [fused page]   vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.fused
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Dimensions are fixed: K = V = 128 key and value channels per head. A head's
+ *    state page is S[v][c] (row v = value channel, column c = key channel),
+ *    128 x 128, contiguous; a slot holds H pages: state[slot][h][v][c].
+ *  - Every pointer argument is a DEVICE pointer unless it says "host". Buffers
+ *    are owned by the caller; the library allocates nothing, keeps no state
+ *    between calls and never synchronises: work is enqueued on `stream` (a
+ *    hipStream_t, NULL for the default stream) and the call returns.
+ *  - BF16 tensors are passed as uint16_t bit patterns; index arrays are int32.
+ *  - Return value: KDA_OK (0), KDA_EINVAL for a bad argument (nothing is
+ *    launched), KDA_ELAUNCH when the HIP launch fails. kda_last_error() gives a
+ *    message for the last failure on the calling thread.
+ *  - Validation reads no device memory (the calls can be captured into a HIP
+ *    graph). Device-side index data (slots, lengths, record rows, pending
+ *    counts) is not range-checked: slots must lie in the pool, record rows in
+ *    the record arrays. Requests of one call must not share a destination,
+ *    boundary or record row, and no request's source may be another request's
+ *    destination (their pages would race).
+ *  - Base pointers, strides and row pitches must keep every 16-byte vector
+ *    access aligned; the library rejects them otherwise.
+ *  - A slot index <= null_slot means "no state" (padding rows).
+ *  - batch == 0 (or tokens == 0 for kda_decay) returns KDA_OK with no launch.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+#define KDA_OK 0
+#define KDA_EINVAL 1
+#define KDA_ELAUNCH 2
+
+#define KDA_STATE_F32 0
+#define KDA_STATE_BF16 1
+
+#define KDA_HEAD_DIM 128
+#define KDA_MAX_WINDOW 8
+
+/* The message of the last failed call on this thread ("" after a success). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+/*
+ * kda_decay — the bounded KDA gate decay, elementwise ([fused page],
+ * KdaFused.decay):
+ *     out[i][h][c] = exp(lower_bound * sigmoid(exp(a_log[h]) * (raw_g[i][h][c] + dt_bias[h][c])))
+ *
+ *   raw_g     BF16 [tokens][heads][128], contiguous
+ *   a_log     FP32 [heads]
+ *   dt_bias   FP32 [heads][128]
+ *   out       FP32 [tokens][heads][128], contiguous; written
+ * lower_bound must be finite. Computed in FP32 (hardware exp2-based exp).
+ */
+int kda_decay(const uint16_t* raw_g, int64_t tokens, int heads, const float* a_log,
+              const float* dt_bias, float lower_bound, float* out, void* stream);
+
+/*
+ * kda_commit — the RecoverSSM commit ([commit page], module docstring, KdaCommit
+ * class docstring and kernel): for every (layer l, request b, head h) item with
+ * n = commit_lens[b] > 0, sources[b] > null_slot, destinations[b] > null_slot and
+ * a record row r >= 0 (r = record_rows[b], or b when record_rows is NULL):
+ *
+ *     S_n = S_0 diag(D_n) + sum_{t<n} u_t (kn_t * P_t)^T,
+ *     D_n = prod_{s<n} d_s,   P_t = prod_{t<s<n} d_s,
+ *
+ * with S_0 the source page, u_t the recorded corrections, kn_t the recorded raw
+ * keys L2-normalised (eps 1e-6 inside the root), d_t the decays of the recorded
+ * raw gates under a_log[l][h], dt_bias[l][h][:]. S_n is written to the
+ * destination page (which may equal the source: an in-place commit). n is
+ * capped at `window`. When boundaries and boundary_lens are given (align) and
+ * m = boundary_lens[b] > 0 with boundaries[b] > null_slot, S_m (m capped at n)
+ * is also written to the boundary page. Items that are not live write nothing.
+ * Arithmetic is FP32; stores round to the state dtype (BF16: nearest-even).
+ *
+ *   layers, heads        L >= 1 and H >= 1
+ *   window               Q in 1..8: the records' token capacity and the cap on n
+ *   batch                B requests
+ *   state_dtype          KDA_STATE_F32 or KDA_STATE_BF16
+ *   state_addrs          HOST array [L] of device base addresses of each layer's
+ *                        state pool [slots][H][128][128]
+ *   state_slot_strides   HOST array [L]: elements between slots (>= H*128*128)
+ *   corr_addrs           HOST array [L]: FP32 corrections [rows][H][Q][128]
+ *   corr_row_strides     HOST array [L]: elements between record rows (>= H*Q*128)
+ *   kg_addrs             HOST array [L]: BF16 key/gate records [rows][H][Q][256]
+ *                        (raw key in 0..127, raw gate in 128..255)
+ *   kg_row_strides       HOST array [L]: elements between record rows (>= H*Q*256)
+ *   a_log                FP32 [L][H];  dt_bias  FP32 [L][H][128]
+ *   sources, commit_lens, destinations      int32 [B]
+ *   boundaries, boundary_lens               int32 [B], or both NULL (align off)
+ *   record_rows          int32 [B] or NULL (row b)
+ *   lower_bound          finite;  null_slot  the padding slot id (usually 0)
+ * Any number of layers is accepted (the library launches them in chunks).
+ */
+int kda_commit(int layers, int heads, int window, int batch, int state_dtype,
+               const uint64_t* state_addrs, const int64_t* state_slot_strides,
+               const uint64_t* corr_addrs, const int64_t* corr_row_strides,
+               const uint64_t* kg_addrs, const int64_t* kg_row_strides,
+               const float* a_log, const float* dt_bias, const int32_t* sources,
+               const int32_t* commit_lens, const int32_t* destinations,
+               const int32_t* boundaries, const int32_t* boundary_lens,
+               const int32_t* record_rows, float lower_bound, int null_slot, void* stream);
+
+/*
+ * kda_verify — the stock RecoverSSM verify of a window of `tokens` new tokens
+ * per request, which never writes the checkpoint ([kernels page],
+ * kda_recoverssm_verify; the recurrence of the [fused page] module docstring).
+ * For every (request b, head h) with slot = state_indices[b]:
+ *  - slot <= null_slot: out rows of the item are zero; nothing else is written;
+ *  - otherwise, from S = state page (FP32), for t < tokens:
+ *        S <- S diag(d_t);  u_t = beta_t (v_t - S kn_t);  S <- S + u_t kn_t^T;  o_t = S q_t
+ *    computed in the chunked (WY) form from the unmodified page; o_t -> out
+ *    (BF16); with beta_t = sigmoid(raw_beta), kn_t the L2-normalised key, q_t
+ *    used as given;
+ *  - record row r = record_rows[b] (or b when NULL); r >= 0: corrections
+ *    [r][h][t][:] = u_t (FP32), key/gate [r][h][t][0:128] = k_t bits and
+ *    [128:256] = raw gate bits, for t < tokens (later record tokens untouched).
+ *
+ *   heads, tokens (1..8), batch
+ *   q, k, raw_g          BF16 [batch*tokens][heads][128], contiguous
+ *   v                    BF16 [batch*tokens][heads][128], contiguous
+ *   raw_beta             BF16 [batch*tokens][heads]
+ *   a_log                FP32 [heads];  dt_bias  FP32 [heads][128]
+ *   state                FP32 pool [slots][heads][128][128]; read only
+ *   state_slot_stride    elements between slots (>= heads*128*128, multiple of 4)
+ *   state_indices        int32 [batch]
+ *   corr                 FP32 records [rows][heads][record_tokens][128]
+ *   kg                   BF16 records [rows][heads][record_tokens][256]
+ *   record_tokens        RQ in tokens..8
+ *   record_rows          int32 [batch] or NULL
+ *   out                  BF16 [batch*tokens][heads*128]; written
+ */
+int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16_t* k,
+               const uint16_t* v, const uint16_t* raw_g, const uint16_t* raw_beta,
+               const float* a_log, const float* dt_bias, float lower_bound, const float* state,
+               int64_t state_slot_stride, const int32_t* state_indices, int null_slot,
+               float* corr, uint16_t* kg, int record_tokens, const int32_t* record_rows,
+               uint16_t* out, void* stream);
+
+/*
+ * kda_fused_replay_verify — deferred RecoverSSM: the previous step's commit and
+ * this step's verify in one pass over the FP32 state ([fused page], module
+ * docstring and KdaFused). Arguments as kda_verify, plus `pending`; state is
+ * read and written. For every (request b, head h) with slot > null_slot:
+ *  1. r = record_rows[b]; n = clamp(pending[r], 0, record_tokens) if r >= 0,
+ *     else 0; the n recorded tokens of row r are replayed onto the page in the
+ *     commit's closed form and S_n is written back to the same page when n > 0;
+ *  2. the window is verified from S_n exactly as kda_verify does;
+ *  3. r >= 0: the records of row r are rewritten for t < tokens, after every
+ *     old record of the item was read.
+ * pending is read only (the defer step of the next step rewrites it). Each
+ * state byte is read once and written at most once.
+ *
+ *   record_rows          int32 [batch], required (< 0: no record row)
+ *   pending              int32 [rows], indexed by record row
+ */
+int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
+                            const uint16_t* k, const uint16_t* v, const uint16_t* raw_g,
+                            const uint16_t* raw_beta, const float* a_log, const float* dt_bias,
+                            float lower_bound, float* state, int64_t state_slot_stride,
+                            const int32_t* state_indices, int null_slot, float* corr,
+                            uint16_t* kg, int record_tokens, const int32_t* record_rows,
+                            const int32_t* pending, uint16_t* out, void* stream);
+
+/*
+ * kda_defer_commit — the defer step of deferred RecoverSSM ([kernels page],
+ * _defer_commit_kernel). For each request b with record_rows[b] >= 0 and
+ * state_indices[b] > null_slot: if eager != NULL and eager[b] != 0,
+ * pending[record_rows[b]] = 0 and commit_lens[b] is kept; otherwise
+ * pending[record_rows[b]] = commit_lens[b] and commit_lens[b] = 0. Other
+ * requests change nothing.
+ *   state_indices, record_rows, eager (or NULL)   int32 [batch]
+ *   commit_lens          int32 [batch], read and written
+ *   pending              int32 [rows], written
+ */
+int kda_defer_commit(int batch, const int32_t* state_indices, int32_t* commit_lens,
+                     const int32_t* record_rows, int32_t* pending, const int32_t* eager,
+                     int null_slot, void* stream);
+
+/*
+ * kda_flush_plan — the plan of an in-place commit of every pending replay
+ * ([kernels page], _prepare_flush_plan_kernel). For each request b:
+ *   n = record_rows[b] >= 0 ? pending[record_rows[b]] : 0, clamped to
+ *   [0, spec_query_len]; commit_lens[b] = (state_indices[b] > null_slot && n > 0) ? n : 0;
+ *   final_indices[b] = state_indices[b]; boundaries[b] = null_slot; boundary_lens[b] = 0.
+ * pending is read only.
+ *   spec_query_len       1..8
+ *   state_indices, record_rows   int32 [batch]
+ *   pending              int32 [rows]
+ *   commit_lens, final_indices, boundaries, boundary_lens   int32 [batch], written
+ */
+int kda_flush_plan(int batch, int spec_query_len, const int32_t* state_indices,
+                   const int32_t* record_rows, const int32_t* pending, int32_t* commit_lens,
+                   int32_t* final_indices, int32_t* boundaries, int32_t* boundary_lens,
+                   int null_slot, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,212 @@
+"""Python binding of libkda, the gfx950 KDA gated delta-rule state-update library.
+
+Argument marshalling only: each function passes device pointers, sizes and the
+current HIP stream to the C entry point of the same name (declared in
+include/kda.h) and raises on a non-zero return code. Every step of the
+computation runs in the library's HIP kernels; there is no fallback path. If
+libkda.so is missing the import fails.
+
+Tensors are torch tensors on a ROCm device: BF16 data as torch.bfloat16, FP32
+as torch.float32, indices as torch.int32, all contiguous.
+"""
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "kda_decay", "kda_commit", "kda_verify", "kda_fused_replay_verify",
+    "kda_defer_commit", "kda_flush_plan", "kda_last_error", "kda_abi_version",
+    "library_path", "KdaError", "KDA_STATE_F32", "KDA_STATE_BF16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_EINVAL, KDA_ELAUNCH = 0, 1, 2
+KDA_STATE_F32, KDA_STATE_BF16 = 0, 1
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(hipcc --offload-arch=gfx950) first")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+_u64a = ctypes.POINTER(ctypes.c_uint64)
+_i64a = ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "kda_last_error": (ctypes.c_char_p, []),
+    "kda_abi_version": (_i, []),
+    "kda_decay": (_i, [_p, _i64, _i, _p, _p, _f, _p, _p]),
+    "kda_commit": (_i, [_i, _i, _i, _i, _i, _u64a, _i64a, _u64a, _i64a, _u64a, _i64a,
+                        _p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p]),
+    "kda_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i64, _p, _i,
+                        _p, _p, _i, _p, _p, _p]),
+    "kda_fused_replay_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i64,
+                                     _p, _i, _p, _p, _i, _p, _p, _p, _p]),
+    "kda_defer_commit": (_i, [_i, _p, _p, _p, _p, _p, _i, _p]),
+    "kda_flush_plan": (_i, [_i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class KdaError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def kda_last_error() -> str:
+    return _lib.kda_last_error().decode()
+
+
+def kda_abi_version() -> int:
+    return _lib.kda_abi_version()
+
+
+def _check(rc: int) -> None:
+    if rc != KDA_OK:
+        raise KdaError(f"[{rc}] {kda_last_error()}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    """Device address of a contiguous device tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be on a ROCm device (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, ref: Optional[torch.Tensor]) -> int:
+    if stream is not None:
+        return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    dev = ref.device if ref is not None else None
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def kda_decay(raw_g: torch.Tensor, a_log: torch.Tensor, dt_bias: torch.Tensor,
+              lower_bound: float, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """out[i,h,c] = exp(lb * sigmoid(exp(a_log[h]) * (raw_g[i,h,c] + dt_bias[h,c])))."""
+    tokens, heads = raw_g.shape[0], raw_g.shape[1]
+    _check(_lib.kda_decay(_ptr(raw_g, torch.bfloat16, "raw_g"), tokens, heads,
+                          _ptr(a_log, torch.float32, "a_log"),
+                          _ptr(dt_bias, torch.float32, "dt_bias"), float(lower_bound),
+                          _ptr(out, torch.float32, "out"), _stream(stream, raw_g)))
+    return out
+
+
+def _table(values, ctype):
+    arr = (ctype * len(values))(*[int(v) for v in values])
+    return arr
+
+
+def kda_commit(*, heads: int, window: int, batch: int, state_dtype: int,
+               state_addrs: Sequence[int], state_slot_strides: Sequence[int],
+               corr_addrs: Sequence[int], corr_row_strides: Sequence[int],
+               kg_addrs: Sequence[int], kg_row_strides: Sequence[int],
+               a_log: torch.Tensor, dt_bias: torch.Tensor, sources: torch.Tensor,
+               commit_lens: torch.Tensor, destinations: torch.Tensor,
+               boundaries: Optional[torch.Tensor] = None,
+               boundary_lens: Optional[torch.Tensor] = None,
+               record_rows: Optional[torch.Tensor] = None, lower_bound: float,
+               null_slot: int = 0, stream=None) -> None:
+    """RecoverSSM commit over L layers. ``*_addrs`` are per-layer device base
+    addresses (``tensor.data_ptr()``), strides in elements."""
+    L = len(state_addrs)
+    if not (len(state_slot_strides) == len(corr_addrs) == len(corr_row_strides)
+            == len(kg_addrs) == len(kg_row_strides) == L):
+        raise ValueError("per-layer tables must all have one entry per layer")
+    st, sst = _table(state_addrs, ctypes.c_uint64), _table(state_slot_strides, ctypes.c_int64)
+    ca, cst = _table(corr_addrs, ctypes.c_uint64), _table(corr_row_strides, ctypes.c_int64)
+    ka, kst = _table(kg_addrs, ctypes.c_uint64), _table(kg_row_strides, ctypes.c_int64)
+    i32 = torch.int32
+    _check(_lib.kda_commit(
+        L, heads, window, batch, state_dtype, st, sst, ca, cst, ka, kst,
+        _ptr(a_log, torch.float32, "a_log"), _ptr(dt_bias, torch.float32, "dt_bias"),
+        _ptr(sources, i32, "sources"), _ptr(commit_lens, i32, "commit_lens"),
+        _ptr(destinations, i32, "destinations"), _ptr(boundaries, i32, "boundaries"),
+        _ptr(boundary_lens, i32, "boundary_lens"), _ptr(record_rows, i32, "record_rows"),
+        float(lower_bound), int(null_slot), _stream(stream, sources)))
+
+
+def _verify_args(q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
+                 record_rows, out):
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    return (_ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"), _ptr(raw_g, bf, "raw_g"),
+            _ptr(raw_beta, bf, "raw_beta"), _ptr(a_log, f32, "a_log"),
+            _ptr(dt_bias, f32, "dt_bias"), _ptr(state, f32, "state"),
+            _ptr(state_indices, i32, "state_indices"), _ptr(corr, f32, "corr"),
+            _ptr(kg, bf, "kg"), _ptr(record_rows, i32, "record_rows"), _ptr(out, bf, "out"))
+
+
+def kda_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta, a_log,
+               dt_bias, lower_bound: float, state, state_slot_stride: int, state_indices,
+               corr, kg, record_tokens: int, out, record_rows=None, null_slot: int = 0,
+               stream=None):
+    """Stock verify: writes out and the records, never the state."""
+    (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
+        q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
+        record_rows, out)
+    _check(_lib.kda_verify(heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd,
+                           float(lower_bound), ps, int(state_slot_stride), psi, int(null_slot),
+                           pc, pkg, int(record_tokens), prr, po, _stream(stream, state)))
+    return out
+
+
+def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta,
+                            a_log, dt_bias, lower_bound: float, state, state_slot_stride: int,
+                            state_indices, corr, kg, record_tokens: int, record_rows, pending,
+                            out, null_slot: int = 0, stream=None):
+    """Replay each request's pending tokens into its page, then verify the window."""
+    (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
+        q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
+        record_rows, out)
+    _check(_lib.kda_fused_replay_verify(
+        heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd, float(lower_bound), ps,
+        int(state_slot_stride), psi, int(null_slot), pc, pkg, int(record_tokens), prr,
+        _ptr(pending, torch.int32, "pending"), po, _stream(stream, state)))
+    return out
+
+
+def kda_defer_commit(*, batch: int, state_indices, commit_lens, record_rows, pending,
+                     eager=None, null_slot: int = 0, stream=None):
+    i32 = torch.int32
+    _check(_lib.kda_defer_commit(batch, _ptr(state_indices, i32, "state_indices"),
+                                 _ptr(commit_lens, i32, "commit_lens"),
+                                 _ptr(record_rows, i32, "record_rows"),
+                                 _ptr(pending, i32, "pending"), _ptr(eager, i32, "eager"),
+                                 int(null_slot), _stream(stream, commit_lens)))
+
+
+def kda_flush_plan(*, batch: int, spec_query_len: int, state_indices, record_rows, pending,
+                   commit_lens, final_indices, boundaries, boundary_lens, null_slot: int = 0,
+                   stream=None):
+    i32 = torch.int32
+    _check(_lib.kda_flush_plan(batch, int(spec_query_len),
+                               _ptr(state_indices, i32, "state_indices"),
+                               _ptr(record_rows, i32, "record_rows"),
+                               _ptr(pending, i32, "pending"),
+                               _ptr(commit_lens, i32, "commit_lens"),
+                               _ptr(final_indices, i32, "final_indices"),
+                               _ptr(boundaries, i32, "boundaries"),
+                               _ptr(boundary_lens, i32, "boundary_lens"), int(null_slot),
+                               _stream(stream, commit_lens)))

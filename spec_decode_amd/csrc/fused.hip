@@ -1,0 +1,347 @@
+// Fused replay+verify and the stock verify over FP32 state pages.
+//
+// Method (the vLLM page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.
+// kda.fused", module docstring and KdaFused): per (request, head) item,
+//  1. replay the n pending tokens from the old records in the commit's closed
+//     form, S_n = S_0 diag(D_n) + sum_{t<n} u_t (kn_t * P_t)^T, writing S_n back
+//     when n > 0 (the stock verify, on the page "vllm.models.kimi_k3.nvidia.
+//     specialized_decode.recoverssm.kernels", is this kernel with no replay);
+//  2. verify the window's T tokens from S_n in chunked (WY) form:
+//     w_t = S_n (Gamma_t * kn_t), y_t = S_n (Gamma_t * q_t) (2T dots per row),
+//     A_ts, B_ts pair products, then per state row
+//     u_t = beta_t (v_t - w_t - sum_{s<t} A_ts u_s), o_t = y_t + sum_{s<=t} B_ts u_s;
+//  3. rewrite the item's records (u_t, raw key, raw gate), after every old
+//     record of the item was read.
+//
+// gfx950 mapping. One workgroup of 256 threads (4 wave64) per item. The page is
+// held in VGPRs as 16x16 tiles, wave w owning row blocks 2w and 2w+1 (all 8
+// column blocks each, 64 VGPRs). Within a tile (rows 16rb.., columns 16cb..),
+// lane l holds S[16rb + l%16][16cb + 4(l/16) + i], i = 0..3: one 16-byte load
+// per tile, and exactly the accumulator layout of V_MFMA_F32_16X16X4_F32 for
+// the transposed tile S^T (M = key channel, N = state row). So
+//  - the replay is S^T <- diag(D_n) S^T + KP U^T: 4 multiplies and one or two
+//    MFMAs (K = replayed tokens, zero-padded to 4 or 8) per tile, in place;
+//  - the same registers are the B operand of the dots: D2[j][v] += X[j][c] S[v][c]
+//    with M = j (2T <= 16 rows of X, zero above 2T), N = v, and the 4 values of a
+//    lane as 4 consecutive K steps (key channels 16cb + 4(l/16) + i);
+// so no lane ever exchanges state values and every state byte is read once.
+//
+// Prologue (while the page loads are in flight): threads 0..127 (channel c) do
+// the new tokens (decays, key norms, Gamma, X, the T^2 pair products reduced
+// over channels by a transposing wave reduction); threads 128..255 do the old
+// records (decays, norms, kp_t = kn_t * prod_{t<s<n} d_s, D_n), the
+// corrections, v and beta. The small loads are issued before the page loads so
+// that the in-order return of loads lets the prologue start early.
+#include "kda_device.h"
+
+namespace kda {
+
+template <int T>
+struct Pairs {
+  static constexpr int NA = T * (T - 1) / 2;  // A_ts, s < t
+  static constexpr int NP = T * T;            // then B_ts, s <= t
+  static constexpr int P2 = NP <= 1 ? 1 : NP <= 2 ? 2 : NP <= 4 ? 4 : NP <= 8 ? 8
+                          : NP <= 16 ? 16 : NP <= 32 ? 32 : 64;
+  static constexpr int G = P2 < 16 ? P2 : 16;  // values reduced per exchange group
+  __device__ static constexpr int a(int t, int s) { return t * (t - 1) / 2 + s; }
+  __device__ static constexpr int b(int t, int s) { return NA + t * (t + 1) / 2 + s; }
+};
+
+// This channel's share of pair product i: A_ts = kn_s * P(s,t) * kn_t or
+// B_ts = kn_s * P(s,t) * q_t with P(s,t) = prod_{s<r<=t} d_r; zero past T^2.
+template <int T>
+__device__ __forceinline__ float pair_share(int i, const float (&kn)[T], const float (&q)[T],
+                                            const float (&d)[T]) {
+  using PI = Pairs<T>;
+  if (i >= PI::NP) return 0.f;
+  // A_ts sits at t(t-1)/2 + s (t >= 1), B_ts at NA + t(t+1)/2 + s (t >= 0): find
+  // the row t whose block holds index j, then s is the offset in that block.
+  const bool is_a = i < PI::NA;
+  const int j = is_a ? i : i - PI::NA;
+  int t = is_a ? 1 : 0;
+  while ((is_a ? (t + 1) * t / 2 : (t + 1) * (t + 2) / 2) <= j) ++t;
+  const int s = j - (is_a ? t * (t - 1) / 2 : t * (t + 1) / 2);
+  float pr = 1.f;
+  for (int r = s + 1; r <= t; ++r) pr *= d[r];
+  return kn[s] * pr * (is_a ? kn[t] : q[t]);
+}
+
+template <int T, bool FUSED>
+__global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
+  using PI = Pairs<T>;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int H = p.heads;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wave = tid / WAVE;
+  const int64_t tok0 = (int64_t)b * T;
+
+  const int slot = p.slots[b];
+  if (slot <= p.null_slot) {
+    // No state: the item's outputs are zero and nothing else is written.
+    if (tid < T * (V / 8)) {
+      const int t = tid / (V / 8);
+      const int c = (tid % (V / 8)) * 8;
+      *reinterpret_cast<uint4*>(p.out + ((tok0 + t) * H + h) * V + c) = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  const int rec = p.rows != nullptr ? p.rows[b] : b;
+  int n = 0;
+  if constexpr (FUSED) {
+    if (rec >= 0) {
+      n = p.pending[rec];
+      n = n < 0 ? 0 : (n > p.rq ? p.rq : n);
+    }
+  }
+  const bool replay = FUSED && n > 0;
+
+  __shared__ __attribute__((aligned(16))) float x_s[16][K];    // Gamma_t kn_t | Gamma_t q_t | 0
+  __shared__ __attribute__((aligned(16))) float kp_s[MAX_T][K];  // replay kn_t P_t (0 past n)
+  __shared__ __attribute__((aligned(16))) float u_s[MAX_T][V];   // replay u_t (0 past n)
+  __shared__ __attribute__((aligned(16))) float dn_s[K];
+  __shared__ __attribute__((aligned(16))) float v_s[T][V];
+  __shared__ __attribute__((aligned(16))) float dots_s[V][16];   // w_t | y_t per state row
+  __shared__ float pair_s[2][PI::P2];
+  __shared__ float ssq_s[2][2][MAX_T];  // [new | old keys][wave of the half][token]
+  __shared__ float beta_s[MAX_T];
+
+  const int c = tid & (K - 1);   // channel / state row of this thread's half
+  const bool lower = tid < K;    // threads 0..127: new tokens; 128..255: records, v, beta
+  const int64_t head_row = (int64_t)h * K + c;
+
+  // ---- 1. Small loads first.
+  uint32_t kgb[T], qb[T], vb[T];  // kgb: raw key bits | raw gate bits << 16
+  uint32_t okb[MAX_T], ogb[MAX_T];
+  float ou[MAX_T];
+  uint32_t rbb = 0;
+  if (lower) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t idx = (tok0 + t) * H * K + head_row;
+      kgb[t] = (uint32_t)p.k[idx] | ((uint32_t)p.g[idx] << 16);
+      qb[t] = p.q[idx];
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + t) * H * V + head_row];
+    if (c < T) rbb = p.rb[(tok0 + c) * H + h];
+    if constexpr (FUSED) {
+      if (replay) {
+        const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
+#pragma unroll
+        for (int t = 0; t < MAX_T; ++t) {
+          okb[t] = 0;
+          ogb[t] = 0;
+          ou[t] = 0.f;
+          if (t < n) {
+            okb[t] = p.kg[(rbase + t) * 2 * K + c];
+            ogb[t] = p.kg[(rbase + t) * 2 * K + K + c];
+            ou[t] = p.corr[(rbase + t) * V + c];
+          }
+        }
+      }
+    }
+  }
+
+  // ---- 2. The page: 16 tiles per wave, one 16-byte load each.
+  float* page = p.state + (int64_t)slot * p.slot_stride + (int64_t)h * PAGE;
+  const int lr = lane & 15;  // row within a tile
+  const int lq = lane >> 4;  // 4-channel group within a tile
+  floatx4 st[2][8];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      st[r][cb] = *reinterpret_cast<const floatx4*>(page + (16 * (2 * wave + r) + lr) * K +
+                                                    16 * cb + 4 * lq);
+
+  // ---- 3. Prologue, part one: decays, key sums of squares, staging.
+  const float ea = __expf(p.a_log[h]);
+  const float dtb = p.dt_bias[head_row];
+  float kf[T], qf[T], dnew[T];
+  float okf[MAX_T], od[MAX_T];
+  if (lower) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      kf[t] = bf16_lo(kgb[t]);
+      qf[t] = bf16_bits_to_f32(qb[t]);
+      dnew[t] = gate_decay(bf16_hi(kgb[t]), ea, dtb, p.lb);
+      const float s = wave_sum(kf[t] * kf[t]);
+      if (lane == 0) ssq_s[0][wave][t] = s;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < T; ++t) v_s[t][c] = bf16_bits_to_f32(vb[t]);
+    if (c < T) beta_s[c] = sigmoidf_fast(bf16_bits_to_f32(rbb));
+    if constexpr (FUSED) {
+      if (replay) {
+#pragma unroll
+        for (int t = 0; t < MAX_T; ++t) {
+          okf[t] = bf16_bits_to_f32(okb[t]);
+          od[t] = gate_decay(bf16_bits_to_f32(ogb[t]), ea, dtb, p.lb);
+          u_s[t][c] = ou[t];  // zero past n
+          if (t < n) {
+            const float s = wave_sum(okf[t] * okf[t]);
+            if (lane == 0) ssq_s[1][wave - 2][t] = s;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. Prologue, part two: X, pair products, replay coefficients.
+  if (lower) {
+    float kn[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      kn[t] = kf[t] * __builtin_amdgcn_rsqf(ssq_s[0][0][t] + ssq_s[0][1][t] + 1e-6f);
+    float gam = 1.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      gam *= dnew[t];
+      x_s[t][c] = gam * kn[t];
+      x_s[T + t][c] = gam * qf[t];
+    }
+#pragma unroll
+    for (int j = 2 * T; j < 16; ++j) x_s[j][c] = 0.f;
+    // A_ts, B_ts summed over the 128 channels: each wave reduces groups of G
+    // values with the transposing exchange, then the two waves' sums meet in LDS.
+#pragma unroll
+    for (int g0 = 0; g0 < PI::P2; g0 += PI::G) {
+      float pv[PI::G];
+#pragma unroll
+      for (int i = 0; i < PI::G; ++i) pv[i] = pair_share<T>(g0 + i, kn, qf, dnew);
+      const float tot = wave_transpose_sum<PI::G>(pv, lane);
+      if (lane < PI::G && g0 + lane < PI::NP) pair_s[wave][g0 + lane] = tot;
+    }
+  } else {
+    if constexpr (FUSED) {
+      if (replay) {
+        float pp = 1.f;
+#pragma unroll
+        for (int t = MAX_T - 1; t >= 0; --t) {
+          float w = 0.f;
+          if (t < n) {
+            const float kn =
+                okf[t] * __builtin_amdgcn_rsqf(ssq_s[1][0][t] + ssq_s[1][1][t] + 1e-6f);
+            w = kn * pp;
+            pp *= od[t];
+          }
+          kp_s[t][c] = w;
+        }
+        dn_s[c] = pp;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. The state pass: replay in place (MFMA), store S_n, 2T dots (MFMA).
+  float ub[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  if (replay) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int vrow = 16 * (2 * wave + r) + lr;
+      ub[r][0] = u_s[lq][vrow];
+      ub[r][1] = u_s[4 + lq][vrow];
+    }
+  }
+  floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const floatx4 xa = *reinterpret_cast<const floatx4*>(&x_s[lr][16 * cb + 4 * lq]);
+    floatx4 dn4 = {1.f, 1.f, 1.f, 1.f};
+    float ka0 = 0.f, ka1 = 0.f;
+    if (replay) {
+      dn4 = *reinterpret_cast<const floatx4*>(&dn_s[16 * cb + 4 * lq]);
+      ka0 = kp_s[lq][16 * cb + lr];
+      ka1 = kp_s[4 + lq][16 * cb + lr];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      floatx4 s = st[r][cb];
+      if (replay) {
+        s = s * dn4;
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka0, ub[r][0], s, 0, 0, 0);
+        if (n > 4) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka1, ub[r][1], s, 0, 0, 0);
+        *reinterpret_cast<floatx4*>(page + (16 * (2 * wave + r) + lr) * K + 16 * cb + 4 * lq) = s;
+      }
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[0], s[0], acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[1], s[1], acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[2], s[2], acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[3], s[3], acc[r], 0, 0, 0);
+    }
+  }
+  // acc[r], lane l, value i: column j = 4(l/16) + i of state row 16(2w+r) + l%16.
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    *reinterpret_cast<floatx4*>(&dots_s[16 * (2 * wave + r) + lr][4 * lq]) = acc[r];
+  __syncthreads();
+
+  // ---- 6. Per state row: the T x T forward substitution, outputs, records.
+  if (lower) {
+    const int vrow = c;
+    float us[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float a = v_s[t][vrow] - dots_s[vrow][t];
+#pragma unroll
+      for (int s = 0; s < t; ++s) {
+        const int ia = PI::a(t, s);
+        a = fmaf(-(pair_s[0][ia] + pair_s[1][ia]), us[s], a);
+      }
+      us[t] = beta_s[t] * a;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float o = dots_s[vrow][T + t];
+#pragma unroll
+      for (int s = 0; s <= t; ++s) {
+        const int ib = PI::b(t, s);
+        o = fmaf(pair_s[0][ib] + pair_s[1][ib], us[s], o);
+      }
+      p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
+    }
+    if (rec >= 0) {
+      const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        p.corr[(rbase + t) * V + vrow] = us[t];
+        p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(kgb[t] & 0xffffu);
+        p.kg[(rbase + t) * 2 * K + K + c] = (uint16_t)(kgb[t] >> 16);
+      }
+    }
+  }
+}
+
+template <bool FUSED>
+static hipError_t launch_t(const VerifyParams& p, int tokens, dim3 grid, hipStream_t stream) {
+  switch (tokens) {
+#define KDA_VERIFY_CASE(TT)                                                                 \
+  case TT:                                                                                 \
+    hipLaunchKernelGGL((verify_kernel<TT, FUSED>), grid, dim3(256), 0, stream, p);         \
+    break;
+    KDA_VERIFY_CASE(1)
+    KDA_VERIFY_CASE(2)
+    KDA_VERIFY_CASE(3)
+    KDA_VERIFY_CASE(4)
+    KDA_VERIFY_CASE(5)
+    KDA_VERIFY_CASE(6)
+    KDA_VERIFY_CASE(7)
+    KDA_VERIFY_CASE(8)
+#undef KDA_VERIFY_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, int batch,
+                         hipStream_t stream) {
+  const dim3 grid(p.heads, batch);
+  return fused ? launch_t<true>(p, tokens, grid, stream) : launch_t<false>(p, tokens, grid, stream);
+}
+
+}  // namespace kda

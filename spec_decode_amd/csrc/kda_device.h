@@ -1,0 +1,145 @@
+// Device helpers and internal launch interfaces of libkda (gfx950 only).
+#pragma once
+
+#include <hip/hip_bf16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int K = 128;  // key channels per head
+constexpr int V = 128;  // value channels per head
+constexpr int PAGE = K * V;
+constexpr int MAX_T = 8;  // largest verify window / record capacity
+constexpr int WAVE = 64;
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// FP32 -> BF16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __hip_bfloat16 h = __float2bfloat16(x);
+  return *reinterpret_cast<uint16_t*>(&h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- gate math
+
+// The bounded KDA gate decay exp(lb * sigmoid(e^{A_log} (g + dt_bias))), with
+// e^{A_log} passed in precomputed. FP32 with the hardware exp2-based exp and
+// reciprocal; a large negative logit gives 1 + inf -> reciprocal 0 -> d = 1.
+__device__ __forceinline__ float gate_decay(float g, float exp_a_log, float dt_bias, float lb) {
+  const float z = exp_a_log * (g + dt_bias);
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+  return __expf(lb * sig);
+}
+
+__device__ __forceinline__ float sigmoidf_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = WAVE / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, WAVE);
+  return x;
+}
+
+// Sums NV per-lane values (NV a power of two <= 64) over the 64 lanes of a
+// wave, leaving in lane l the total of value index (l % NV). Each exchange step
+// halves the live values: a lane keeps the half selected by one bit of its id
+// and adds the partner's copy of that half, so NV - 1 exchanges replace the
+// NV * 6 of separate butterflies.
+template <int NV>
+__device__ __forceinline__ float wave_transpose_sum(float (&x)[NV], int lane) {
+#pragma unroll
+  for (int half = NV / 2; half >= 1; half >>= 1) {
+    const bool upper = (lane & half) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float keep = upper ? x[i + half] : x[i];
+      const float send = upper ? x[i] : x[i + half];
+      x[i] = keep + __shfl_xor(send, half, WAVE);
+    }
+  }
+  float r = x[0];
+#pragma unroll
+  for (int off = NV; off < WAVE; off <<= 1) r += __shfl_xor(r, off, WAVE);
+  return r;
+}
+
+// ---------------------------------------------------------------- launch params
+
+constexpr int COMMIT_LAYERS_PER_LAUNCH = 16;
+
+struct CommitLayer {
+  void* state;            // pool base [slots][H][V][K] (BF16 bits or FP32)
+  const float* corr;      // corrections [rows][H][Q][V]
+  const uint16_t* kg;     // key/gate records [rows][H][Q][2K]
+  int64_t state_stride;   // elements between slots
+  int64_t corr_stride;    // elements between record rows
+  int64_t kg_stride;      // elements between record rows
+};
+
+struct CommitParams {
+  CommitLayer layer[COMMIT_LAYERS_PER_LAUNCH];
+  const float* a_log;     // [L][H], at the launch's first layer
+  const float* dt_bias;   // [L][H][K], at the launch's first layer
+  const int32_t* sources;
+  const int32_t* lens;
+  const int32_t* dests;
+  const int32_t* bounds;  // NULL: align off
+  const int32_t* blens;
+  const int32_t* rows;    // NULL: row b
+  int heads;
+  int null_slot;
+  float lb;
+};
+
+struct VerifyParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* rb;
+  const float* a_log;
+  const float* dt_bias;
+  float* state;
+  int64_t slot_stride;
+  const int32_t* slots;
+  const int32_t* rows;     // NULL (verify only): row b
+  const int32_t* pending;  // fused only
+  float* corr;
+  uint16_t* kg;
+  uint16_t* out;
+  int rq;
+  int heads;
+  int null_slot;
+  float lb;
+};
+
+hipError_t launch_decay(const uint16_t* raw_g, int64_t tokens, int heads, const float* a_log,
+                        const float* dt_bias, float lb, float* out, hipStream_t stream);
+hipError_t launch_commit(const CommitParams& p, int window, bool bf16, bool align, int batch,
+                         int layers, hipStream_t stream);
+hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, int batch,
+                         hipStream_t stream);
+hipError_t launch_defer(int batch, const int32_t* state_indices, int32_t* commit_lens,
+                        const int32_t* record_rows, int32_t* pending, const int32_t* eager,
+                        int null_slot, hipStream_t stream);
+hipError_t launch_flush_plan(int batch, int spec_query_len, const int32_t* state_indices,
+                             const int32_t* record_rows, const int32_t* pending,
+                             int32_t* commit_lens, int32_t* final_indices, int32_t* boundaries,
+                             int32_t* boundary_lens, int null_slot, hipStream_t stream);
+
+}  // namespace kda

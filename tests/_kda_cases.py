@@ -1,0 +1,196 @@
+"""GPU-vs-oracle case runners for the parity tests.
+
+Each runner takes host inputs (from the seeded generators in ``workloads``),
+runs the library on the GPU through its C ABI (via the ``spec_decode_amd``
+binding), runs the FP64 oracle on host copies of the same inputs, and compares
+every output: within the tolerances of ``_compare`` where the call writes, and
+bit-exact everywhere else (memory the call must not touch).
+
+Nothing produced by the GPU is ever fed to the oracle.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+from _compare import assert_bf16_close, assert_exact, assert_f32_close
+
+K = V = 128
+DEV = "cuda:0"
+
+
+def announce(msg: str) -> None:
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- transfers
+
+def np_of(t: torch.Tensor) -> np.ndarray:
+    """Host numpy copy; BF16 tensors become uint16 bit patterns."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def to_dev(x):
+    if isinstance(x, np.ndarray):
+        return dev_bf16(x) if x.dtype == np.uint16 else dev(x)
+    return x.to(DEV)
+
+
+# ---------------------------------------------------------------- commit
+
+def commit_written(layers, H, B, Q, lens, src, dst, bnd, blen, rows, null_slot=0):
+    """(layer, slot, head) pages a commit writes, and with which length."""
+    out = {}
+    for l in range(layers):
+        for b in range(B):
+            r = b if rows is None else rows[b]
+            n = int(lens[b])
+            if not (n > 0 and src[b] > null_slot and dst[b] > null_slot and r >= 0):
+                continue
+            for h in range(H):
+                out[(l, int(dst[b]), h)] = "dst"
+                if bnd is not None and blen[b] > 0 and bnd[b] > null_slot:
+                    out[(l, int(bnd[b]), h)] = "bnd"
+    return out
+
+
+def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_layers, a_log,
+                    dt_bias, src, lens, dst, bnd=None, blen=None, rows=None,
+                    lb=W.LOWER_BOUND, null_slot=0, label="commit"):
+    """layers_state: per-layer flat host pools (uint16 bits or float32)."""
+    L = len(layers_state)
+    announce(f"{label}: L={L} H={H} B={B} Q={Q} bf16={bf16} align={bnd is not None}")
+    d_state = [to_dev(s) for s in layers_state]
+    d_corr = [to_dev(c) for c in corr_layers]
+    d_kg = [to_dev(k) for k in kg_layers]
+    i32 = lambda a: None if a is None else dev(np.asarray(a, np.int32))
+    import spec_decode_amd as kda
+    kda.kda_commit(heads=H, window=Q, batch=B,
+                   state_dtype=kda.KDA_STATE_BF16 if bf16 else kda.KDA_STATE_F32,
+                   state_addrs=[t.data_ptr() for t in d_state], state_slot_strides=strides,
+                   corr_addrs=[t.data_ptr() for t in d_corr],
+                   corr_row_strides=[H * Q * V] * L,
+                   kg_addrs=[t.data_ptr() for t in d_kg],
+                   kg_row_strides=[H * Q * 2 * K] * L,
+                   a_log=dev(np.asarray(a_log, np.float32)),
+                   dt_bias=dev(np.asarray(dt_bias, np.float32)), sources=i32(src),
+                   commit_lens=i32(lens), destinations=i32(dst), boundaries=i32(bnd),
+                   boundary_lens=i32(blen), record_rows=i32(rows), lower_bound=lb,
+                   null_slot=null_slot)
+    torch.cuda.synchronize()
+    gpu = [np_of(t) for t in d_state]
+    ref = [s.copy() for s in layers_state]
+    oracle.commit(heads=H, window=Q, batch=B, state_bf16=bf16, state_layers=ref,
+                  state_slot_strides=strides, corr_layers=corr_layers,
+                  corr_row_strides=[H * Q * V] * L, kg_layers=kg_layers,
+                  kg_row_strides=[H * Q * 2 * K] * L, a_log=a_log, dt_bias=dt_bias,
+                  sources=src, commit_lens=lens, destinations=dst, boundaries=bnd,
+                  boundary_lens=blen, record_rows=rows, lower_bound=lb, null_slot=null_slot)
+    written = commit_written(L, H, B, Q, lens, src, dst, bnd, blen, rows, null_slot)
+    for l in range(L):
+        mask = np.zeros(layers_state[l].size, dtype=bool)
+        for (ll, slot, h) in written:
+            if ll == l:
+                o = slot * strides[l] + h * V * K
+                mask[o:o + V * K] = True
+        if bf16:
+            assert_bf16_close(f"{label} layer {l} written pages", gpu[l][mask], ref[l][mask])
+        else:
+            assert_f32_close(f"{label} layer {l} written pages", gpu[l][mask], ref[l][mask])
+        assert_exact(f"{label} layer {l} untouched", gpu[l][~mask], layers_state[l][~mask])
+    return gpu, ref, written
+
+
+# ---------------------------------------------------------------- verify / fused
+
+def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, win,
+                    rows=None, pending=None, lb=W.LOWER_BOUND, null_slot=0, label="verify",
+                    stride=None, check=True):
+    """All host arrays: state float32 flat, corr float32 [rows,H,RQ,V], kg uint16
+    [rows,H,RQ,2K], win a dict of uint16 arrays (q, k, v, raw_g, raw_beta).
+    Returns (gpu results, oracle results) as dicts of host arrays."""
+    stride = H * V * K if stride is None else stride
+    announce(f"{label}: fused={fused} H={H} B={B} T={T} RQ={RQ}")
+    import spec_decode_amd as kda
+    d = dict(state=dev(state), corr=dev(corr), kg=dev_bf16(kg),
+             out=torch.full((B * T, H * V), 0, dtype=torch.bfloat16, device=DEV))
+    d["out"].view(torch.int16).fill_(0x7FFF)  # a sentinel: every element must be written
+    args = dict(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]), k=dev_bf16(win["k"]),
+                v=dev_bf16(win["v"]), raw_g=dev_bf16(win["raw_g"]),
+                raw_beta=dev_bf16(win["raw_beta"]), a_log=dev(np.asarray(a_log, np.float32)),
+                dt_bias=dev(np.asarray(dt_bias, np.float32)), lower_bound=lb,
+                state=d["state"], state_slot_stride=stride,
+                state_indices=dev(np.asarray(slots, np.int32)), corr=d["corr"], kg=d["kg"],
+                record_tokens=RQ, out=d["out"], null_slot=null_slot,
+                record_rows=None if rows is None else dev(np.asarray(rows, np.int32)))
+    if fused:
+        kda.kda_fused_replay_verify(pending=dev(np.asarray(pending, np.int32)), **args)
+    else:
+        kda.kda_verify(**args)
+    torch.cuda.synchronize()
+    gpu = {k: np_of(v) for k, v in d.items()}
+    ref = dict(state=state.copy(), corr=corr.copy(), kg=kg.copy(),
+               out=np.full((B * T, H * V), 0x7FFF, np.uint16))
+    oargs = dict(heads=H, tokens=T, batch=B, q=win["q"], k=win["k"], v=win["v"],
+                 raw_g=win["raw_g"], raw_beta=win["raw_beta"], a_log=a_log, dt_bias=dt_bias,
+                 lower_bound=lb, state=ref["state"], state_slot_stride=stride,
+                 state_indices=slots, corr=ref["corr"], kg=ref["kg"], record_tokens=RQ,
+                 out=ref["out"], record_rows=rows, null_slot=null_slot)
+    if fused:
+        oracle.fused_replay_verify(pending=pending, **oargs)
+    else:
+        oracle.verify(**oargs)
+    if check:
+        compare_verify(gpu, ref, dict(state=state, corr=corr, kg=kg), fused=fused, H=H, B=B,
+                       T=T, RQ=RQ, slots=slots, rows=rows, pending=pending, stride=stride,
+                       null_slot=null_slot, label=label)
+    return gpu, ref
+
+
+def verify_written(*, fused, H, B, T, RQ, slots, rows, pending, stride, null_slot, n_state,
+                   corr_shape):
+    smask = np.zeros(n_state, dtype=bool)
+    cmask = np.zeros(corr_shape, dtype=bool)
+    for b in range(B):
+        if slots[b] <= null_slot:
+            continue
+        r = b if rows is None else int(rows[b])
+        if r >= 0:
+            cmask[r, :, :T, :] = True
+            if fused:
+                n = min(max(int(pending[r]), 0), RQ)
+                if n > 0:
+                    for h in range(H):
+                        o = int(slots[b]) * stride + h * V * K
+                        smask[o:o + V * K] = True
+    return smask, cmask
+
+
+def compare_verify(gpu, ref, orig, *, fused, H, B, T, RQ, slots, rows, pending, stride,
+                   null_slot, label):
+    smask, cmask = verify_written(fused=fused, H=H, B=B, T=T, RQ=RQ, slots=slots, rows=rows,
+                                  pending=pending, stride=stride, null_slot=null_slot,
+                                  n_state=orig["state"].size, corr_shape=orig["corr"].shape)
+    assert_bf16_close(f"{label} out", gpu["out"], ref["out"])
+    assert_exact(f"{label} key/gate records", gpu["kg"], ref["kg"])
+    assert_f32_close(f"{label} corrections (written)", gpu["corr"][cmask], ref["corr"][cmask])
+    assert_exact(f"{label} corrections (untouched)", gpu["corr"][~cmask], orig["corr"][~cmask])
+    assert_f32_close(f"{label} state (replayed)", gpu["state"][smask], ref["state"][smask])
+    assert_exact(f"{label} state (untouched)", gpu["state"][~smask], orig["state"][~smask])
+
+
+def window_np(win: "W.Window"):
+    return {name: np_of(getattr(win, name)) for name in ("q", "k", "v", "raw_g", "raw_beta")}

@@ -1,0 +1,119 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/kda.h declares, reports its ABI version, and rejects bad arguments
+with KDA_EINVAL before any launch (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIB = os.path.join(ROOT, "spec_decode_amd", "libkda.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libkda.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("kda_decay", "kda_commit", "kda_verify", "kda_fused_replay_verify",
+                 "kda_defer_commit", "kda_flush_plan", "kda_last_error", "kda_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    lib.kda_abi_version.restype = ctypes.c_int
+    text = open(HEADER).read()
+    want = int(re.search(r"#define KDA_ABI_VERSION (\d+)", text).group(1))
+    assert lib.kda_abi_version() == want
+
+
+def _err(lib):
+    lib.kda_last_error.restype = ctypes.c_char_p
+    return lib.kda_last_error().decode()
+
+
+def test_rejects_bad_arguments_without_launch(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    lib.kda_verify.restype = ctypes.c_int
+    args = [ctypes.c_int(4), ctypes.c_int(9), ctypes.c_int(2)] + [fake] * 7 + [
+        ctypes.c_float(-5.0), fake, ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
+        fake, fake, ctypes.c_int(8), P(None), fake, P(None)]
+    assert lib.kda_verify(*args) == 1
+    assert "tokens must be in 1..8" in _err(lib)
+
+    lib.kda_fused_replay_verify.restype = ctypes.c_int
+    args = [ctypes.c_int(4), ctypes.c_int(4), ctypes.c_int(2)] + [fake] * 7 + [
+        ctypes.c_float(-5.0), fake, ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
+        fake, fake, ctypes.c_int(4), P(None), P(None), fake, P(None)]
+    assert lib.kda_fused_replay_verify(*args) == 1
+    assert "record_rows and pending are required" in _err(lib)
+
+    # record_tokens below tokens
+    args[17] = ctypes.c_int(3)
+    assert lib.kda_fused_replay_verify(*args) == 1
+    assert "record_tokens" in _err(lib)
+
+    # a misaligned state base
+    args = [ctypes.c_int(4), ctypes.c_int(4), ctypes.c_int(2)] + [fake] * 7 + [
+        ctypes.c_float(-5.0), P(0x1004), ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
+        fake, fake, ctypes.c_int(4), fake, fake, fake, P(None)]
+    assert lib.kda_fused_replay_verify(*args) == 1
+    assert "16-byte aligned" in _err(lib)
+
+    # a non-finite lower bound
+    lib.kda_decay.restype = ctypes.c_int
+    assert lib.kda_decay(fake, ctypes.c_int64(3), ctypes.c_int(2), fake, fake,
+                         ctypes.c_float(float("nan")), fake, P(None)) == 1
+    assert "finite" in _err(lib)
+
+
+def test_commit_rejects_bad_tables(lib):
+    lib.kda_commit.restype = ctypes.c_int
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    U64 = ctypes.c_uint64 * 1
+    I64 = ctypes.c_int64 * 1
+
+    def call(window=4, stride=2 * 128 * 128, bnd=None, blen=None, addr=0x2000, dtype=1):
+        return lib.kda_commit(ctypes.c_int(1), ctypes.c_int(2), ctypes.c_int(window),
+                              ctypes.c_int(3), ctypes.c_int(dtype), U64(addr), I64(stride),
+                              U64(0x3000), I64(2 * window * 128), U64(0x4000),
+                              I64(2 * window * 256), fake, fake, fake, fake, fake,
+                              P(bnd), P(blen), P(None), ctypes.c_float(-5.0), ctypes.c_int(0),
+                              P(None))
+
+    assert call(window=9) == 1 and "window" in _err(lib)
+    assert call(stride=100) == 1 and "slot stride" in _err(lib)
+    assert call(stride=2 * 128 * 128 + 3) == 1 and "slot stride" in _err(lib)
+    assert call(bnd=0x5000) == 1 and "together" in _err(lib)
+    assert call(addr=0x2008) == 1 and "16-byte aligned" in _err(lib)
+    assert call(dtype=7) == 1 and "state_dtype" in _err(lib)
+
+
+def test_zero_batch_is_a_no_op(lib):
+    P = ctypes.c_void_p
+    lib.kda_defer_commit.restype = ctypes.c_int
+    assert lib.kda_defer_commit(ctypes.c_int(0), P(None), P(None), P(None), P(None), P(None),
+                                ctypes.c_int(0), P(None)) == 0
+    assert _err(lib) == ""
+    lib.kda_flush_plan.restype = ctypes.c_int
+    assert lib.kda_flush_plan(ctypes.c_int(0), ctypes.c_int(4), *([P(None)] * 7),
+                              ctypes.c_int(0), P(None)) == 0

@@ -1,0 +1,231 @@
+"""GPU parity on small seeded cases that span every template instance (window
+1..8, BF16/FP32 state, align on/off, verify/fused) plus the edge cases: null
+slots, record row -1, n = 0, n above the capacity, negative pending, m > n,
+in-place commits, per-layer stride tables and more layers than one launch
+holds. Every output is compared with the FP64 oracle element by element."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _compare import assert_exact, assert_f32_close
+from _kda_cases import (DEV, announce, dev, dev_bf16, np_of, run_commit_case,
+                        run_verify_case, window_np)
+
+pytestmark = pytest.mark.gpu
+
+K = V = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import spec_decode_amd  # noqa: F401  (fails loudly without libkda.so)
+
+    torch.cuda.init()
+    yield
+
+
+# ---------------------------------------------------------------- plan steps
+
+@pytest.mark.parametrize("eager", [False, True])
+def test_plan_steps_bit_exact(eager):
+    import spec_decode_amd as kda
+
+    rng = np.random.default_rng(3)
+    B, rows_n = 777, 900
+    si = rng.integers(-2, 5, B).astype(np.int32)
+    rows = rng.permutation(rows_n)[:B].astype(np.int32)
+    rows[rng.random(B) < 0.1] = -1
+    lens = rng.integers(-3, 12, B).astype(np.int32)
+    pending = rng.integers(-5, 20, rows_n).astype(np.int32)
+    eg = (rng.random(B) < 0.3).astype(np.int32) if eager else None
+    announce(f"plan: defer B={B} eager={eager}")
+    d_lens, d_pend = dev(lens), dev(pending)
+    kda.kda_defer_commit(batch=B, state_indices=dev(si), commit_lens=d_lens,
+                         record_rows=dev(rows), pending=d_pend,
+                         eager=None if eg is None else dev(eg))
+    torch.cuda.synchronize()
+    r_lens, r_pend = lens.copy(), pending.copy()
+    oracle.defer(si, r_lens, rows, r_pend, eg)
+    assert_exact("defer commit_lens", np_of(d_lens), r_lens)
+    assert_exact("defer pending", np_of(d_pend), r_pend)
+    for q in (1, 4, 8):
+        announce(f"plan: flush B={B} q={q}")
+        outs = [torch.full((B,), -99, dtype=torch.int32, device=DEV) for _ in range(4)]
+        kda.kda_flush_plan(batch=B, spec_query_len=q, state_indices=dev(si),
+                           record_rows=dev(rows), pending=dev(r_pend), commit_lens=outs[0],
+                           final_indices=outs[1], boundaries=outs[2], boundary_lens=outs[3])
+        torch.cuda.synchronize()
+        ref = oracle.flush_plan(si, rows, r_pend, q)
+        for name, g, r in zip(("commit_lens", "final", "boundaries", "boundary_lens"), outs, ref):
+            assert_exact(f"flush {name} q={q}", np_of(g), r)
+
+
+# ---------------------------------------------------------------- decay
+
+@pytest.mark.parametrize("lb", [-5.0, 0.0, -0.5])
+def test_decay(lb):
+    import spec_decode_amd as kda
+
+    g = W._gen(5)
+    N, H = 37, 5
+    raw = W.bf16(W.normal(g, (N, H, K)) * 3.0)
+    raw[0, 0, :4] = torch.tensor([60.0, -60.0, 0.0, -0.0]).to(torch.bfloat16)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    announce(f"decay N={N} H={H} lb={lb}")
+    out = torch.empty((N, H, K), dtype=torch.float32, device=DEV)
+    kda.kda_decay(raw.to(DEV), a_log[0].to(DEV), dtb[0].to(DEV), lb, out)
+    torch.cuda.synchronize()
+    ref = oracle.decay_buf(W.bits(raw), a_log[0].numpy(), dtb[0].numpy(), lb)
+    assert_f32_close("decay", np_of(out), ref)
+    if lb == 0.0:
+        assert np.all(np_of(out) == 1.0)
+
+
+# ---------------------------------------------------------------- commit
+
+def _commit_inputs(seed, L, H, B, Q, bf16, slots, pad=(0,)):
+    g = W._gen(seed)
+    page = H * V * K
+    strides = [page + pad[l % len(pad)] for l in range(L)]
+    dt = torch.bfloat16 if bf16 else torch.float32
+    states, corrs, kgs = [], [], []
+    for l in range(L):
+        s = W.draw_state(seed * 31 + l, slots * strides[l], dt)
+        states.append(W.bits(s) if bf16 else s.numpy().copy())
+        c, k = W.draw_records(g, B, H, Q)
+        corrs.append(c.numpy().copy())
+        kgs.append(W.bits(k))
+    a_log, dtb = W.draw_gate_params(g, L, H)
+    return states, strides, corrs, kgs, a_log.numpy(), dtb.numpy()
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("Q", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_commit_windows(bf16, Q):
+    H, B, L, S = 3, 7, 1, 16
+    states, strides, corrs, kgs, a_log, dtb = _commit_inputs(100 + Q, L, H, B, Q, bf16, S)
+    rng = np.random.default_rng(Q)
+    perm = rng.permutation(np.arange(1, S))
+    src = perm[:B].astype(np.int32)
+    dst = perm[B:2 * B].astype(np.int32)
+    lens = rng.integers(0, Q + 3, B).astype(np.int32)  # includes 0 and > Q
+    lens[0], lens[1] = 0, Q + 2
+    src[2] = 0  # null source: no-op
+    dst[3] = 0  # null destination: no-op
+    run_commit_case(H=H, B=B, Q=Q, bf16=bf16, layers_state=states, strides=strides,
+                    corr_layers=corrs, kg_layers=kgs, a_log=a_log, dt_bias=dtb, src=src,
+                    lens=lens, dst=dst, label=f"commit Q={Q} bf16={bf16}")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_commit_align_multilayer_strides(bf16):
+    H, B, L, Q, S = 2, 6, 3, 8, 24
+    states, strides, corrs, kgs, a_log, dtb = _commit_inputs(7, L, H, B, Q, bf16, S,
+                                                             pad=(0, 64, 128))
+    rng = np.random.default_rng(8)
+    perm = rng.permutation(np.arange(1, S))
+    src, dst, bnd = (perm[i * B:(i + 1) * B].astype(np.int32) for i in range(3))
+    lens = np.array([8, 5, 3, 1, 6, 0], np.int32)
+    blen = np.array([3, 0, 7, 1, 6, 2], np.int32)  # m = 0, m > n, m = n, lens 0
+    bnd[4] = 0  # null boundary: no boundary store
+    rows = rng.permutation(B).astype(np.int32)
+    run_commit_case(H=H, B=B, Q=Q, bf16=bf16, layers_state=states, strides=strides,
+                    corr_layers=corrs, kg_layers=kgs, a_log=a_log, dt_bias=dtb, src=src,
+                    lens=lens, dst=dst, bnd=bnd, blen=blen, rows=rows,
+                    label=f"commit align L={L} bf16={bf16}")
+
+
+def test_commit_inplace_record_rows_fp32():
+    H, B, L, Q, S = 4, 5, 1, 8, 8
+    states, strides, corrs, kgs, a_log, dtb = _commit_inputs(9, L, H, B, Q, False, S)
+    src = np.array([1, 2, 3, 4, 5], np.int32)
+    lens = np.array([8, 1, 0, 4, 7], np.int32)
+    rows = np.array([4, -1, 2, 0, 1], np.int32)  # row -1: no-op
+    run_commit_case(H=H, B=B, Q=Q, bf16=False, layers_state=states, strides=strides,
+                    corr_layers=corrs, kg_layers=kgs, a_log=a_log, dt_bias=dtb, src=src,
+                    lens=lens, dst=src.copy(), rows=rows, label="commit in-place fp32")
+
+
+def test_commit_more_layers_than_one_launch():
+    H, B, L, Q, S = 1, 2, 18, 3, 5
+    states, strides, corrs, kgs, a_log, dtb = _commit_inputs(11, L, H, B, Q, True, S, pad=(0, 8))
+    src = np.array([1, 2], np.int32)
+    dst = np.array([3, 4], np.int32)
+    lens = np.array([3, 2], np.int32)
+    run_commit_case(H=H, B=B, Q=Q, bf16=True, layers_state=states, strides=strides,
+                    corr_layers=corrs, kg_layers=kgs, a_log=a_log, dt_bias=dtb, src=src,
+                    lens=lens, dst=dst, label="commit L=18")
+
+
+# ---------------------------------------------------------------- verify / fused
+
+def _vf_case(seed, H, B, T, RQ, S, null_rows=(), norec_rows=()):
+    c = W.small_fused_case(seed, H, B, T, RQ, S, null_rows=null_rows, no_record_rows=norec_rows)
+    return dict(state=c["state"].numpy().copy(), slots=c["state_indices"].numpy().copy(),
+                rows=c["record_rows"].numpy().copy(), corr=c["corr"].numpy().copy(),
+                kg=W.bits(c["kg"]), a_log=c["a_log"][0].numpy(), dt_bias=c["dt_bias"][0].numpy(),
+                win=window_np(c["window"]))
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_verify_windows(T):
+    H, B = 3, 5
+    for RQ in sorted({T, 8}):
+        c = _vf_case(200 + T, H, B, T, RQ, 9, null_rows=(1,), norec_rows=(3,))
+        run_verify_case(fused=False, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
+                        corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                        win=c["win"], rows=c["rows"], label=f"verify T={T} RQ={RQ}")
+    # record_rows = NULL: request b writes row b
+    c = _vf_case(300 + T, H, B, T, T, 9)
+    run_verify_case(fused=False, H=H, B=B, T=T, RQ=T, state=c["state"], slots=c["slots"],
+                    corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                    win=c["win"], rows=None, label=f"verify T={T} rows=NULL")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_fused_windows(T):
+    H, B = 3, 6
+    for RQ in sorted({T, 8}):
+        c = _vf_case(400 + T, H, B, T, RQ, 10, null_rows=(1,), norec_rows=(3,))
+        rng = np.random.default_rng(T * 10 + RQ)
+        pending = rng.integers(0, RQ + 1, B).astype(np.int32)
+        rows = c["rows"]
+        # edge pending values on live rows: 0, RQ, above RQ, negative, 1..4 and 5..8
+        live = [b for b in range(B) if b not in (1, 3)]
+        edge = [0, RQ, RQ + 3, -2]
+        for b, e in zip(live, edge):
+            pending[rows[b]] = e
+        run_verify_case(fused=True, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
+                        corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                        win=c["win"], rows=rows, pending=pending, label=f"fused T={T} RQ={RQ}")
+
+
+def test_fused_every_pending_count():
+    """One request per n = 0..8 (the replay's one- and two-MFMA paths)."""
+    H, B, T, RQ = 2, 9, 4, 8
+    c = _vf_case(77, H, B, T, RQ, 12)
+    pending = np.zeros(B, np.int32)
+    for b in range(B):
+        pending[c["rows"][b]] = b
+    run_verify_case(fused=True, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
+                    corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                    win=c["win"], rows=c["rows"], pending=pending, label="fused n=0..8")
+
+
+def test_fused_padded_slot_stride():
+    H, B, T, RQ, S = 2, 4, 3, 4, 6
+    stride = H * V * K + 256
+    g = W._gen(55)
+    state = W.draw_state(56, S * stride, torch.float32).numpy().copy()
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    corr, kg = W.draw_records(g, B, H, RQ)
+    win = window_np(W.draw_window(g, B, T, H))
+    slots = np.array([5, 2, 0, 3], np.int32)
+    rows = np.array([1, 3, 0, 2], np.int32)
+    pending = np.array([2, 4, 1, 3], np.int32)
+    run_verify_case(fused=True, H=H, B=B, T=T, RQ=RQ, state=state, slots=slots,
+                    corr=corr.numpy().copy(), kg=W.bits(kg), a_log=a_log[0].numpy(),
+                    dt_bias=dtb[0].numpy(), win=win, rows=rows, pending=pending, stride=stride,
+                    label="fused padded stride")

@@ -1,0 +1,388 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA state-update hot path on one MI355X.
+
+One step is one pass of the whole path over the large decode batch (L=1, H=64
+heads, B=512 requests, q=8 tokens, FP32 state of 512 slots x 64 heads x 64 KiB
+= 2 GiB, about 5% no-op rows):
+
+  1. the sampler's accepted counts land in the commit-length buffer (a 2 KiB
+     device copy),
+  2. kda_fused_replay_verify: replay each request's pending tokens from its
+     records into its page, verify the 8-token window, rewrite the records,
+  3. kda_defer_commit: the accepted counts become the pending counts,
+  4. kda_flush_plan + kda_commit (FP32, in place, record rows): fold the pending
+     replays into the checkpoints (the flush path).
+
+All inputs are synthetic (seeded generators in ``workloads``) and resident in
+HBM before timing; the records the first step replays come from a verify of a
+prior window. W untimed warm-up steps, then K timed steps between device
+synchronisations. Kernel durations come from HIP events recorded on the stream
+the kernels are launched on.
+
+Printed: one JSON line. ``value`` is the step's state bandwidth: algorithmic
+state bytes (pages read + pages written, from the actual plan) per second.
+``roofline`` is the fused kernel's algorithmic bytes per launch over its mean
+event-timed duration, against 8 TB/s. ``cpu_baseline`` times the FP64 oracle on
+a sample of the same step on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+K = V = 128
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-requests", type=int, default=128,
+                    help="requests of the batch the CPU baseline runs (all 64 heads each)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain 2 GiB device copy (streaming ceiling)")
+    return ap.parse_args()
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+FUSED_SOURCES = ["spec_decode_amd/csrc/fused.hip", "spec_decode_amd/csrc/kda_device.h"]
+COMMIT_SOURCES = ["spec_decode_amd/csrc/commit.hip", "spec_decode_amd/csrc/kda_device.h"]
+
+
+def measured_traffic(name, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------- accounting
+
+def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0):
+    """Algorithmic bytes of one fused launch: (state bytes, total bytes)."""
+    page = V * K * 4
+    state = total = 0
+    for b in range(len(slots)):
+        if slots[b] <= null_slot:
+            total += H * T * V * 2  # zero outputs
+            continue
+        r = int(rows[b])
+        n = min(max(int(pending[r]), 0), RQ) if r >= 0 else 0
+        s = page + (page if n > 0 else 0)
+        t = s + n * (V * 4 + 2 * K * 2)            # old records read
+        t += (T * (V * 4 + 2 * K * 2)) if r >= 0 else 0  # new records written
+        t += T * (3 * K * 2 + V * 2) + T * 2        # q, k, raw_g, v, raw_beta
+        t += T * V * 2                              # o
+        state += H * s
+        total += H * t
+    return state, total
+
+
+def commit_bytes(slots, lens, rows, H, Q, null_slot=0):
+    """Algorithmic bytes of one in-place FP32 commit launch: (state, total)."""
+    page = V * K * 4
+    state = total = 0
+    for b in range(len(slots)):
+        n = int(lens[b])
+        r = int(rows[b])
+        if not (n > 0 and slots[b] > null_slot and r >= 0):
+            continue
+        n = min(n, Q)
+        state += H * 2 * page
+        total += H * (2 * page + n * (V * 4 + 2 * K * 2))
+    return state, total
+
+
+def simulate_plan(slots, rows, pending0, accepted, steps, q, null_slot=0):
+    """Per step: (pending the fused step replays, flush commit lengths)."""
+    pending = pending0.copy()
+    out = []
+    for _ in range(steps):
+        fused_pending = pending.copy()
+        for b in range(len(slots)):  # defer
+            r = int(rows[b])
+            if r >= 0 and slots[b] > null_slot:
+                pending[r] = accepted[b]
+        lens = [0] * len(slots)
+        for b in range(len(slots)):  # flush plan
+            r = int(rows[b])
+            n = int(pending[r]) if r >= 0 else 0
+            n = min(max(n, 0), q)
+            lens[b] = n if (slots[b] > null_slot and n > 0) else 0
+        out.append((fused_pending, lens))
+    return out
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(host, H, T, RQ, n_req, lb):
+    """The FP64 oracle on the first n_req live requests (all heads) of the same
+    step: fused replay+verify, then the in-place commit of the accepted tokens.
+    Reports state GB/s of that sample (the same accounting as the GPU line)."""
+    import numpy as np
+    import oracle
+
+    slots, rows = host["slots"], host["rows"]
+    pick = [b for b in range(len(slots)) if slots[b] > 0 and rows[b] >= 0][:n_req]
+    B = len(pick)
+    page = H * V * K
+    # A compact copy: request j owns slot j + 1 and record row j.
+    state = np.zeros((B + 1) * page, np.float32)
+    for j, b in enumerate(pick):
+        state[(j + 1) * page:(j + 2) * page] = host["state_pages"][b]
+    sl = np.arange(1, B + 1, dtype=np.int32)
+    rr = np.arange(B, dtype=np.int32)
+    corr = np.ascontiguousarray(host["corr"][rows[pick]])
+    kg = np.ascontiguousarray(host["kg"][rows[pick]])
+    pend = np.ascontiguousarray(host["pending"][rows[pick]]).astype(np.int32)
+    acc = np.ascontiguousarray(host["accepted"][pick]).astype(np.int32)
+    tok = np.concatenate([np.arange(b * T, (b + 1) * T) for b in pick])
+    win = {k: np.ascontiguousarray(v[tok]) for k, v in host["win"].items()}
+    out = np.zeros((B * T, H * V), np.uint16)
+    threads = oracle.default_threads()
+    oracle._load()
+    t0 = time.perf_counter()
+    oracle.fused_replay_verify(heads=H, tokens=T, batch=B, q=win["q"], k=win["k"], v=win["v"],
+                               raw_g=win["raw_g"], raw_beta=win["raw_beta"], a_log=host["a_log"],
+                               dt_bias=host["dt_bias"], lower_bound=lb, state=state,
+                               state_slot_stride=page, state_indices=sl, corr=corr, kg=kg,
+                               record_tokens=RQ, record_rows=rr, pending=pend, out=out,
+                               threads=threads)
+    lens = acc.copy()
+    pending2 = pend.copy()
+    oracle.defer(sl, lens, rr, pending2)
+    fl, fin, _, _ = oracle.flush_plan(sl, rr, pending2, T)
+    oracle.commit(heads=H, window=RQ, batch=B, state_bf16=False, state_layers=[state],
+                  state_slot_strides=[page], corr_layers=[corr], corr_row_strides=[H * RQ * V],
+                  kg_layers=[kg], kg_row_strides=[H * RQ * 2 * K],
+                  a_log=host["a_log"][None, :], dt_bias=host["dt_bias"][None, :],
+                  sources=fin, commit_lens=fl, destinations=fin, record_rows=rr,
+                  lower_bound=lb, threads=threads)
+    dt = time.perf_counter() - t0
+    fs, _ = fused_bytes(sl, rr, pend, T, RQ, H)
+    cs, _ = commit_bytes(sl, fl, rr, H, RQ)
+    return {
+        "value": round((fs + cs) / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fused replay+verify then defer/flush/in-place commit of {B} of the "
+                   f"{len(slots)} requests (all {H} heads, {B * H} items), FP64, "
+                   f"{dt:.2f} s wall"),
+        "items_per_s": round(B * H / dt, 1),
+    }
+
+
+# ----------------------------------------------------------------- main
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
+              "shards by request or head with no collective: run one process per GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import spec_decode_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.config4(device=dev)
+    H, B, T, RQ = w.heads, w.batch, w.tokens, w.record_tokens
+    page = H * V * K
+    lb = w.lower_bound
+    a = w.arrays
+    state = a["state"]
+    slots = a["state_indices"].to(dev)
+    rows = a["record_rows"].to(dev)
+    pending = a["pending"].to(dev)
+    accepted = a["accepted"].to(dev)
+    a_log = a["a_log"][0].contiguous().to(dev)
+    dt_bias = a["dt_bias"][0].contiguous().to(dev)
+    corr = a["corr"].to(dev)
+    kg = a["kg"].to(dev)
+    new = w.windows["new"].to(dev)
+    prior = w.windows["prior"].to(dev)
+    out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=dev)
+    commit_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    flush = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
+
+    # The records the first step replays: a verify of the prior window.
+    kda.kda_verify(heads=H, tokens=T, batch=B, q=prior.q, k=prior.k, v=prior.v,
+                   raw_g=prior.raw_g, raw_beta=prior.raw_beta, a_log=a_log, dt_bias=dt_bias,
+                   lower_bound=lb, state=state, state_slot_stride=page, state_indices=slots,
+                   corr=corr, kg=kg, record_tokens=RQ, record_rows=rows, out=out)
+    torch.cuda.synchronize()
+
+    host = None
+    if not args.no_cpu_baseline:
+        sl_h = slots.cpu().numpy()
+        host = dict(slots=sl_h, rows=rows.cpu().numpy(), pending=pending.cpu().numpy(),
+                    accepted=accepted.cpu().numpy(), a_log=a_log.cpu().numpy(),
+                    dt_bias=dt_bias.cpu().numpy(), corr=corr.cpu().numpy(),
+                    kg=kg.cpu().view(torch.int16).numpy().view(np.uint16),
+                    win={n: getattr(new, n).cpu().view(torch.int16).numpy().view(np.uint16)
+                         for n in ("q", "k", "v", "raw_g", "raw_beta")})
+        pick = [b for b in range(B) if sl_h[b] > 0][: args.cpu_requests + 32]
+        host["state_pages"] = {b: state[int(sl_h[b]) * page:(int(sl_h[b]) + 1) * page].cpu().numpy()
+                               for b in pick}
+
+    state_stride = page
+    commit_args = dict(heads=H, window=RQ, batch=B, state_dtype=kda.KDA_STATE_F32,
+                       state_addrs=[state.data_ptr()], state_slot_strides=[state_stride],
+                       corr_addrs=[corr.data_ptr()], corr_row_strides=[H * RQ * V],
+                       kg_addrs=[kg.data_ptr()], kg_row_strides=[H * RQ * 2 * K],
+                       a_log=a_log, dt_bias=dt_bias, sources=flush[1], commit_lens=flush[0],
+                       destinations=flush[1], record_rows=rows, lower_bound=lb)
+
+    total = args.warmup + args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+
+    def step(i):
+        e = ev[i]
+        commit_lens.copy_(accepted)
+        e[0].record()
+        kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v,
+                                    raw_g=new.raw_g, raw_beta=new.raw_beta, a_log=a_log,
+                                    dt_bias=dt_bias, lower_bound=lb, state=state,
+                                    state_slot_stride=state_stride, state_indices=slots,
+                                    corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
+                                    pending=pending, out=out)
+        e[1].record()
+        kda.kda_defer_commit(batch=B, state_indices=slots, commit_lens=commit_lens,
+                             record_rows=rows, pending=pending)
+        kda.kda_flush_plan(batch=B, spec_query_len=T, state_indices=slots, record_rows=rows,
+                           pending=pending, commit_lens=flush[0], final_indices=flush[1],
+                           boundaries=flush[2], boundary_lens=flush[3])
+        e[2].record()
+        kda.kda_commit(**commit_args)
+        e[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if not bool(torch.isfinite(state[: 64 * page]).all()):
+        sys.exit("non-finite state after the run")
+
+    timed = ev[args.warmup:]
+    fused_ms = [e[0].elapsed_time(e[1]) for e in timed]
+    commit_ms = [e[2].elapsed_time(e[3]) for e in timed]
+    step_ms = [e[0].elapsed_time(e[3]) for e in timed]
+
+    # Algorithmic bytes from the plan of each step.
+    sl_h, rr_h = slots.cpu().numpy(), rows.cpu().numpy()
+    plan = simulate_plan(sl_h, rr_h, a["pending"].numpy(), a["accepted"].numpy(), total, T)
+    fb = [fused_bytes(sl_h, rr_h, p, T, RQ, H) for p, _ in plan[args.warmup:]]
+    cb = [commit_bytes(sl_h, l, rr_h, H, RQ) for _, l in plan[args.warmup:]]
+    state_bytes = sum(f[0] + c[0] for f, c in zip(fb, cb))
+    ms_per_step = wall * 1e3 / args.steps
+    value = state_bytes / wall / 1e9
+    items = B * H
+    fused_mean_ms = sum(fused_ms) / len(fused_ms)
+    commit_mean_ms = sum(commit_ms) / len(commit_ms)
+    fused_total = sum(f[1] for f in fb) / len(fb)
+    fused_state = sum(f[0] for f in fb) / len(fb)
+    commit_total = sum(c[1] for c in cb) / len(cb)
+    commit_state = sum(c[0] for c in cb) / len(cb)
+    achieved = fused_total / (fused_mean_ms * 1e-3) / 1e9
+    traffic = measured_traffic("fused_replay_verify/large_decode",
+                               source_digest(FUSED_SOURCES))
+
+    result = {
+        "metric": "state GB/s (% of HBM peak) + (req,head) items/s, KDA commit & fused verify",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "large_decode: L=1 H=64 K=V=128 B=512 q=8 FP32 state 512 slots "
+                        "(2 GiB), ~5% no-op rows; step = fused replay+verify, defer, "
+                        "flush plan, in-place FP32 commit",
+            "global_batch": B, "seq_len": T, "heads": H, "parallelism": "none",
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "items_per_s": round(items / (wall / args.steps), 1),
+        "kernels": {
+            "fused_replay_verify": {
+                "mean_ms": round(fused_mean_ms, 4), "min_ms": round(min(fused_ms), 4),
+                "state_gbs": round(fused_state / (fused_mean_ms * 1e-3) / 1e9, 1),
+                "total_gbs": round(achieved, 1),
+                "items_per_s": round(items / (fused_mean_ms * 1e-3), 1)},
+            "commit_fp32_inplace": {
+                "mean_ms": round(commit_mean_ms, 4), "min_ms": round(min(commit_ms), 4),
+                "state_gbs": round(commit_state / (commit_mean_ms * 1e-3) / 1e9, 1),
+                "total_gbs": round(commit_total / (commit_mean_ms * 1e-3) / 1e9, 1),
+                "items_per_s": round(items / (commit_mean_ms * 1e-3), 1)},
+            "step_event_ms": round(sum(step_ms) / len(step_ms), 4),
+        },
+        "roofline": {
+            "kernel": "fused_replay_verify",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(fused_total),
+        },
+    }
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        result["copy_probe"] = {"bytes": 2 * src.numel() * 4, "ms": round(ms, 4),
+                                "gbs": round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
+    if host is not None:
+        result["cpu_baseline"] = cpu_baseline(host, H, T, RQ, args.cpu_requests, lb)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

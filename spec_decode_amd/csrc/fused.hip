@@ -32,6 +32,8 @@
 // records (decays, norms, kp_t = kn_t * prod_{t<s<n} d_s, D_n), the
 // corrections, v and beta. The small loads are issued before the page loads so
 // that the in-order return of loads lets the prologue start early.
+#include <utility>
+
 #include "kda_device.h"
 
 namespace kda {
@@ -47,23 +49,73 @@ struct Pairs {
   __device__ static constexpr int b(int t, int s) { return NA + t * (t + 1) / 2 + s; }
 };
 
-// This channel's share of pair product i: A_ts = kn_s * P(s,t) * kn_t or
-// B_ts = kn_s * P(s,t) * q_t with P(s,t) = prod_{s<r<=t} d_r; zero past T^2.
+// Which pair product sits at index i: A_ts (s < t) at t(t-1)/2 + s, then B_ts
+// (s <= t) at NA + t(t+1)/2 + s. Built at compile time so that every register
+// index below folds to a constant.
 template <int T>
-__device__ __forceinline__ float pair_share(int i, const float (&kn)[T], const float (&q)[T],
+struct PairTable {
+  int s[64], t[64], is_a[64];
+  constexpr PairTable() : s(), t(), is_a() {
+    int i = 0;
+    for (int tt = 1; tt < T; ++tt)
+      for (int ss = 0; ss < tt; ++ss) { s[i] = ss; t[i] = tt; is_a[i] = 1; ++i; }
+    for (int tt = 0; tt < T; ++tt)
+      for (int ss = 0; ss <= tt; ++ss) { s[i] = ss; t[i] = tt; is_a[i] = 0; ++i; }
+    for (; i < 64; ++i) { s[i] = 0; t[i] = 0; is_a[i] = -1; }
+  }
+};
+
+// This channel's share of pair product I: A_ts = kn_s * P(s,t) * kn_t or
+// B_ts = kn_s * P(s,t) * q_t with P(s,t) = prod_{s<r<=t} d_r; zero past T^2.
+template <int T, int I>
+__device__ __forceinline__ float pair_share(const float (&kn)[T], const float (&q)[T],
                                             const float (&d)[T]) {
-  using PI = Pairs<T>;
-  if (i >= PI::NP) return 0.f;
-  // A_ts sits at t(t-1)/2 + s (t >= 1), B_ts at NA + t(t+1)/2 + s (t >= 0): find
-  // the row t whose block holds index j, then s is the offset in that block.
-  const bool is_a = i < PI::NA;
-  const int j = is_a ? i : i - PI::NA;
-  int t = is_a ? 1 : 0;
-  while ((is_a ? (t + 1) * t / 2 : (t + 1) * (t + 2) / 2) <= j) ++t;
-  const int s = j - (is_a ? t * (t - 1) / 2 : t * (t + 1) / 2);
-  float pr = 1.f;
-  for (int r = s + 1; r <= t; ++r) pr *= d[r];
-  return kn[s] * pr * (is_a ? kn[t] : q[t]);
+  constexpr PairTable<T> tab{};
+  constexpr int s = tab.s[I], t = tab.t[I], kind = tab.is_a[I];
+  if constexpr (kind < 0) {
+    return 0.f;
+  } else {
+    float pr = kn[s];
+#pragma unroll
+    for (int r = s + 1; r <= t; ++r) pr *= d[r];
+    return pr * (kind == 1 ? kn[t] : q[t]);
+  }
+}
+
+template <int T, int G0, int... Is>
+__device__ __forceinline__ void pair_group(float (&pv)[sizeof...(Is)], const float (&kn)[T],
+                                           const float (&q)[T], const float (&d)[T],
+                                           std::integer_sequence<int, Is...>) {
+  ((pv[Is] = pair_share<T, G0 + Is>(kn, q, d)), ...);
+}
+
+// The pair products summed over the 128 channels, stage one (lower waves, one
+// channel per lane): two in-register transposing steps over the lane quads
+// leave each lane P2/4 partial sums of 4 channels (for P2 >= 4), which go to
+// part[pair][quad of the half] in LDS; stage two sums those per pair.
+template <int T>
+struct PairStage {
+  static constexpr int P2 = Pairs<T>::P2;
+  static constexpr int STEPS = P2 >= 4 ? 2 : (P2 == 2 ? 1 : 0);
+  static constexpr int R = P2 >> STEPS;           // values a lane keeps
+  static constexpr int PARTS = 128 >> STEPS;      // partials per pair (both waves)
+};
+
+template <int T, int... Is>
+__device__ __forceinline__ void pair_stage_one(const float (&kn)[T], const float (&q)[T],
+                                               const float (&d)[T], int lane, int wave,
+                                               float* part, std::integer_sequence<int, Is...>) {
+  using PS = PairStage<T>;
+  float pv[PS::P2];
+  ((pv[Is] = pair_share<T, Is>(kn, q, d)), ...);
+  if constexpr (PS::STEPS >= 1) quad_transpose_step<PS::P2, 1>(pv);
+  if constexpr (PS::STEPS >= 2) quad_transpose_step<PS::P2 / 2, 2>(pv);
+  // Lane l now holds, in slot i, pair i + R*(bit1 of l) + 2R*(bit0 of l)
+  // (only the bits the steps used), summed over its 2^STEPS lanes.
+  const int sel = PS::STEPS == 2 ? ((lane & 1) * 2 + ((lane >> 1) & 1)) : (PS::STEPS == 1 ? (lane & 1) : 0);
+  const int group = wave * (64 >> PS::STEPS) + (lane >> PS::STEPS);
+#pragma unroll
+  for (int i = 0; i < PS::R; ++i) part[(i + PS::R * sel) * PS::PARTS + group] = pv[i];
 }
 
 template <int T, bool FUSED>
@@ -74,7 +126,9 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   const int H = p.heads;
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
-  const int wave = tid / WAVE;
+  // The wave index as a scalar: branches on it are uniform (s_cbranch), so a
+  // wave runs only its own half's code and waits only on its own loads.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
   const int64_t tok0 = (int64_t)b * T;
 
   const int slot = p.slots[b];
@@ -103,71 +157,86 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   __shared__ __attribute__((aligned(16))) float dn_s[K];
   __shared__ __attribute__((aligned(16))) float v_s[T][V];
   __shared__ __attribute__((aligned(16))) float dots_s[V][16];   // w_t | y_t per state row
-  __shared__ float pair_s[2][PI::P2];
+  __shared__ float pair_s[PI::P2];
+  __shared__ __attribute__((aligned(16))) float part_s[PI::P2][PairStage<T>::PARTS];
   __shared__ float ssq_s[2][2][MAX_T];  // [new | old keys][wave of the half][token]
   __shared__ float beta_s[MAX_T];
+  __shared__ uint32_t kg_s[T][K];  // raw key | raw gate << 16 of the window, for the records
 
   const int c = tid & (K - 1);   // channel / state row of this thread's half
-  const bool lower = tid < K;    // threads 0..127: new tokens; 128..255: records, v, beta
+  const bool lower = wave < 2;   // threads 0..127: new tokens; 128..255: records, v, beta
   const int64_t head_row = (int64_t)h * K + c;
 
-  // ---- 1. Small loads first.
-  uint32_t kgb[T], qb[T], vb[T];  // kgb: raw key bits | raw gate bits << 16
+  // ---- 1-2. Loads. Loads return in order, so a wave's first use of a small
+  // input waits for every load issued before it. The new-token waves (0, 1)
+  // issue their small loads first and the page after, so their prologue starts
+  // while the page streams in; the record waves (2, 3) issue the page first,
+  // then theirs (their prologue needs the records, which arrive after).
+  const float a_log_h = p.a_log[h];
+  const float dtb = p.dt_bias[head_row];
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t kb[T], gb[T], qb[T];  // lower: new raw key, gate, q bits
+  uint32_t vb[T];                // upper: new v bits
   uint32_t okb[MAX_T], ogb[MAX_T];
   float ou[MAX_T];
   uint32_t rbb = 0;
-  if (lower) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int64_t idx = (tok0 + t) * H * K + head_row;
-      kgb[t] = (uint32_t)p.k[idx] | ((uint32_t)p.g[idx] << 16);
-      qb[t] = p.q[idx];
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + t) * H * V + head_row];
-    if (c < T) rbb = p.rb[(tok0 + c) * H + h];
-    if constexpr (FUSED) {
-      if (replay) {
-        const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
-#pragma unroll
-        for (int t = 0; t < MAX_T; ++t) {
-          okb[t] = 0;
-          ogb[t] = 0;
-          ou[t] = 0.f;
-          if (t < n) {
-            okb[t] = p.kg[(rbase + t) * 2 * K + c];
-            ogb[t] = p.kg[(rbase + t) * 2 * K + K + c];
-            ou[t] = p.corr[(rbase + t) * V + c];
-          }
-        }
-      }
-    }
-  }
-
-  // ---- 2. The page: 16 tiles per wave, one 16-byte load each.
   float* page = p.state + (int64_t)slot * p.slot_stride + (int64_t)h * PAGE;
   const int lr = lane & 15;  // row within a tile
   const int lq = lane >> 4;  // 4-channel group within a tile
   floatx4 st[2][8];
+  const float* tile0 = page + (16 * (2 * wave) + lr) * K + 4 * lq;
+  if (lower) {
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+    for (int t = 0; t < T; ++t) {
+      const int64_t idx = (tok0 + t) * H * K + head_row;
+      kb[t] = p.k[idx];
+      gb[t] = p.g[idx];
+      qb[t] = p.q[idx];
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-      st[r][cb] = *reinterpret_cast<const floatx4*>(page + (16 * (2 * wave + r) + lr) * K +
-                                                    16 * cb + 4 * lq);
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+        st[r][cb] = *reinterpret_cast<const floatx4*>(tile0 + 16 * r * K + 16 * cb);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+        st[r][cb] = *reinterpret_cast<const floatx4*>(tile0 + 16 * r * K + 16 * cb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + t) * H * V + head_row];
+    rbb = p.rb[(tok0 + (c < T ? c : T - 1)) * H + h];  // unconditional: no divergent load
+    if constexpr (FUSED) {
+      const int64_t rbase = ((int64_t)(rec < 0 ? 0 : rec) * H + h) * p.rq;
+#pragma unroll
+      for (int t = 0; t < MAX_T; ++t) {
+        okb[t] = 0;
+        ogb[t] = 0;
+        ou[t] = 0.f;
+        if (t < n) {
+          okb[t] = p.kg[(rbase + t) * 2 * K + c];
+          ogb[t] = p.kg[(rbase + t) * 2 * K + K + c];
+          ou[t] = p.corr[(rbase + t) * V + c];
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- 3. Prologue, part one: decays, key sums of squares, staging.
-  const float ea = __expf(p.a_log[h]);
-  const float dtb = p.dt_bias[head_row];
+  const float ea = __expf(a_log_h);
   float kf[T], qf[T], dnew[T];
   float okf[MAX_T], od[MAX_T];
   if (lower) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      kf[t] = bf16_lo(kgb[t]);
+      kf[t] = bf16_bits_to_f32(kb[t]);
       qf[t] = bf16_bits_to_f32(qb[t]);
-      dnew[t] = gate_decay(bf16_hi(kgb[t]), ea, dtb, p.lb);
+      dnew[t] = gate_decay(bf16_bits_to_f32(gb[t]), ea, dtb, p.lb);
+      kg_s[t][c] = kb[t] | (gb[t] << 16);  // raw bits for the record write-back
       const float s = wave_sum(kf[t] * kf[t]);
       if (lane == 0) ssq_s[0][wave][t] = s;
     }
@@ -209,14 +278,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     for (int j = 2 * T; j < 16; ++j) x_s[j][c] = 0.f;
     // A_ts, B_ts summed over the 128 channels: each wave reduces groups of G
     // values with the transposing exchange, then the two waves' sums meet in LDS.
-#pragma unroll
-    for (int g0 = 0; g0 < PI::P2; g0 += PI::G) {
-      float pv[PI::G];
-#pragma unroll
-      for (int i = 0; i < PI::G; ++i) pv[i] = pair_share<T>(g0 + i, kn, qf, dnew);
-      const float tot = wave_transpose_sum<PI::G>(pv, lane);
-      if (lane < PI::G && g0 + lane < PI::NP) pair_s[wave][g0 + lane] = tot;
-    }
+    pair_stage_one<T>(kn, qf, dnew, lane, wave, &part_s[0][0],
+                      std::make_integer_sequence<int, PI::P2>{});
   } else {
     if constexpr (FUSED) {
       if (replay) {
@@ -237,6 +300,22 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
   }
   __syncthreads();
+
+  // ---- Pair products, stage two: 4 threads per pair add its partials.
+  {
+    using PS = PairStage<T>;
+    constexpr int PER = PS::PARTS / 4;
+    if (tid < PS::P2 * 4) {
+      const int pr = tid >> 2;
+      const float* src = &part_s[pr][(tid & 3) * PER];
+      float acc2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc2 += src[i];
+      acc2 += dpp_f<DPP_XOR1>(acc2);
+      acc2 += dpp_f<DPP_XOR2>(acc2);
+      if ((tid & 3) == 0) pair_s[pr] = acc2;
+    }
+  }
 
   // ---- 5. The state pass: replay in place (MFMA), store S_n, 2T dots (MFMA).
   float ub[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
@@ -290,7 +369,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
       for (int s = 0; s < t; ++s) {
         const int ia = PI::a(t, s);
-        a = fmaf(-(pair_s[0][ia] + pair_s[1][ia]), us[s], a);
+        a = fmaf(-pair_s[ia], us[s], a);
       }
       us[t] = beta_s[t] * a;
     }
@@ -300,7 +379,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
       for (int s = 0; s <= t; ++s) {
         const int ib = PI::b(t, s);
-        o = fmaf(pair_s[0][ib] + pair_s[1][ib], us[s], o);
+        o = fmaf(pair_s[ib], us[s], o);
       }
       p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
     }
@@ -309,8 +388,9 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         p.corr[(rbase + t) * V + vrow] = us[t];
-        p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(kgb[t] & 0xffffu);
-        p.kg[(rbase + t) * 2 * K + K + c] = (uint16_t)(kgb[t] >> 16);
+        const uint32_t bits = kg_s[t][c];
+        p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(bits & 0xffffu);
+        p.kg[(rbase + t) * 2 * K + K + c] = (uint16_t)(bits >> 16);
       }
     }
   }

@@ -47,35 +47,64 @@ __device__ __forceinline__ float sigmoidf_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// ---------------------------------------------------------------- reductions
+// ---------------------------------------------------------------- cross-lane
 
+// DPP move of a float (gfx9 controls): lanes whose source is outside the
+// pattern, or whose row is masked off, read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, true));
+}
+constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_SHR1 = 0x111;
+constexpr int DPP_ROW_SHR2 = 0x112;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+// Sum over the 64 lanes of a wave, returned to every lane (as a scalar).
+// Row sums by row shifts, then the row-broadcast steps fold the four rows into
+// lane 63; no LDS round trip.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = WAVE / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, WAVE);
-  return x;
+  x += dpp_f<DPP_ROW_SHR1>(x);
+  x += dpp_f<DPP_ROW_SHR2>(x);
+  x += dpp_f<DPP_ROW_SHR4>(x);
+  x += dpp_f<DPP_ROW_SHR8>(x);
+  x += dpp_f<DPP_ROW_BCAST15, 0xa>(x);
+  x += dpp_f<DPP_ROW_BCAST31, 0xc>(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-// Sums NV per-lane values (NV a power of two <= 64) over the 64 lanes of a
-// wave, leaving in lane l the total of value index (l % NV). Each exchange step
-// halves the live values: a lane keeps the half selected by one bit of its id
-// and adds the partner's copy of that half, so NV - 1 exchanges replace the
-// NV * 6 of separate butterflies.
-template <int NV>
-__device__ __forceinline__ float wave_transpose_sum(float (&x)[NV], int lane) {
-#pragma unroll
-  for (int half = NV / 2; half >= 1; half >>= 1) {
-    const bool upper = (lane & half) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float keep = upper ? x[i + half] : x[i];
-      const float send = upper ? x[i] : x[i + half];
-      x[i] = keep + __shfl_xor(send, half, WAVE);
-    }
-  }
-  float r = x[0];
-#pragma unroll
-  for (int off = NV; off < WAVE; off <<= 1) r += __shfl_xor(r, off, WAVE);
+// Per-lane choice by a constant lane mask: lanes whose bit is set in MASK take
+// `if_set`. Written as one opaque v_cndmask so the compiler cannot turn a pair
+// of such choices over one register array into a dynamically indexed read.
+template <uint64_t MASK>
+__device__ __forceinline__ float lane_pick(float if_set, float if_clear) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(MASK));
   return r;
+}
+constexpr uint64_t LANES_BIT0 = 0xAAAAAAAAAAAAAAAAull;  // lanes with bit 0 set
+constexpr uint64_t LANES_BIT1 = 0xCCCCCCCCCCCCCCCCull;  // lanes with bit 1 set
+
+// One transposing exchange step over lane pairs (l, l ^ DIST), DIST in {1, 2},
+// on the first NV values of x: a lane keeps the half selected by its lane bit
+// and adds the partner's copy of that half, halving the values it holds.
+template <int NV, int DIST, int N>
+__device__ __forceinline__ void quad_transpose_step(float (&x)[N]) {
+  static_assert(NV <= N && NV % 2 == 0, "step over the first NV values");
+  constexpr int half = NV / 2;
+  constexpr uint64_t mask = DIST == 1 ? LANES_BIT0 : LANES_BIT1;
+  constexpr int ctrl = DIST == 1 ? DPP_XOR1 : DPP_XOR2;
+#pragma unroll
+  for (int i = 0; i < half; ++i) {
+    const float keep = lane_pick<mask>(x[i + half], x[i]);
+    const float send = lane_pick<mask>(x[i], x[i + half]);
+    x[i] = keep + dpp_f<ctrl>(send);
+  }
 }
 
 // ---------------------------------------------------------------- launch params

@@ -44,7 +44,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--cpu-requests", type=int, default=128,
+    ap.add_argument("--cpu-requests", type=int, default=512,
                     help="requests of the batch the CPU baseline runs (all 64 heads each)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 2 GiB device copy (streaming ceiling)")

@@ -17,10 +17,61 @@
 // L2 norm (eps 1e-6 inside the root), and suffix products walked from the
 // last replayed token down: kp_t = kn_t * prod_{t<s<n} d_s, D_n. The commit
 // page computes the same products in log space; the direct product is exact
-// to FP32 rounding and needs no log or exp per token.
+// to FP32 rounding and needs no log or exp per token. With align, S_m is
+// folded first, stored to the boundary page, and folded on to S_n.
 #include "kda_device.h"
 
 namespace kda {
+
+// s[i][e] <- s[i][e] * D[c0 + e] + sum_{t0 <= t < t1} u[t][r0 + RPP i] * kp[t][c0 + e]
+template <int EPC, int PASSES, int RPP, int Q>
+__device__ __forceinline__ void fold_stage(float (&s)[PASSES][EPC], const float* D,
+                                           const float* kp, const float* u, int t0, int t1,
+                                           int c0, int r0) {
+  float dd[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) dd[e] = D[c0 + e];
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) s[i][e] *= dd[e];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {
+    if (t >= t0 && t < t1) {
+      float k[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) k[e] = kp[t * K + c0 + e];
+#pragma unroll
+      for (int i = 0; i < PASSES; ++i) {
+        const float uu = u[t * V + r0 + RPP * i];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s[i][e] = fmaf(uu, k[e], s[i][e]);
+      }
+    }
+  }
+}
+
+// The page's 16-byte chunks, rounded to the state dtype (BF16: nearest-even).
+template <bool BF16, int EPC, int PASSES, int RPP, typename Elem>
+__device__ __forceinline__ void store_page(const float (&s)[PASSES][EPC], Elem* pg, int c0,
+                                           int r0) {
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    uint4 w;
+    if constexpr (BF16) {
+      w.x = pack_bf16x2(s[i][0], s[i][1]);
+      w.y = pack_bf16x2(s[i][2], s[i][3]);
+      w.z = pack_bf16x2(s[i][4], s[i][5]);
+      w.w = pack_bf16x2(s[i][6], s[i][7]);
+    } else {
+      w.x = __float_as_uint(s[i][0]);
+      w.y = __float_as_uint(s[i][1]);
+      w.z = __float_as_uint(s[i][2]);
+      w.w = __float_as_uint(s[i][3]);
+    }
+    *reinterpret_cast<uint4*>(pg + (r0 + RPP * i) * K + c0) = w;
+  }
+}
 
 template <bool BF16, int Q, bool ALIGN>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
@@ -60,48 +111,55 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   __shared__ float dm_s[ALIGN ? K : 1];
   __shared__ float ssq_s[2][Q];
 
-  // ---- 1. Record loads (issued first so the page loads queue behind them).
+  // ---- 1-2. Loads. The record loads go first, branch-free (token index
+  // clamped, values masked later) and kept raw, then the page loads right
+  // behind them: loads return in order, so the coefficient work below can start
+  // when the records arrive while the page is still streaming in.
+  const int lane = tid & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const bool lower = wave < 2;  // waves 0, 1: key channels; 2, 3: corrections
+  const int c = tid & (K - 1);
   const int64_t rec_tok0 = ((int64_t)h * Q);
-  float kraw[Q], graw[Q], uval[Q];
-  if (tid < K) {
-    const uint16_t* kg = L.kg + (int64_t)row * L.kg_stride + rec_tok0 * 2 * K;
-#pragma unroll
-    for (int t = 0; t < Q; ++t) {
-      kraw[t] = 0.f;
-      graw[t] = 0.f;
-      if (t < ne) {
-        kraw[t] = bf16_bits_to_f32(kg[t * 2 * K + tid]);
-        graw[t] = bf16_bits_to_f32(kg[t * 2 * K + K + tid]);
-      }
-    }
-  } else {
-    const float* corr = L.corr + (int64_t)row * L.corr_stride + rec_tok0 * V;
-#pragma unroll
-    for (int t = 0; t < Q; ++t) uval[t] = t < ne ? corr[t * V + (tid - K)] : 0.f;
-  }
-
-  // ---- 2. The source page: PASSES 16-byte chunks per thread, in flight.
+  uint32_t kb[Q], gb[Q];
+  float uval[Q];
   const int c0 = (tid % CPR) * EPC;
   const int r0 = tid / CPR;
   const Elem* srcp =
       reinterpret_cast<const Elem*>(L.state) + (int64_t)src * L.state_stride + (int64_t)h * PAGE;
   uint4 raw[PASSES];
+  const float a_log_lh = p.a_log[l * H + h];
+  const float dtb = p.dt_bias[((int64_t)l * H + h) * K + c];
+  {
+    // Branch-free: every thread loads its channel's recorded key, gate and
+    // correction (each half of the workgroup uses one of them; the duplicate
+    // reads hit L2), so no value is defined on one path only.
+    const uint16_t* kg = L.kg + (int64_t)row * L.kg_stride + rec_tok0 * 2 * K;
+    const float* corr = L.corr + (int64_t)row * L.corr_stride + rec_tok0 * V;
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const int tt = t < ne ? t : 0;
+      kb[t] = kg[tt * 2 * K + c];
+      gb[t] = kg[tt * 2 * K + K + c];
+      uval[t] = corr[tt * V + c];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < PASSES; ++i)
     raw[i] = *reinterpret_cast<const uint4*>(srcp + (r0 + RPP * i) * K + c0);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- 3. Per-channel coefficients.
-  const int lane = tid & (WAVE - 1);
-  const int wave = tid / WAVE;
-  float d[Q];
-  if (tid < K) {
-    const float ea = __expf(p.a_log[l * H + h]);
-    const float dtb = p.dt_bias[((int64_t)l * H + h) * K + tid];
+  float d[Q], kraw[Q];
+  if (lower) {
+    const float ea = __expf(a_log_lh);
 #pragma unroll
     for (int t = 0; t < Q; ++t) {
       d[t] = 1.f;
+      kraw[t] = 0.f;
       if (t < ne) {
-        d[t] = gate_decay(graw[t], ea, dtb, p.lb);
+        kraw[t] = bf16_bits_to_f32(kb[t]);
+        d[t] = gate_decay(bf16_bits_to_f32(gb[t]), ea, dtb, p.lb);
         const float s = wave_sum(kraw[t] * kraw[t]);
         if (lane == 0) ssq_s[wave][t] = s;
       }
@@ -109,40 +167,47 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   } else {
 #pragma unroll
     for (int t = 0; t < Q; ++t)
-      if (t < ne) u_s[t][tid - K] = uval[t];
+      if (t < ne) u_s[t][c] = uval[t];
   }
   __syncthreads();
-  if (tid < K) {
+  // With a live boundary the fold runs in two stages through S_m (the commit
+  // composes: S_n is the commit of tokens m..n-1 onto S_m), so one accumulator
+  // serves both stores. mm = m when the boundary is live, else 0.
+  const int mm = (ALIGN && blive) ? me : 0;
+  if (lower) {
     float kn[Q];
 #pragma unroll
     for (int t = 0; t < Q; ++t)
       kn[t] = t < ne ? kraw[t] * __builtin_amdgcn_rsqf(ssq_s[0][t] + ssq_s[1][t] + 1e-6f) : 0.f;
-    float pp = 1.f;
+    // Stage two (tokens mm..ne-1): kp_t = kn_t prod_{t<s<ne} d_s, D = prod_{mm<=s<ne} d_s.
+    float pp = 1.f, dmn = 1.f;
 #pragma unroll
     for (int t = Q - 1; t >= 0; --t) {
       if (t < ne) {
-        kp_s[t][tid] = kn[t] * pp;
+        kp_s[t][c] = kn[t] * pp;
         pp *= d[t];
+        if (t == mm) dmn = pp;
       }
     }
-    dn_s[tid] = pp;
+    dn_s[c] = dmn;
+    // Stage one (tokens 0..mm-1): kpm_t = kn_t prod_{t<s<mm} d_s, D_m = prod_{s<mm} d_s.
     if constexpr (ALIGN) {
-      if (blive) {
+      if (mm > 0) {
         float pm = 1.f;
 #pragma unroll
         for (int t = Q - 1; t >= 0; --t) {
-          if (t < me) {
-            kpm_s[t][tid] = kn[t] * pm;
+          if (t < mm) {
+            kpm_s[t][c] = kn[t] * pm;
             pm *= d[t];
           }
         }
-        dm_s[tid] = pm;
+        dm_s[c] = pm;
       }
     }
   }
   __syncthreads();
 
-  // ---- 4. The fold, in registers: s = S_0 diag(D) then += u_t kp_t per token.
+  // ---- 4. The fold, in registers: per stage s = s diag(D) + sum_t u_t kp_t.
   float s[PASSES][EPC];
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
@@ -160,96 +225,17 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
       s[i][3] = __uint_as_float(raw[i].w);
     }
   }
-  float sb[ALIGN ? PASSES : 1][EPC];
-  {
-    float dn[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) dn[e] = dn_s[c0 + e];
-    if constexpr (ALIGN) {
-      if (blive) {
-        float dm[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) dm[e] = dm_s[c0 + e];
-#pragma unroll
-        for (int i = 0; i < PASSES; ++i)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) sb[i][e] = s[i][e] * dm[e];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) s[i][e] *= dn[e];
-  }
-#pragma unroll
-  for (int t = 0; t < Q; ++t) {
-    if (t < ne) {
-      float kp[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) kp[e] = kp_s[t][c0 + e];
-      const bool bt = ALIGN && blive && t < me;
-      float kpm[EPC];
-      if constexpr (ALIGN) {
-        if (bt) {
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) kpm[e] = kpm_s[t][c0 + e];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < PASSES; ++i) {
-        const float u = u_s[t][r0 + RPP * i];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) s[i][e] = fmaf(u, kp[e], s[i][e]);
-        if constexpr (ALIGN) {
-          if (bt) {
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) sb[i][e] = fmaf(u, kpm[e], sb[i][e]);
-          }
-        }
-      }
-    }
-  }
-
-  // ---- 5. Stores: destination (and boundary) page, 16 bytes per chunk.
   Elem* base = reinterpret_cast<Elem*>(L.state);
-  Elem* dstp = base + (int64_t)dst * L.state_stride + (int64_t)h * PAGE;
-#pragma unroll
-  for (int i = 0; i < PASSES; ++i) {
-    uint4 w;
-    if constexpr (BF16) {
-      w.x = pack_bf16x2(s[i][0], s[i][1]);
-      w.y = pack_bf16x2(s[i][2], s[i][3]);
-      w.z = pack_bf16x2(s[i][4], s[i][5]);
-      w.w = pack_bf16x2(s[i][6], s[i][7]);
-    } else {
-      w.x = __float_as_uint(s[i][0]);
-      w.y = __float_as_uint(s[i][1]);
-      w.z = __float_as_uint(s[i][2]);
-      w.w = __float_as_uint(s[i][3]);
-    }
-    *reinterpret_cast<uint4*>(dstp + (r0 + RPP * i) * K + c0) = w;
-  }
   if constexpr (ALIGN) {
-    if (blive) {
-      Elem* bp = base + (int64_t)bnd * L.state_stride + (int64_t)h * PAGE;
-#pragma unroll
-      for (int i = 0; i < PASSES; ++i) {
-        uint4 w;
-        if constexpr (BF16) {
-          w.x = pack_bf16x2(sb[i][0], sb[i][1]);
-          w.y = pack_bf16x2(sb[i][2], sb[i][3]);
-          w.z = pack_bf16x2(sb[i][4], sb[i][5]);
-          w.w = pack_bf16x2(sb[i][6], sb[i][7]);
-        } else {
-          w.x = __float_as_uint(sb[i][0]);
-          w.y = __float_as_uint(sb[i][1]);
-          w.z = __float_as_uint(sb[i][2]);
-          w.w = __float_as_uint(sb[i][3]);
-        }
-        *reinterpret_cast<uint4*>(bp + (r0 + RPP * i) * K + c0) = w;
-      }
+    if (mm > 0) {
+      fold_stage<EPC, PASSES, RPP, Q>(s, &dm_s[0], &kpm_s[0][0], &u_s[0][0], 0, mm, c0, r0);
+      store_page<BF16, EPC, PASSES, RPP>(s, base + (int64_t)bnd * L.state_stride + (int64_t)h * PAGE,
+                                         c0, r0);
     }
   }
+  fold_stage<EPC, PASSES, RPP, Q>(s, &dn_s[0], &kp_s[0][0], &u_s[0][0], mm, ne, c0, r0);
+  store_page<BF16, EPC, PASSES, RPP>(s, base + (int64_t)dst * L.state_stride + (int64_t)h * PAGE,
+                                     c0, r0);
 }
 
 template <bool BF16, bool ALIGN>

@@ -365,6 +365,27 @@ def main():
             "algorithmic_bytes_per_launch": int(fused_total),
         },
     }
+    # The in-place read+write ceiling of this pool in the fused kernel's access
+    # pattern (every named page loaded and stored back unchanged).
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(2):
+        kda.kda_page_rw_probe(heads=H, batch=B, state=state, state_slot_stride=state_stride,
+                              state_indices=slots)
+    pe[0].record()
+    for _ in range(10):
+        kda.kda_page_rw_probe(heads=H, batch=B, state=state, state_slot_stride=state_stride,
+                              state_indices=slots)
+    pe[1].record()
+    torch.cuda.synchronize()
+    probe_ms = pe[0].elapsed_time(pe[1]) / 10
+    probe_bytes = 2 * int((sl_h > 0).sum()) * H * V * K * 4
+    ceiling = probe_bytes / (probe_ms * 1e-3) / 1e9
+    result["rw_ceiling"] = {
+        "kernel": "kda_page_rw_probe", "gbs": round(ceiling, 1),
+        "pct_of_peak": round(100 * ceiling / HBM_PEAK_GBS, 2), "ms": round(probe_ms, 4),
+        "fused_frac_of_ceiling": round(achieved / ceiling, 4),
+        "commit_frac_of_ceiling": round(commit_total / (commit_mean_ms * 1e-3) / 1e9 / ceiling, 4),
+    }
     if args.copy_probe:
         src = torch.empty(1 << 29, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

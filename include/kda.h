@@ -212,6 +212,19 @@ int kda_flush_plan(int batch, int spec_query_len, const int32_t* state_indices,
                    int32_t* final_indices, int32_t* boundaries, int32_t* boundary_lens,
                    int null_slot, void* stream);
 
+/*
+ * kda_page_rw_probe — measurement aid, not a step of the method: loads every
+ * page of every named slot (state_indices[b] > null_slot, all heads) and stores
+ * it back unchanged, in the fused kernel's access pattern (16x16 tiles, one
+ * 16-byte load and store per lane and tile, one workgroup per page). Its rate
+ * is the in-place read+write ceiling of the pool on the running GPU; the
+ * benchmark reports its kernels against it next to the HBM peak. The pool's
+ * contents are unchanged. Arguments as kda_fused_replay_verify's state,
+ * state_slot_stride, state_indices and null_slot.
+ */
+int kda_page_rw_probe(int heads, int batch, float* state, int64_t state_slot_stride,
+                      const int32_t* state_indices, int null_slot, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

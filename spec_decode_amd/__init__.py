@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "kda_decay", "kda_commit", "kda_verify", "kda_fused_replay_verify",
     "kda_defer_commit", "kda_flush_plan", "kda_last_error", "kda_abi_version",
+    "kda_page_rw_probe",
     "library_path", "KdaError", "KDA_STATE_F32", "KDA_STATE_BF16",
 ]
 
@@ -53,6 +54,7 @@ _SIGS = {
                                      _p, _i, _p, _p, _i, _p, _p, _p, _p]),
     "kda_defer_commit": (_i, [_i, _p, _p, _p, _p, _p, _i, _p]),
     "kda_flush_plan": (_i, [_i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
+    "kda_page_rw_probe": (_i, [_i, _i, _p, _i64, _p, _i, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -210,3 +212,13 @@ def kda_flush_plan(*, batch: int, spec_query_len: int, state_indices, record_row
                                _ptr(boundaries, i32, "boundaries"),
                                _ptr(boundary_lens, i32, "boundary_lens"), int(null_slot),
                                _stream(stream, commit_lens)))
+
+
+def kda_page_rw_probe(*, heads: int, batch: int, state, state_slot_stride: int, state_indices,
+                      null_slot: int = 0, stream=None):
+    """Measurement aid: read and rewrite every named page unchanged (the pool's
+    in-place read+write ceiling in the fused kernel's access pattern)."""
+    _check(_lib.kda_page_rw_probe(heads, batch, _ptr(state, torch.float32, "state"),
+                                  int(state_slot_stride),
+                                  _ptr(state_indices, torch.int32, "state_indices"),
+                                  int(null_slot), _stream(stream, state)))

@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["abi.hip", "plan.hip", "decay.hip", "commit.hip", "fused.hip"]
+SOURCES = ["abi.hip", "plan.hip", "decay.hip", "commit.hip", "fused.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -255,4 +255,18 @@ int kda_flush_plan(int batch, int spec_query_len, const int32_t* state_indices,
                   "kda_flush_plan");
 }
 
+int kda_page_rw_probe(int heads, int batch, float* state, int64_t state_slot_stride,
+                      const int32_t* state_indices, int null_slot, void* stream) {
+  KDA_REQUIRE(heads >= 1 && heads <= 65535, "kda_page_rw_probe: heads must be in 1..65535");
+  KDA_REQUIRE(batch >= 0 && batch <= 65535, "kda_page_rw_probe: batch must be in 0..65535");
+  if (batch == 0) return ok();
+  KDA_REQUIRE(state && state_indices, "kda_page_rw_probe: null pointer argument");
+  KDA_REQUIRE(aligned16(state), "kda_page_rw_probe: state must be 16-byte aligned");
+  KDA_REQUIRE(state_slot_stride >= heads * kPage && state_slot_stride % 4 == 0,
+              "kda_page_rw_probe: state_slot_stride must be >= heads*128*128 and a multiple of 4");
+  return launched(kda::launch_page_rw(state, state_slot_stride, state_indices, batch, heads,
+                                      null_slot, reinterpret_cast<hipStream_t>(stream)),
+                  "kda_page_rw_probe");
+}
+
 }  // extern "C"

@@ -163,6 +163,8 @@ hipError_t launch_commit(const CommitParams& p, int window, bool bf16, bool alig
                          int layers, hipStream_t stream);
 hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, int batch,
                          hipStream_t stream);
+hipError_t launch_page_rw(float* state, int64_t slot_stride, const int32_t* slots, int batch,
+                          int heads, int null_slot, hipStream_t stream);
 hipError_t launch_defer(int batch, const int32_t* state_indices, int32_t* commit_lens,
                         const int32_t* record_rows, int32_t* pending, const int32_t* eager,
                         int null_slot, hipStream_t stream);

@@ -229,3 +229,18 @@ def test_fused_padded_slot_stride():
                     corr=corr.numpy().copy(), kg=W.bits(kg), a_log=a_log[0].numpy(),
                     dt_bias=dtb[0].numpy(), win=win, rows=rows, pending=pending, stride=stride,
                     label="fused padded stride")
+
+
+def test_page_rw_probe_leaves_pool_unchanged():
+    import spec_decode_amd as kda
+
+    H, B, S = 3, 5, 8
+    g = W._gen(66)
+    state = W.draw_state(67, S * H * V * K, torch.float32).to(DEV)
+    before = state.clone()
+    slots = dev(np.array([3, 0, 7, 1, 5], np.int32))
+    announce("page_rw_probe H=3 B=5")
+    kda.kda_page_rw_probe(heads=H, batch=B, state=state, state_slot_stride=H * V * K,
+                          state_indices=slots)
+    torch.cuda.synchronize()
+    assert torch.equal(state.view(torch.int32), before.view(torch.int32))

@@ -61,7 +61,7 @@ def _load():
                              d, i, _i64p, l, i]),
         "kda_o_verify": (i, [i, i, i, i, i, _u16p, _u16p, _u16p, _u16p, _u16p, _fp, _fp,
                              d, _fp, ctypes.c_int64, _i32p, i, _fp, _u16p, i, _i32p,
-                             _i32p, i, _u16p, _i64p, l, i]),
+                             _i32p, i, _u16p, _i64p, l, i, _u16p, _fp, d]),
         "kda_o_decay_buf": (None, [l, i, i, _u16p, _fp, _fp, d, _fp]),
         "kda_o_defer": (None, [i, _i32p, _i32p, _i32p, _i32p, _i32p, i]),
         "kda_o_flush_plan": (None, [i, i, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
@@ -250,7 +250,8 @@ def commit(*, heads, window, batch, key_dim=128, value_dim=128, state_bf16,
 def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
                 dt_bias, lower_bound, state, state_slot_stride, state_indices,
                 corr, kg, record_tokens, record_rows, pending, out, null_slot,
-                key_dim, value_dim, items, threads):
+                key_dim, value_dim, items, threads, gate=None, norm_weight=None,
+                norm_eps=1e-5):
     _check_inplace(state, np.float32, "state")
     _check_inplace(corr, np.float32, "corr")
     _check_inplace(kg, np.uint16, "kg")
@@ -263,32 +264,39 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
     rows = None if record_rows is None else _c(record_rows, np.int32)
     pend = None if pending is None else _c(pending, np.int32)
     ip, ni, _keep = _items_arg(items)
+    gt = None if gate is None else _c(gate, np.uint16)
+    nw = None if norm_weight is None else _c(norm_weight, np.float32)
     _load().kda_o_verify(
         heads, tokens, batch, key_dim, value_dim, _ptr(q, _u16p), _ptr(k, _u16p),
         _ptr(v, _u16p), _ptr(g, _u16p), _ptr(rb, _u16p), _ptr(a_log, _fp),
         _ptr(dt_bias, _fp), float(lower_bound), _ptr(state, _fp), int(state_slot_stride),
         _ptr(slots, _i32p), int(null_slot), _ptr(corr, _fp), _ptr(kg, _u16p),
         int(record_tokens), _ptr(rows, _i32p), _ptr(pend, _i32p), int(fused),
-        _ptr(out, _u16p), ip, ni, default_threads() if threads is None else int(threads))
+        _ptr(out, _u16p), ip, ni, default_threads() if threads is None else int(threads),
+        _ptr(gt, _u16p), _ptr(nw, _fp), float(norm_eps))
 
 
 def verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log, dt_bias,
            lower_bound, state, state_slot_stride, state_indices, corr, kg,
            record_tokens, out, record_rows=None, null_slot=0, key_dim=128,
-           value_dim=128, items=None, threads=None):
-    """Stock verify: o and records; the state is never written."""
+           value_dim=128, items=None, threads=None, gate=None, norm_weight=None,
+           norm_eps=1e-5):
+    """Stock verify: o (or, with gate and norm_weight, the gated RMSNorm of o)
+    and records; the state is never written."""
     _verify_buf(False, heads=heads, tokens=tokens, batch=batch, q=q, k=k, v=v,
                 raw_g=raw_g, raw_beta=raw_beta, a_log=a_log, dt_bias=dt_bias,
                 lower_bound=lower_bound, state=state, state_slot_stride=state_slot_stride,
                 state_indices=state_indices, corr=corr, kg=kg, record_tokens=record_tokens,
                 record_rows=record_rows, pending=None, out=out, null_slot=null_slot,
-                key_dim=key_dim, value_dim=value_dim, items=items, threads=threads)
+                key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
+                gate=gate, norm_weight=norm_weight, norm_eps=norm_eps)
 
 
 def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
                         dt_bias, lower_bound, state, state_slot_stride, state_indices,
                         corr, kg, record_tokens, record_rows, pending, out, null_slot=0,
-                        key_dim=128, value_dim=128, items=None, threads=None):
+                        key_dim=128, value_dim=128, items=None, threads=None, gate=None,
+                        norm_weight=None, norm_eps=1e-5):
     """Replay the pending tokens from the old records (writing S_n when n > 0),
     then the stock verify from S_n, rewriting the records."""
     if record_rows is None or pending is None:
@@ -298,7 +306,8 @@ def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log
                 lower_bound=lower_bound, state=state, state_slot_stride=state_slot_stride,
                 state_indices=state_indices, corr=corr, kg=kg, record_tokens=record_tokens,
                 record_rows=record_rows, pending=pending, out=out, null_slot=null_slot,
-                key_dim=key_dim, value_dim=value_dim, items=items, threads=threads)
+                key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
+                gate=gate, norm_weight=norm_weight, norm_eps=norm_eps)
 
 
 def decay_buf(raw_g, a_log, dt_bias, lower_bound):

@@ -436,7 +436,28 @@ struct verify_ctx {
   const int32_t* pending;
   uint16_t* out;
   const int64_t* items;
+  const uint16_t* gate;  /* optional gated RMSNorm epilogue */
+  const float* norm_w;
+  double norm_eps;
 };
+
+/* Gated RMSNorm of one token's outputs ([fused page] KdaFused.kernel, the
+ * output stage): o is first rounded to BF16 (a stock rounding point); then
+ * rstd = 1 / sqrt(mean_v(o_bf^2) + eps) and out = o_bf * rstd * w[v] * sigmoid(gate[v]). */
+static void gated_rmsnorm(int V, const double* o, const uint16_t* gate, const float* w,
+                          double eps, uint16_t* out) {
+  double ss = 0.0;
+  for (int v = 0; v < V; ++v) {
+    double ob = kda_o_bf16_to_double(kda_o_double_to_bf16(o[v]));
+    ss += ob * ob;
+  }
+  double rstd = 1.0 / sqrt(ss / (double)V + eps);
+  for (int v = 0; v < V; ++v) {
+    double ob = kda_o_bf16_to_double(kda_o_double_to_bf16(o[v]));
+    double gv = kda_o_sigmoid(kda_o_bf16_to_double(gate[v]));
+    out[v] = kda_o_double_to_bf16(ob * rstd * (double)w[v] * gv);
+  }
+}
 
 static void verify_item(void* p, long it) {
   const struct verify_ctx* c = (const struct verify_ctx*)p;
@@ -514,9 +535,15 @@ static void verify_item(void* p, long it) {
   }
   kda_o_verify_seq(K, V, T, S, qq, kn, vv, d, beta, o, u);
 
-  for (int t = 0; t < T; ++t)
-    for (int v = 0; v < V; ++v)
-      c->out[((int64_t)b * T + t) * H * V + (int64_t)h * V + v] = kda_o_double_to_bf16(o[t * V + v]);
+  for (int t = 0; t < T; ++t) {
+    uint16_t* orow = c->out + ((int64_t)b * T + t) * H * V + (int64_t)h * V;
+    if (c->gate && c->norm_w) {
+      gated_rmsnorm(V, o + t * V, c->gate + ((int64_t)b * T + t) * H * V + (int64_t)h * V,
+                    c->norm_w, c->norm_eps, orow);
+    } else {
+      for (int v = 0; v < V; ++v) orow[v] = kda_o_double_to_bf16(o[t * V + v]);
+    }
+  }
   if (rec >= 0) {
     float* corr = c->corr + (((int64_t)rec * H + h) * RQ) * V;
     uint16_t* kg = c->kg + (((int64_t)rec * H + h) * RQ) * 2 * K;
@@ -547,12 +574,14 @@ int kda_o_verify(int H, int T, int B, int K, int V, const uint16_t* q, const uin
                  int64_t state_slot_stride, const int32_t* state_indices, int null_slot,
                  float* corr, uint16_t* kg, int RQ, const int32_t* record_rows,
                  const int32_t* pending, int fused, uint16_t* out, const int64_t* items,
-                 long n_items, int threads) {
+                 long n_items, int threads, const uint16_t* gate, const float* norm_w,
+                 double norm_eps) {
   struct verify_ctx c = {H,          T,          B,       K,          V,
                          RQ,         fused,      q,       k,          v,
                          raw_g,      raw_beta,   a_log,   dt_bias,    lower_bound,
                          state,      state_slot_stride, state_indices, null_slot, corr,
-                         kg,         record_rows, pending, out,       items};
+                         kg,         record_rows, pending, out,       items,
+                         gate,       norm_w,     norm_eps};
   long count = items ? n_items : (long)B * H;
   parallel_for(count, threads, verify_item, &c);
   return 0;

@@ -302,3 +302,81 @@ def test_fused_pending_clamped_to_record_capacity():
         assert np.array_equal(a, b)
     mid = run(RQ - 1, 1)
     assert not np.array_equal(mid[0], ref[0])  # the clamp point matters
+
+
+# --------------------------------------------------------------------------
+# Gated RMSNorm output stage (fused page, KdaFused output stage)
+# --------------------------------------------------------------------------
+
+def _gated_run(c, H, B, T, RQ, state, v_scale=1.0, gate_val=None, w=None, eps=0.0, seed=3):
+    win = c["window"]
+    g = W._gen(seed)
+    gate = W.bits(W.bf16(W.normal(g, (B * T, H * V)))) if gate_val is None else \
+        np.full((B * T, H * V), W.bits(torch.tensor([gate_val]).to(torch.bfloat16))[0], np.uint16)
+    wv = np.ones(V, np.float32) if w is None else w
+    vbits = W.bits((win.v.float() * v_scale).to(torch.bfloat16))
+    out = np.zeros((B * T, H * V), np.uint16)
+    oracle.verify(heads=H, tokens=T, batch=B, q=_np(win.q), k=_np(win.k), v=vbits,
+                  raw_g=_np(win.raw_g), raw_beta=_np(win.raw_beta), a_log=_np(c["a_log"])[0],
+                  dt_bias=_np(c["dt_bias"])[0], lower_bound=W.LOWER_BOUND, state=state,
+                  state_slot_stride=H * V * K, state_indices=_np(c["state_indices"]),
+                  corr=_np(c["corr"]), kg=_np(c["kg"]), record_tokens=RQ, out=out,
+                  record_rows=_np(c["record_rows"]), gate=gate, norm_weight=wv, norm_eps=eps)
+    return out
+
+
+def test_gated_rmsnorm_scale_invariance_exact():
+    """With eps = 0 the output is invariant under scaling the state and v by 2:
+    o scales by 2 exactly, BF16 rounding commutes with it, rstd halves exactly."""
+    H, B, T, RQ = 2, 3, 4, 4
+    c = _case(seed=31, H=H, B=B, T=T, RQ=RQ, slots=5, null_rows=(2,))
+    s0 = _np(c["state"])
+    a = _gated_run(c, H, B, T, RQ, s0.copy())
+    b = _gated_run(c, H, B, T, RQ, (s0 * 2.0).astype(np.float32), v_scale=2.0)
+    assert np.array_equal(a, b)
+    assert np.all(a[2 * T:3 * T] == 0)  # the null-slot request: zeros
+    assert np.count_nonzero(a[:2 * T]) > 0.9 * a[:2 * T].size
+
+
+def test_gated_rmsnorm_unit_rms_and_gate_half():
+    """Saturated gate (sigmoid(60) == 1 in FP64), unit weight, eps = 0: every
+    (token, head) output row has mean square 1 up to BF16 rounding. Gate 0
+    halves every output exactly (sigmoid(0) = 1/2 and halving is exact)."""
+    H, B, T, RQ = 2, 2, 3, 3
+    c = _case(seed=32, H=H, B=B, T=T, RQ=RQ, slots=4)
+    s0 = _np(c["state"])
+    full = _gated_run(c, H, B, T, RQ, s0.copy(), gate_val=60.0)
+    half = _gated_run(c, H, B, T, RQ, s0.copy(), gate_val=0.0)
+    f = oracle.bf16_to_f64(full).reshape(B * T, H, V)
+    ms = (f * f).mean(axis=2)
+    assert np.allclose(ms, 1.0, atol=3e-3)  # BF16 output rounding moves it by ~1e-3 at most here
+    assert np.array_equal(oracle.bf16_to_f64(half), oracle.bf16_to_f64(full) * 0.5)
+
+
+def test_gated_rmsnorm_weight_scales_channels():
+    """A weight of 2 on one channel doubles that channel's output exactly and
+    leaves the others (the mean is over o, not over the weighted output)."""
+    H, B, T, RQ = 1, 2, 2, 2
+    c = _case(seed=33, H=H, B=B, T=T, RQ=RQ, slots=3)
+    s0 = _np(c["state"])
+    w = np.ones(V, np.float32)
+    base = _gated_run(c, H, B, T, RQ, s0.copy(), w=w, eps=1e-5)
+    w2 = w.copy()
+    w2[17] = 2.0
+    two = _gated_run(c, H, B, T, RQ, s0.copy(), w=w2, eps=1e-5)
+    bv, tv = oracle.bf16_to_f64(base), oracle.bf16_to_f64(two)
+    assert np.array_equal(tv[:, 17], 2.0 * bv[:, 17])
+    other = np.arange(V) != 17
+    assert np.array_equal(tv[:, other], bv[:, other])
+
+
+def test_gated_rmsnorm_eps_dominated_exact():
+    """eps = 2^24, far above mean(o^2): rstd = 2^-12 (1 + O(1e-9)), so with a
+    saturated gate and unit weight the output is the plain BF16 output times
+    2^-12, exactly (a power-of-two scale of a BF16 value needs no rounding)."""
+    H, B, T, RQ = 2, 2, 3, 3
+    c = _case(seed=34, H=H, B=B, T=T, RQ=RQ, slots=4)
+    s0 = _np(c["state"])
+    gated = _gated_run(c, H, B, T, RQ, s0.copy(), gate_val=60.0, eps=2.0 ** 24)
+    _, _, _, plain = _run_verify(c, H, B, T, RQ, False, state=s0.copy())
+    assert np.array_equal(oracle.bf16_to_f64(gated), oracle.bf16_to_f64(plain) * 2.0 ** -12)

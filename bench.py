@@ -46,6 +46,8 @@ def parse_args():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-requests", type=int, default=512,
                     help="requests of the batch the CPU baseline runs (all 64 heads each)")
+    ap.add_argument("--gated-output", action="store_true",
+                    help="run the fused step with the gated RMSNorm output stage on")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 2 GiB device copy (streaming ceiling)")
     return ap.parse_args()
@@ -79,8 +81,9 @@ def measured_traffic(name, digest):
 
 # ----------------------------------------------------------------- accounting
 
-def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0):
-    """Algorithmic bytes of one fused launch: (state bytes, total bytes)."""
+def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False):
+    """Algorithmic bytes of one fused launch: (state bytes, total bytes). The
+    gated output stage reads q*256 B of gates per live item."""
     page = V * K * 4
     state = total = 0
     for b in range(len(slots)):
@@ -94,6 +97,7 @@ def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0):
         t += (T * (V * 4 + 2 * K * 2)) if r >= 0 else 0  # new records written
         t += T * (3 * K * 2 + V * 2) + T * 2        # q, k, raw_g, v, raw_beta
         t += T * V * 2                              # o
+        t += T * V * 2 if gated else 0              # gate
         state += H * s
         total += H * t
     return state, total
@@ -231,6 +235,11 @@ def main():
     new = w.windows["new"].to(dev)
     prior = w.windows["prior"].to(dev)
     out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=dev)
+    gate = norm_w = None
+    norm_eps = 1e-5
+    if args.gated_output:
+        gate, norm_w, norm_eps = W.draw_output_stage(W._gen(4 + 200), B, T, H)
+        gate, norm_w = gate.to(dev), norm_w.to(dev)
     commit_lens = torch.empty(B, dtype=torch.int32, device=dev)
     flush = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
 
@@ -274,7 +283,8 @@ def main():
                                     dt_bias=dt_bias, lower_bound=lb, state=state,
                                     state_slot_stride=state_stride, state_indices=slots,
                                     corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
-                                    pending=pending, out=out)
+                                    pending=pending, out=out, gate=gate, norm_weight=norm_w,
+                                    norm_eps=norm_eps)
         e[1].record()
         kda.kda_defer_commit(batch=B, state_indices=slots, commit_lens=commit_lens,
                              record_rows=rows, pending=pending)
@@ -304,7 +314,8 @@ def main():
     # Algorithmic bytes from the plan of each step.
     sl_h, rr_h = slots.cpu().numpy(), rows.cpu().numpy()
     plan = simulate_plan(sl_h, rr_h, a["pending"].numpy(), a["accepted"].numpy(), total, T)
-    fb = [fused_bytes(sl_h, rr_h, p, T, RQ, H) for p, _ in plan[args.warmup:]]
+    fb = [fused_bytes(sl_h, rr_h, p, T, RQ, H, gated=args.gated_output)
+          for p, _ in plan[args.warmup:]]
     cb = [commit_bytes(sl_h, l, rr_h, H, RQ) for _, l in plan[args.warmup:]]
     state_bytes = sum(f[0] + c[0] for f, c in zip(fb, cb))
     ms_per_step = wall * 1e3 / args.steps
@@ -338,6 +349,7 @@ def main():
                         "(2 GiB), ~5% no-op rows; step = fused replay+verify, defer, "
                         "flush plan, in-place FP32 commit",
             "global_batch": B, "seq_len": T, "heads": H, "parallelism": "none",
+            "gated_output": bool(args.gated_output),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "items_per_s": round(items / (wall / args.steps), 1),

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 #define KDA_OK 0
 #define KDA_EINVAL 1
@@ -146,6 +146,13 @@ int kda_commit(int layers, int heads, int window, int batch, int state_dtype,
  *   kg                   BF16 records [rows][heads][record_tokens][256]
  *   record_tokens        RQ in tokens..8
  *   record_rows          int32 [batch] or NULL
+ *   gate, norm_weight    the optional gated RMSNorm output stage ([fused page],
+ *                        KdaFused output stage), both NULL to write o itself:
+ *                        gate BF16 [batch*tokens][heads*128], norm_weight FP32 [128]
+ *                        (shared by the heads). Per (token, head), with o_bf = BF16(o),
+ *                        out = BF16(o_bf * rsqrt(mean_v(o_bf^2) + norm_eps)
+ *                                   * norm_weight[v] * sigmoid(gate[v]))
+ *   norm_eps             finite, >= 0 (used with gate)
  *   out                  BF16 [batch*tokens][heads*128]; written
  */
 int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16_t* k,
@@ -153,7 +160,8 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
                const float* a_log, const float* dt_bias, float lower_bound, const float* state,
                int64_t state_slot_stride, const int32_t* state_indices, int null_slot,
                float* corr, uint16_t* kg, int record_tokens, const int32_t* record_rows,
-               uint16_t* out, void* stream);
+               const uint16_t* gate, const float* norm_weight, float norm_eps, uint16_t* out,
+               void* stream);
 
 /*
  * kda_fused_replay_verify — deferred RecoverSSM: the previous step's commit and
@@ -171,6 +179,7 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
  *
  *   record_rows          int32 [batch], required (< 0: no record row)
  *   pending              int32 [rows], indexed by record row
+ *   gate, norm_weight, norm_eps   the optional output stage, as kda_verify
  */
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             const uint16_t* k, const uint16_t* v, const uint16_t* raw_g,
@@ -178,7 +187,9 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             float lower_bound, float* state, int64_t state_slot_stride,
                             const int32_t* state_indices, int null_slot, float* corr,
                             uint16_t* kg, int record_tokens, const int32_t* record_rows,
-                            const int32_t* pending, uint16_t* out, void* stream);
+                            const int32_t* pending, const uint16_t* gate,
+                            const float* norm_weight, float norm_eps, uint16_t* out,
+                            void* stream);
 
 /*
  * kda_defer_commit — the defer step of deferred RecoverSSM ([kernels page],

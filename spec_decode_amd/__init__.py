@@ -49,9 +49,9 @@ _SIGS = {
     "kda_commit": (_i, [_i, _i, _i, _i, _i, _u64a, _i64a, _u64a, _i64a, _u64a, _i64a,
                         _p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p]),
     "kda_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i64, _p, _i,
-                        _p, _p, _i, _p, _p, _p]),
+                        _p, _p, _i, _p, _p, _p, _f, _p, _p]),
     "kda_fused_replay_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i64,
-                                     _p, _i, _p, _p, _i, _p, _p, _p, _p]),
+                                     _p, _i, _p, _p, _i, _p, _p, _p, _p, _f, _p, _p]),
     "kda_defer_commit": (_i, [_i, _p, _p, _p, _p, _p, _i, _p]),
     "kda_flush_plan": (_i, [_i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
     "kda_page_rw_probe": (_i, [_i, _i, _p, _i64, _p, _i, _p]),
@@ -160,24 +160,31 @@ def _verify_args(q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices,
             _ptr(kg, bf, "kg"), _ptr(record_rows, i32, "record_rows"), _ptr(out, bf, "out"))
 
 
+def _gate_args(gate, norm_weight):
+    return (_ptr(gate, torch.bfloat16, "gate"), _ptr(norm_weight, torch.float32, "norm_weight"))
+
+
 def kda_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta, a_log,
                dt_bias, lower_bound: float, state, state_slot_stride: int, state_indices,
                corr, kg, record_tokens: int, out, record_rows=None, null_slot: int = 0,
-               stream=None):
-    """Stock verify: writes out and the records, never the state."""
+               gate=None, norm_weight=None, norm_eps: float = 1e-5, stream=None):
+    """Stock verify: writes out (o, or its gated RMSNorm with gate and
+    norm_weight) and the records, never the state."""
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
         q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
         record_rows, out)
     _check(_lib.kda_verify(heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd,
                            float(lower_bound), ps, int(state_slot_stride), psi, int(null_slot),
-                           pc, pkg, int(record_tokens), prr, po, _stream(stream, state)))
+                           pc, pkg, int(record_tokens), prr, *_gate_args(gate, norm_weight),
+                           float(norm_eps), po, _stream(stream, state)))
     return out
 
 
 def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta,
                             a_log, dt_bias, lower_bound: float, state, state_slot_stride: int,
                             state_indices, corr, kg, record_tokens: int, record_rows, pending,
-                            out, null_slot: int = 0, stream=None):
+                            out, null_slot: int = 0, gate=None, norm_weight=None,
+                            norm_eps: float = 1e-5, stream=None):
     """Replay each request's pending tokens into its page, then verify the window."""
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
         q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
@@ -185,7 +192,8 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
     _check(_lib.kda_fused_replay_verify(
         heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd, float(lower_bound), ps,
         int(state_slot_stride), psi, int(null_slot), pc, pkg, int(record_tokens), prr,
-        _ptr(pending, torch.int32, "pending"), po, _stream(stream, state)))
+        _ptr(pending, torch.int32, "pending"), *_gate_args(gate, norm_weight),
+        float(norm_eps), po, _stream(stream, state)))
     return out
 
 

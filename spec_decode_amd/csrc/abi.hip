@@ -153,8 +153,9 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
                          const float* dt_bias, float lower_bound, float* state,
                          int64_t state_slot_stride, const int32_t* state_indices,
                          int null_slot, float* corr, uint16_t* kg, int record_tokens,
-                         const int32_t* record_rows, const int32_t* pending, uint16_t* out,
-                         void* stream) {
+                         const int32_t* record_rows, const int32_t* pending,
+                         const uint16_t* gate, const float* norm_weight, float norm_eps,
+                         uint16_t* out, void* stream) {
   KDA_REQUIRE(heads >= 1 && heads <= 65535, "%s: heads must be in 1..65535 (got %d)", who,
               heads);
   KDA_REQUIRE(tokens >= 1 && tokens <= KDA_MAX_WINDOW, "%s: tokens must be in 1..8 (got %d)",
@@ -165,6 +166,10 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
               "%s: record_tokens must be in tokens..8 (got %d with tokens %d)", who,
               record_tokens, tokens);
   KDA_REQUIRE(std::isfinite(lower_bound), "%s: lower_bound must be finite", who);
+  KDA_REQUIRE((gate == nullptr) == (norm_weight == nullptr),
+              "%s: gate and norm_weight must be given together", who);
+  KDA_REQUIRE(gate == nullptr || (std::isfinite(norm_eps) && norm_eps >= 0.f),
+              "%s: norm_eps must be finite and >= 0", who);
   if (batch == 0) return ok();
   KDA_REQUIRE(q && k && v && raw_g && raw_beta && a_log && dt_bias && state && state_indices &&
                   corr && kg && out,
@@ -192,6 +197,9 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
   p.corr = corr;
   p.kg = kg;
   p.out = out;
+  p.gate = gate;
+  p.norm_w = norm_weight;
+  p.norm_eps = norm_eps;
   p.rq = record_tokens;
   p.heads = heads;
   p.null_slot = null_slot;
@@ -205,11 +213,12 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
                const float* a_log, const float* dt_bias, float lower_bound, const float* state,
                int64_t state_slot_stride, const int32_t* state_indices, int null_slot,
                float* corr, uint16_t* kg, int record_tokens, const int32_t* record_rows,
-               uint16_t* out, void* stream) {
+               const uint16_t* gate, const float* norm_weight, float norm_eps, uint16_t* out,
+               void* stream) {
   return verify_common("kda_verify", false, heads, tokens, batch, q, k, v, raw_g, raw_beta,
                        a_log, dt_bias, lower_bound, const_cast<float*>(state),
                        state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
-                       record_rows, nullptr, out, stream);
+                       record_rows, nullptr, gate, norm_weight, norm_eps, out, stream);
 }
 
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
@@ -218,11 +227,13 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             float lower_bound, float* state, int64_t state_slot_stride,
                             const int32_t* state_indices, int null_slot, float* corr,
                             uint16_t* kg, int record_tokens, const int32_t* record_rows,
-                            const int32_t* pending, uint16_t* out, void* stream) {
+                            const int32_t* pending, const uint16_t* gate,
+                            const float* norm_weight, float norm_eps, uint16_t* out,
+                            void* stream) {
   return verify_common("kda_fused_replay_verify", true, heads, tokens, batch, q, k, v, raw_g,
                        raw_beta, a_log, dt_bias, lower_bound, state, state_slot_stride,
                        state_indices, null_slot, corr, kg, record_tokens, record_rows, pending,
-                       out, stream);
+                       gate, norm_weight, norm_eps, out, stream);
 }
 
 int kda_defer_commit(int batch, const int32_t* state_indices, int32_t* commit_lens,

@@ -118,7 +118,7 @@ __device__ __forceinline__ void pair_stage_one(const float (&kn)[T], const float
   for (int i = 0; i < PS::R; ++i) part[(i + PS::R * sel) * PS::PARTS + group] = pv[i];
 }
 
-template <int T, bool FUSED>
+template <int T, bool FUSED, bool GATED>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   using PI = Pairs<T>;
   const int h = blockIdx.x;
@@ -161,7 +161,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   __shared__ __attribute__((aligned(16))) float part_s[PI::P2][PairStage<T>::PARTS];
   __shared__ float ssq_s[2][2][MAX_T];  // [new | old keys][wave of the half][token]
   __shared__ float beta_s[MAX_T];
-  __shared__ uint32_t kg_s[T][K];  // raw key | raw gate << 16 of the window, for the records
+  __shared__ uint32_t kg_s[T][K];
+  __shared__ float osq_s[2][T];  // output stage: per-wave sums of o_bf^2  // raw key | raw gate << 16 of the window, for the records
 
   const int c = tid & (K - 1);   // channel / state row of this thread's half
   const bool lower = wave < 2;   // threads 0..127: new tokens; 128..255: records, v, beta
@@ -174,6 +175,15 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // then theirs (their prologue needs the records, which arrive after).
   const float a_log_h = p.a_log[h];
   const float dtb = p.dt_bias[head_row];
+  // Output stage inputs (compiled in only for the gated instances).
+  constexpr bool gated = GATED;
+  float nw = 1.f;
+  uint32_t gtb[T];
+  if constexpr (GATED) {
+    nw = p.norm_w[c];
+#pragma unroll
+    for (int t = 0; t < T; ++t) gtb[t] = p.gate[(tok0 + t) * H * V + head_row];
+  }
   __builtin_amdgcn_sched_barrier(0);
   uint32_t kb[T], gb[T], qb[T];  // lower: new raw key, gate, q bits
   uint32_t vb[T];                // upper: new v bits
@@ -360,6 +370,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   __syncthreads();
 
   // ---- 6. Per state row: the T x T forward substitution, outputs, records.
+  float ob[T];
   if (lower) {
     const int vrow = c;
     float us[T];
@@ -381,7 +392,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         const int ib = PI::b(t, s);
         o = fmaf(pair_s[ib], us[s], o);
       }
-      p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
+      if constexpr (GATED) {
+        // The output stage normalises the BF16-rounded o over the head's rows.
+        ob[t] = bf16_bits_to_f32(f32_to_bf16_bits(o));
+        const float sq = wave_sum(ob[t] * ob[t]);
+        if (lane == 0) osq_s[wave][t] = sq;
+      } else {
+        p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
+      }
     }
     if (rec >= 0) {
       const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
@@ -394,14 +412,27 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       }
     }
   }
+  if constexpr (GATED) {
+    __syncthreads();
+    if (lower) {
+      const float inv_v = 1.0f / V;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float rstd =
+            __builtin_amdgcn_rsqf((osq_s[0][t] + osq_s[1][t]) * inv_v + p.norm_eps);
+        const float sg = sigmoidf_fast(bf16_bits_to_f32(gtb[t]));
+        p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(ob[t] * rstd * nw * sg);
+      }
+    }
+  }
 }
 
-template <bool FUSED>
+template <bool FUSED, bool GATED>
 static hipError_t launch_t(const VerifyParams& p, int tokens, dim3 grid, hipStream_t stream) {
   switch (tokens) {
-#define KDA_VERIFY_CASE(TT)                                                                 \
-  case TT:                                                                                 \
-    hipLaunchKernelGGL((verify_kernel<TT, FUSED>), grid, dim3(256), 0, stream, p);         \
+#define KDA_VERIFY_CASE(TT)                                                                  \
+  case TT:                                                                                  \
+    hipLaunchKernelGGL((verify_kernel<TT, FUSED, GATED>), grid, dim3(256), 0, stream, p);    \
     break;
     KDA_VERIFY_CASE(1)
     KDA_VERIFY_CASE(2)
@@ -421,7 +452,12 @@ static hipError_t launch_t(const VerifyParams& p, int tokens, dim3 grid, hipStre
 hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, int batch,
                          hipStream_t stream) {
   const dim3 grid(p.heads, batch);
-  return fused ? launch_t<true>(p, tokens, grid, stream) : launch_t<false>(p, tokens, grid, stream);
+  const bool gated = p.gate != nullptr;
+  if (fused)
+    return gated ? launch_t<true, true>(p, tokens, grid, stream)
+                 : launch_t<true, false>(p, tokens, grid, stream);
+  return gated ? launch_t<false, true>(p, tokens, grid, stream)
+               : launch_t<false, false>(p, tokens, grid, stream);
 }
 
 }  // namespace kda

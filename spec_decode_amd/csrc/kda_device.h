@@ -151,6 +151,9 @@ struct VerifyParams {
   float* corr;
   uint16_t* kg;
   uint16_t* out;
+  const uint16_t* gate;    // optional gated RMSNorm output stage: [B*T][H*V] BF16
+  const float* norm_w;     // [V] FP32 (with gate)
+  float norm_eps;
   int rq;
   int heads;
   int null_slot;

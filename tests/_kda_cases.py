@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads as W
-from _compare import assert_bf16_close, assert_exact, assert_f32_close
+from _compare import GATED_OUT_ULPS, assert_bf16_close, assert_exact, assert_f32_close
 
 K = V = 128
 DEV = "cuda:0"
@@ -118,7 +118,7 @@ def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_lay
 
 def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, win,
                     rows=None, pending=None, lb=W.LOWER_BOUND, null_slot=0, label="verify",
-                    stride=None, check=True):
+                    stride=None, check=True, gate=None, norm_weight=None, norm_eps=1e-5):
     """All host arrays: state float32 flat, corr float32 [rows,H,RQ,V], kg uint16
     [rows,H,RQ,2K], win a dict of uint16 arrays (q, k, v, raw_g, raw_beta).
     Returns (gpu results, oracle results) as dicts of host arrays."""
@@ -135,7 +135,10 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
                 state=d["state"], state_slot_stride=stride,
                 state_indices=dev(np.asarray(slots, np.int32)), corr=d["corr"], kg=d["kg"],
                 record_tokens=RQ, out=d["out"], null_slot=null_slot,
-                record_rows=None if rows is None else dev(np.asarray(rows, np.int32)))
+                record_rows=None if rows is None else dev(np.asarray(rows, np.int32)),
+                gate=None if gate is None else dev_bf16(gate),
+                norm_weight=None if norm_weight is None else dev(np.asarray(norm_weight, np.float32)),
+                norm_eps=norm_eps)
     if fused:
         kda.kda_fused_replay_verify(pending=dev(np.asarray(pending, np.int32)), **args)
     else:
@@ -148,7 +151,8 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
                  raw_g=win["raw_g"], raw_beta=win["raw_beta"], a_log=a_log, dt_bias=dt_bias,
                  lower_bound=lb, state=ref["state"], state_slot_stride=stride,
                  state_indices=slots, corr=ref["corr"], kg=ref["kg"], record_tokens=RQ,
-                 out=ref["out"], record_rows=rows, null_slot=null_slot)
+                 out=ref["out"], record_rows=rows, null_slot=null_slot, gate=gate,
+                 norm_weight=norm_weight, norm_eps=norm_eps)
     if fused:
         oracle.fused_replay_verify(pending=pending, **oargs)
     else:
@@ -156,7 +160,8 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
     if check:
         compare_verify(gpu, ref, dict(state=state, corr=corr, kg=kg), fused=fused, H=H, B=B,
                        T=T, RQ=RQ, slots=slots, rows=rows, pending=pending, stride=stride,
-                       null_slot=null_slot, label=label)
+                       null_slot=null_slot, label=label,
+                       out_ulps=GATED_OUT_ULPS if gate is not None else 1)
     return gpu, ref
 
 
@@ -180,11 +185,11 @@ def verify_written(*, fused, H, B, T, RQ, slots, rows, pending, stride, null_slo
 
 
 def compare_verify(gpu, ref, orig, *, fused, H, B, T, RQ, slots, rows, pending, stride,
-                   null_slot, label):
+                   null_slot, label, out_ulps=1):
     smask, cmask = verify_written(fused=fused, H=H, B=B, T=T, RQ=RQ, slots=slots, rows=rows,
                                   pending=pending, stride=stride, null_slot=null_slot,
                                   n_state=orig["state"].size, corr_shape=orig["corr"].shape)
-    assert_bf16_close(f"{label} out", gpu["out"], ref["out"])
+    assert_bf16_close(f"{label} out", gpu["out"], ref["out"], out_ulps)
     assert_exact(f"{label} key/gate records", gpu["kg"], ref["kg"])
     assert_f32_close(f"{label} corrections (written)", gpu["corr"][cmask], ref["corr"][cmask])
     assert_exact(f"{label} corrections (untouched)", gpu["corr"][~cmask], orig["corr"][~cmask])

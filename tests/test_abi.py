@@ -55,16 +55,24 @@ def test_rejects_bad_arguments_without_launch(lib):
     lib.kda_verify.restype = ctypes.c_int
     args = [ctypes.c_int(4), ctypes.c_int(9), ctypes.c_int(2)] + [fake] * 7 + [
         ctypes.c_float(-5.0), fake, ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
-        fake, fake, ctypes.c_int(8), P(None), fake, P(None)]
+        fake, fake, ctypes.c_int(8), P(None), P(None), P(None), ctypes.c_float(1e-5), fake,
+        P(None)]
     assert lib.kda_verify(*args) == 1
     assert "tokens must be in 1..8" in _err(lib)
 
     lib.kda_fused_replay_verify.restype = ctypes.c_int
     args = [ctypes.c_int(4), ctypes.c_int(4), ctypes.c_int(2)] + [fake] * 7 + [
         ctypes.c_float(-5.0), fake, ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
-        fake, fake, ctypes.c_int(4), P(None), P(None), fake, P(None)]
+        fake, fake, ctypes.c_int(4), P(None), P(None), P(None), P(None), ctypes.c_float(1e-5),
+        fake, P(None)]
     assert lib.kda_fused_replay_verify(*args) == 1
     assert "record_rows and pending are required" in _err(lib)
+
+    # gate without norm_weight
+    args2 = list(args)
+    args2[18], args2[19], args2[20], args2[21] = fake, fake, fake, P(None)
+    assert lib.kda_fused_replay_verify(*args2) == 1
+    assert "gate and norm_weight" in _err(lib)
 
     # record_tokens below tokens
     args[17] = ctypes.c_int(3)
@@ -74,7 +82,8 @@ def test_rejects_bad_arguments_without_launch(lib):
     # a misaligned state base
     args = [ctypes.c_int(4), ctypes.c_int(4), ctypes.c_int(2)] + [fake] * 7 + [
         ctypes.c_float(-5.0), P(0x1004), ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
-        fake, fake, ctypes.c_int(4), fake, fake, fake, P(None)]
+        fake, fake, ctypes.c_int(4), fake, fake, P(None), P(None), ctypes.c_float(1e-5), fake,
+        P(None)]
     assert lib.kda_fused_replay_verify(*args) == 1
     assert "16-byte aligned" in _err(lib)
 

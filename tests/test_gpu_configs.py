@@ -125,6 +125,25 @@ def test_config2_fused_full():
                     lb=w.lower_bound, label="config2 fused")
 
 
+def test_config2_fused_full_gated_output():
+    """The fused workload with the gated RMSNorm output stage on."""
+    w = W.config2()
+    H, B, T, RQ = w.heads, w.batch, w.tokens, w.record_tokens
+    a = w.arrays
+    state = a["state"].numpy().copy()
+    slots, rows = a["state_indices"].numpy(), a["record_rows"].numpy()
+    corr, kg = a["corr"].numpy().copy(), W.bits(a["kg"])
+    _oracle_prior_records(w, state, corr, kg, slots, rows, T, RQ, H, B)
+    pending = np.zeros(B, np.int32)
+    pending[rows] = a["pending"].numpy()
+    gate, weight, eps = W.draw_output_stage(W._gen(2 + 200), B, T, H)
+    run_verify_case(fused=True, H=H, B=B, T=T, RQ=RQ, state=state, slots=slots, corr=corr,
+                    kg=kg, a_log=a["a_log"][0].numpy(), dt_bias=a["dt_bias"][0].numpy(),
+                    win=window_np(w.windows["new"]), rows=rows, pending=pending,
+                    lb=w.lower_bound, gate=W.bits(gate), norm_weight=weight.numpy(),
+                    norm_eps=eps, label="config2 fused gated output")
+
+
 # ---------------------------------------------------------------- config 3
 
 def test_config3_align_commit_full_size_sampled():

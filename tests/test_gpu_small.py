@@ -244,3 +244,18 @@ def test_page_rw_probe_leaves_pool_unchanged():
                           state_indices=slots)
     torch.cuda.synchronize()
     assert torch.equal(state.view(torch.int32), before.view(torch.int32))
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 8])
+@pytest.mark.parametrize("fused", [False, True])
+def test_gated_output_stage(T, fused):
+    H, B, RQ = 3, 5, 8
+    c = _vf_case(500 + T, H, B, T, RQ, 9, null_rows=(1,), norec_rows=(3,))
+    gate, weight, eps = W.draw_output_stage(W._gen(600 + T), B, T, H)
+    rng = np.random.default_rng(T)
+    pending = rng.integers(0, RQ + 1, B).astype(np.int32)
+    run_verify_case(fused=fused, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
+                    corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                    win=c["win"], rows=c["rows"], pending=pending if fused else None,
+                    gate=W.bits(gate), norm_weight=weight.numpy(), norm_eps=eps,
+                    label=f"gated output fused={fused} T={T}")

@@ -278,6 +278,15 @@ def config4(seed: int = 4, device="cpu") -> Workload:
     return w
 
 
+def draw_output_stage(gen, B: int, T: int, H: int):
+    """Inputs of the gated RMSNorm output stage: gate = BF16(N(0,1)) per output
+    element, weight 1 + N(0, 0.1) per value channel (shared by the heads),
+    eps 1e-5."""
+    gate = bf16(normal(gen, (B * T, H * V)))
+    weight = 1.0 + normal(gen, (V,), 0.1)
+    return gate, weight, 1e-5
+
+
 CONFIGS = {0: config0, 1: config1, 2: config2, 3: config3, 4: config4}
 
 

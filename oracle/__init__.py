@@ -60,8 +60,8 @@ def _load():
                              _fp, _fp, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
                              d, i, _i64p, l, i]),
         "kda_o_verify": (i, [i, i, i, i, i, _u16p, _u16p, _u16p, _u16p, _u16p, _fp, _fp,
-                             d, _fp, ctypes.c_int64, _i32p, i, _fp, _u16p, i, _i32p,
-                             _i32p, i, _u16p, _i64p, l, i, _u16p, _fp, d]),
+                             d, _vp, ctypes.c_int64, _i32p, i, _fp, _u16p, i, _i32p,
+                             _i32p, i, _u16p, _i64p, l, i, _u16p, _fp, d, i]),
         "kda_o_decay_buf": (None, [l, i, i, _u16p, _fp, _fp, d, _fp]),
         "kda_o_defer": (None, [i, _i32p, _i32p, _i32p, _i32p, _i32p, i]),
         "kda_o_flush_plan": (None, [i, i, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
@@ -252,7 +252,8 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
                 corr, kg, record_tokens, record_rows, pending, out, null_slot,
                 key_dim, value_dim, items, threads, gate=None, norm_weight=None,
                 norm_eps=1e-5):
-    _check_inplace(state, np.float32, "state")
+    state_bf16 = isinstance(state, np.ndarray) and state.dtype == np.uint16
+    _check_inplace(state, np.uint16 if state_bf16 else np.float32, "state")
     _check_inplace(corr, np.float32, "corr")
     _check_inplace(kg, np.uint16, "kg")
     _check_inplace(out, np.uint16, "out")
@@ -269,11 +270,12 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
     _load().kda_o_verify(
         heads, tokens, batch, key_dim, value_dim, _ptr(q, _u16p), _ptr(k, _u16p),
         _ptr(v, _u16p), _ptr(g, _u16p), _ptr(rb, _u16p), _ptr(a_log, _fp),
-        _ptr(dt_bias, _fp), float(lower_bound), _ptr(state, _fp), int(state_slot_stride),
+        _ptr(dt_bias, _fp), float(lower_bound), ctypes.c_void_p(state.ctypes.data),
+        int(state_slot_stride),
         _ptr(slots, _i32p), int(null_slot), _ptr(corr, _fp), _ptr(kg, _u16p),
         int(record_tokens), _ptr(rows, _i32p), _ptr(pend, _i32p), int(fused),
         _ptr(out, _u16p), ip, ni, default_threads() if threads is None else int(threads),
-        _ptr(gt, _u16p), _ptr(nw, _fp), float(norm_eps))
+        _ptr(gt, _u16p), _ptr(nw, _fp), float(norm_eps), int(state_bf16))
 
 
 def verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log, dt_bias,
@@ -282,7 +284,8 @@ def verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log, dt_bias,
            value_dim=128, items=None, threads=None, gate=None, norm_weight=None,
            norm_eps=1e-5):
     """Stock verify: o (or, with gate and norm_weight, the gated RMSNorm of o)
-    and records; the state is never written."""
+    and records; the state is never written. The pool is FP32 (float32) or
+    BF16 (uint16 bits), by the dtype of ``state``."""
     _verify_buf(False, heads=heads, tokens=tokens, batch=batch, q=q, k=k, v=v,
                 raw_g=raw_g, raw_beta=raw_beta, a_log=a_log, dt_bias=dt_bias,
                 lower_bound=lower_bound, state=state, state_slot_stride=state_slot_stride,

@@ -421,12 +421,12 @@ int kda_o_commit(int L, int H, int Q, int B, int K, int V, int state_bf16,
  *    raw gate bit copies), after every old record of the item was read.
  * q is used as given; keys are normalised; beta = sigmoid(raw_beta). */
 struct verify_ctx {
-  int H, T, B, K, V, RQ, fused;
+  int H, T, B, K, V, RQ, fused, state_bf16;
   const uint16_t *q, *k, *v, *g, *rb;
   const float* a_log;
   const float* dt_bias;
   double lb;
-  float* state;
+  void* state; /* FP32 or BF16 pool */
   int64_t slot_stride;
   const int32_t* slots;
   int null_slot;
@@ -492,8 +492,8 @@ static void verify_item(void* p, long it) {
   double* o = (double*)malloc(sizeof(double) * (size_t)T * V);
   double* kr = (double*)malloc(sizeof(double) * (size_t)K);
 
-  float* page = c->state + (int64_t)slot * c->slot_stride + (int64_t)h * (int64_t)VK;
-  for (size_t i = 0; i < VK; ++i) S0[i] = (double)page[i];
+  const int64_t page = (int64_t)slot * c->slot_stride + (int64_t)h * (int64_t)VK;
+  for (size_t i = 0; i < VK; ++i) S0[i] = state_get(c->state, c->state_bf16, page + (int64_t)i);
   double a = c->a_log[h];
   const float* dtb = c->dt_bias + (int64_t)h * K;
 
@@ -512,7 +512,7 @@ static void verify_item(void* p, long it) {
       kda_o_knorm(K, kr, kn + t * K);
     }
     kda_o_commit_seq(K, V, n, S0, u, kn, d, S);
-    for (size_t i = 0; i < VK; ++i) page[i] = to_f32(S[i]);
+    for (size_t i = 0; i < VK; ++i) state_put(c->state, c->state_bf16, page + (int64_t)i, S[i]);
   } else {
     memcpy(S, S0, sizeof(double) * VK);
   }
@@ -570,14 +570,14 @@ static void verify_item(void* p, long it) {
 
 int kda_o_verify(int H, int T, int B, int K, int V, const uint16_t* q, const uint16_t* k,
                  const uint16_t* v, const uint16_t* raw_g, const uint16_t* raw_beta,
-                 const float* a_log, const float* dt_bias, double lower_bound, float* state,
+                 const float* a_log, const float* dt_bias, double lower_bound, void* state,
                  int64_t state_slot_stride, const int32_t* state_indices, int null_slot,
                  float* corr, uint16_t* kg, int RQ, const int32_t* record_rows,
                  const int32_t* pending, int fused, uint16_t* out, const int64_t* items,
                  long n_items, int threads, const uint16_t* gate, const float* norm_w,
-                 double norm_eps) {
+                 double norm_eps, int state_bf16) {
   struct verify_ctx c = {H,          T,          B,       K,          V,
-                         RQ,         fused,      q,       k,          v,
+                         RQ,         fused,      state_bf16, q,       k,          v,
                          raw_g,      raw_beta,   a_log,   dt_bias,    lower_bound,
                          state,      state_slot_stride, state_indices, null_slot, corr,
                          kg,         record_rows, pending, out,       items,

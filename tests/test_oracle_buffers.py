@@ -380,3 +380,36 @@ def test_gated_rmsnorm_eps_dominated_exact():
     gated = _gated_run(c, H, B, T, RQ, s0.copy(), gate_val=60.0, eps=2.0 ** 24)
     _, _, _, plain = _run_verify(c, H, B, T, RQ, False, state=s0.copy())
     assert np.array_equal(oracle.bf16_to_f64(gated), oracle.bf16_to_f64(plain) * 2.0 ** -12)
+
+
+def test_fused_bf16_state_matches_fp32_state():
+    """The same BF16-representable pool as BF16 bits and as FP32: the outputs
+    and records are bit-identical (both continue from the FP64 S_n), and the
+    BF16 page written back is the FP32 page's value rounded to nearest even
+    (they differ only by the final store rounding)."""
+    H, B, T, RQ = 2, 4, 3, 5
+    c = _case(seed=41, H=H, B=B, T=T, RQ=RQ, slots=7, null_rows=(3,), no_record_rows=(2,))
+    s_bits = W.bits(c["state"].to(torch.bfloat16))
+    s_f32 = oracle.bf16_to_f64(s_bits).astype(np.float32)
+    rows = _np(c["record_rows"])
+    pend = np.zeros(B, np.int32)
+    for b, n in enumerate([4, 0, 3, 5]):
+        if rows[b] >= 0:
+            pend[rows[b]] = n
+    rb = _run_verify(c, H, B, T, RQ, True, state=s_bits.copy(), pending=pend)
+    rf = _run_verify(c, H, B, T, RQ, True, state=s_f32.copy(), pending=pend)
+    assert np.array_equal(rb[1], rf[1]) and np.array_equal(rb[2], rf[2])  # records
+    assert np.array_equal(rb[3], rf[3])  # outputs
+    got = oracle.bf16_to_f64(rb[0])
+    want = oracle.bf16_to_f64(oracle.round_bf16(rf[0].astype(np.float64)))
+    # float -> bf16 of the FP32 page can differ from double -> bf16 only at an
+    # exact FP32 tie: allow those, nothing else.
+    diff = got != want
+    assert diff.mean() < 1e-3
+    assert np.all(np.abs(got[diff] - want[diff]) <= np.abs(want[diff]) * 2.0 ** -7)
+    # slots nobody names are untouched bit for bit
+    named = set(int(x) for x in _np(c["state_indices"]))
+    pages = rb[0].reshape(-1, H * V * K)
+    for sl in range(pages.shape[0]):
+        if sl not in named:
+            assert np.array_equal(pages[sl], s_bits.reshape(-1, H * V * K)[sl])

@@ -55,7 +55,7 @@ def bf16(x: torch.Tensor) -> torch.Tensor:
 
 def bits(x: torch.Tensor) -> np.ndarray:
     """A BF16 tensor's bit patterns as a uint16 numpy array (host copy)."""
-    return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16).copy()
 
 
 @dataclass

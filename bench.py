@@ -48,6 +48,9 @@ def parse_args():
                     help="requests of the batch the CPU baseline runs (all 64 heads each)")
     ap.add_argument("--gated-output", action="store_true",
                     help="run the fused step with the gated RMSNorm output stage on")
+    ap.add_argument("--state-dtype", choices=("f32", "bf16"), default="f32",
+                    help="element type of the state pool (the workload's is f32; bf16 "
+                         "rounds the same pool to BF16 and commits in BF16)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 2 GiB device copy (streaming ceiling)")
     return ap.parse_args()
@@ -81,10 +84,11 @@ def measured_traffic(name, digest):
 
 # ----------------------------------------------------------------- accounting
 
-def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False):
+def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False, es=4):
     """Algorithmic bytes of one fused launch: (state bytes, total bytes). The
-    gated output stage reads q*256 B of gates per live item."""
-    page = V * K * 4
+    gated output stage reads q*256 B of gates per live item; es is the state
+    element size."""
+    page = V * K * es
     state = total = 0
     for b in range(len(slots)):
         if slots[b] <= null_slot:
@@ -103,9 +107,9 @@ def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False):
     return state, total
 
 
-def commit_bytes(slots, lens, rows, H, Q, null_slot=0):
-    """Algorithmic bytes of one in-place FP32 commit launch: (state, total)."""
-    page = V * K * 4
+def commit_bytes(slots, lens, rows, H, Q, null_slot=0, es=4):
+    """Algorithmic bytes of one in-place commit launch: (state, total)."""
+    page = V * K * es
     state = total = 0
     for b in range(len(slots)):
         n = int(lens[b])
@@ -140,7 +144,7 @@ def simulate_plan(slots, rows, pending0, accepted, steps, q, null_slot=0):
 
 # ----------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(host, H, T, RQ, n_req, lb):
+def cpu_baseline(host, H, T, RQ, n_req, lb, bf16=False):
     """The FP64 oracle on the first n_req live requests (all heads) of the same
     step: fused replay+verify, then the in-place commit of the accepted tokens.
     Reports state GB/s of that sample (the same accounting as the GPU line)."""
@@ -152,7 +156,7 @@ def cpu_baseline(host, H, T, RQ, n_req, lb):
     B = len(pick)
     page = H * V * K
     # A compact copy: request j owns slot j + 1 and record row j.
-    state = np.zeros((B + 1) * page, np.float32)
+    state = np.zeros((B + 1) * page, np.uint16 if bf16 else np.float32)
     for j, b in enumerate(pick):
         state[(j + 1) * page:(j + 2) * page] = host["state_pages"][b]
     sl = np.arange(1, B + 1, dtype=np.int32)
@@ -177,15 +181,16 @@ def cpu_baseline(host, H, T, RQ, n_req, lb):
     pending2 = pend.copy()
     oracle.defer(sl, lens, rr, pending2)
     fl, fin, _, _ = oracle.flush_plan(sl, rr, pending2, T)
-    oracle.commit(heads=H, window=RQ, batch=B, state_bf16=False, state_layers=[state],
+    oracle.commit(heads=H, window=RQ, batch=B, state_bf16=bf16, state_layers=[state],
                   state_slot_strides=[page], corr_layers=[corr], corr_row_strides=[H * RQ * V],
                   kg_layers=[kg], kg_row_strides=[H * RQ * 2 * K],
                   a_log=host["a_log"][None, :], dt_bias=host["dt_bias"][None, :],
                   sources=fin, commit_lens=fl, destinations=fin, record_rows=rr,
                   lower_bound=lb, threads=threads)
     dt = time.perf_counter() - t0
-    fs, _ = fused_bytes(sl, rr, pend, T, RQ, H)
-    cs, _ = commit_bytes(sl, fl, rr, H, RQ)
+    es = 2 if bf16 else 4
+    fs, _ = fused_bytes(sl, rr, pend, T, RQ, H, es=es)
+    cs, _ = commit_bytes(sl, fl, rr, H, RQ, es=es)
     return {
         "value": round((fs + cs) / dt / 1e9, 3),
         "unit": "GB/s",
@@ -223,7 +228,12 @@ def main():
     page = H * V * K
     lb = w.lower_bound
     a = w.arrays
-    state = a["state"]
+    bf16 = args.state_dtype == "bf16"
+    es = 2 if bf16 else 4
+    state = a.pop("state")
+    if bf16:
+        state = state.to(torch.bfloat16)
+        torch.cuda.empty_cache()
     slots = a["state_indices"].to(dev)
     rows = a["record_rows"].to(dev)
     pending = a["pending"].to(dev)
@@ -260,11 +270,15 @@ def main():
                     win={n: getattr(new, n).cpu().view(torch.int16).numpy().view(np.uint16)
                          for n in ("q", "k", "v", "raw_g", "raw_beta")})
         pick = [b for b in range(B) if sl_h[b] > 0][: args.cpu_requests + 32]
-        host["state_pages"] = {b: state[int(sl_h[b]) * page:(int(sl_h[b]) + 1) * page].cpu().numpy()
-                               for b in pick}
+        pages = state.view(torch.int16) if bf16 else state
+        host["state_pages"] = {
+            b: pages[int(sl_h[b]) * page:(int(sl_h[b]) + 1) * page].cpu().numpy().view(
+                np.uint16 if bf16 else np.float32)
+            for b in pick}
 
     state_stride = page
-    commit_args = dict(heads=H, window=RQ, batch=B, state_dtype=kda.KDA_STATE_F32,
+    commit_args = dict(heads=H, window=RQ, batch=B,
+                       state_dtype=kda.KDA_STATE_BF16 if bf16 else kda.KDA_STATE_F32,
                        state_addrs=[state.data_ptr()], state_slot_strides=[state_stride],
                        corr_addrs=[corr.data_ptr()], corr_row_strides=[H * RQ * V],
                        kg_addrs=[kg.data_ptr()], kg_row_strides=[H * RQ * 2 * K],
@@ -314,9 +328,9 @@ def main():
     # Algorithmic bytes from the plan of each step.
     sl_h, rr_h = slots.cpu().numpy(), rows.cpu().numpy()
     plan = simulate_plan(sl_h, rr_h, a["pending"].numpy(), a["accepted"].numpy(), total, T)
-    fb = [fused_bytes(sl_h, rr_h, p, T, RQ, H, gated=args.gated_output)
+    fb = [fused_bytes(sl_h, rr_h, p, T, RQ, H, gated=args.gated_output, es=es)
           for p, _ in plan[args.warmup:]]
-    cb = [commit_bytes(sl_h, l, rr_h, H, RQ) for _, l in plan[args.warmup:]]
+    cb = [commit_bytes(sl_h, l, rr_h, H, RQ, es=es) for _, l in plan[args.warmup:]]
     state_bytes = sum(f[0] + c[0] for f, c in zip(fb, cb))
     ms_per_step = wall * 1e3 / args.steps
     value = state_bytes / wall / 1e9
@@ -328,7 +342,7 @@ def main():
     commit_total = sum(c[1] for c in cb) / len(cb)
     commit_state = sum(c[0] for c in cb) / len(cb)
     achieved = fused_total / (fused_mean_ms * 1e-3) / 1e9
-    traffic = measured_traffic("fused_replay_verify/large_decode",
+    traffic = measured_traffic("fused_replay_verify/large_decode" + ("_bf16" if bf16 else ""),
                                source_digest(FUSED_SOURCES))
 
     result = {
@@ -347,9 +361,13 @@ def main():
         "config": {
             "workload": "large_decode: L=1 H=64 K=V=128 B=512 q=8 FP32 state 512 slots "
                         "(2 GiB), ~5% no-op rows; step = fused replay+verify, defer, "
-                        "flush plan, in-place FP32 commit",
+                        "flush plan, in-place FP32 commit" if not bf16 else
+                        "large_decode with the pool rounded to BF16: L=1 H=64 K=V=128 B=512 "
+                        "q=8 BF16 state 512 slots (1 GiB), ~5% no-op rows; step = fused "
+                        "replay+verify, defer, flush plan, in-place BF16 commit",
             "global_batch": B, "seq_len": T, "heads": H, "parallelism": "none",
             "gated_output": bool(args.gated_output),
+            "state_dtype": args.state_dtype,
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "items_per_s": round(items / (wall / args.steps), 1),
@@ -359,7 +377,7 @@ def main():
                 "state_gbs": round(fused_state / (fused_mean_ms * 1e-3) / 1e9, 1),
                 "total_gbs": round(achieved, 1),
                 "items_per_s": round(items / (fused_mean_ms * 1e-3), 1)},
-            "commit_fp32_inplace": {
+            ("commit_bf16_inplace" if bf16 else "commit_fp32_inplace"): {
                 "mean_ms": round(commit_mean_ms, 4), "min_ms": round(min(commit_ms), 4),
                 "state_gbs": round(commit_state / (commit_mean_ms * 1e-3) / 1e9, 1),
                 "total_gbs": round(commit_total / (commit_mean_ms * 1e-3) / 1e9, 1),
@@ -378,26 +396,30 @@ def main():
         },
     }
     # The in-place read+write ceiling of this pool in the fused kernel's access
-    # pattern (every named page loaded and stored back unchanged).
+    # pattern (every named page loaded and stored back unchanged; FP32 pools).
     pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(2):
-        kda.kda_page_rw_probe(heads=H, batch=B, state=state, state_slot_stride=state_stride,
-                              state_indices=slots)
-    pe[0].record()
-    for _ in range(10):
-        kda.kda_page_rw_probe(heads=H, batch=B, state=state, state_slot_stride=state_stride,
-                              state_indices=slots)
-    pe[1].record()
-    torch.cuda.synchronize()
-    probe_ms = pe[0].elapsed_time(pe[1]) / 10
-    probe_bytes = 2 * int((sl_h > 0).sum()) * H * V * K * 4
-    ceiling = probe_bytes / (probe_ms * 1e-3) / 1e9
-    result["rw_ceiling"] = {
-        "kernel": "kda_page_rw_probe", "gbs": round(ceiling, 1),
-        "pct_of_peak": round(100 * ceiling / HBM_PEAK_GBS, 2), "ms": round(probe_ms, 4),
-        "fused_frac_of_ceiling": round(achieved / ceiling, 4),
-        "commit_frac_of_ceiling": round(commit_total / (commit_mean_ms * 1e-3) / 1e9 / ceiling, 4),
-    }
+    if bf16:
+        pe = None
+    if pe is not None:
+        for _ in range(2):
+            kda.kda_page_rw_probe(heads=H, batch=B, state=state,
+                                  state_slot_stride=state_stride, state_indices=slots)
+        pe[0].record()
+        for _ in range(10):
+            kda.kda_page_rw_probe(heads=H, batch=B, state=state,
+                                  state_slot_stride=state_stride, state_indices=slots)
+        pe[1].record()
+        torch.cuda.synchronize()
+        probe_ms = pe[0].elapsed_time(pe[1]) / 10
+        probe_bytes = 2 * int((sl_h > 0).sum()) * H * V * K * 4
+        ceiling = probe_bytes / (probe_ms * 1e-3) / 1e9
+        result["rw_ceiling"] = {
+            "kernel": "kda_page_rw_probe", "gbs": round(ceiling, 1),
+            "pct_of_peak": round(100 * ceiling / HBM_PEAK_GBS, 2), "ms": round(probe_ms, 4),
+            "fused_frac_of_ceiling": round(achieved / ceiling, 4),
+            "commit_frac_of_ceiling": round(
+                commit_total / (commit_mean_ms * 1e-3) / 1e9 / ceiling, 4),
+        }
     if args.copy_probe:
         src = torch.empty(1 << 29, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -413,7 +435,7 @@ def main():
                                 "gbs": round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}
         del src, dst
     if host is not None:
-        result["cpu_baseline"] = cpu_baseline(host, H, T, RQ, args.cpu_requests, lb)
+        result["cpu_baseline"] = cpu_baseline(host, H, T, RQ, args.cpu_requests, lb, bf16)
     print(json.dumps(result), flush=True)
 
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 #define KDA_OK 0
 #define KDA_EINVAL 1
@@ -125,7 +125,7 @@ int kda_commit(int layers, int heads, int window, int batch, int state_dtype,
  * kda_recoverssm_verify; the recurrence of the [fused page] module docstring).
  * For every (request b, head h) with slot = state_indices[b]:
  *  - slot <= null_slot: out rows of the item are zero; nothing else is written;
- *  - otherwise, from S = state page (FP32), for t < tokens:
+ *  - otherwise, from S = state page (FP32, or BF16 widened exactly), for t < tokens:
  *        S <- S diag(d_t);  u_t = beta_t (v_t - S kn_t);  S <- S + u_t kn_t^T;  o_t = S q_t
  *    computed in the chunked (WY) form from the unmodified page; o_t -> out
  *    (BF16); with beta_t = sigmoid(raw_beta), kn_t the L2-normalised key, q_t
@@ -139,8 +139,11 @@ int kda_commit(int layers, int heads, int window, int batch, int state_dtype,
  *   v                    BF16 [batch*tokens][heads][128], contiguous
  *   raw_beta             BF16 [batch*tokens][heads]
  *   a_log                FP32 [heads];  dt_bias  FP32 [heads][128]
- *   state                FP32 pool [slots][heads][128][128]; read only
- *   state_slot_stride    elements between slots (>= heads*128*128, multiple of 4)
+ *   state_dtype          KDA_STATE_F32 or KDA_STATE_BF16: the element type of state
+ *   state                pool [slots][heads][128][128] of state_dtype (BF16 as bits);
+ *                        read only
+ *   state_slot_stride    elements between slots (>= heads*128*128; slots 16-byte
+ *                        aligned: a multiple of 4 for FP32, of 8 for BF16)
  *   state_indices        int32 [batch]
  *   corr                 FP32 records [rows][heads][record_tokens][128]
  *   kg                   BF16 records [rows][heads][record_tokens][256]
@@ -157,21 +160,23 @@ int kda_commit(int layers, int heads, int window, int batch, int state_dtype,
  */
 int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16_t* k,
                const uint16_t* v, const uint16_t* raw_g, const uint16_t* raw_beta,
-               const float* a_log, const float* dt_bias, float lower_bound, const float* state,
-               int64_t state_slot_stride, const int32_t* state_indices, int null_slot,
-               float* corr, uint16_t* kg, int record_tokens, const int32_t* record_rows,
-               const uint16_t* gate, const float* norm_weight, float norm_eps, uint16_t* out,
-               void* stream);
+               const float* a_log, const float* dt_bias, float lower_bound, int state_dtype,
+               const void* state, int64_t state_slot_stride, const int32_t* state_indices,
+               int null_slot, float* corr, uint16_t* kg, int record_tokens,
+               const int32_t* record_rows, const uint16_t* gate, const float* norm_weight,
+               float norm_eps, uint16_t* out, void* stream);
 
 /*
  * kda_fused_replay_verify — deferred RecoverSSM: the previous step's commit and
- * this step's verify in one pass over the FP32 state ([fused page], module
+ * this step's verify in one pass over the state ([fused page], module
  * docstring and KdaFused). Arguments as kda_verify, plus `pending`; state is
  * read and written. For every (request b, head h) with slot > null_slot:
  *  1. r = record_rows[b]; n = clamp(pending[r], 0, record_tokens) if r >= 0,
  *     else 0; the n recorded tokens of row r are replayed onto the page in the
- *     commit's closed form and S_n is written back to the same page when n > 0;
- *  2. the window is verified from S_n exactly as kda_verify does;
+ *     commit's closed form (FP32 arithmetic) and S_n is written back to the same
+ *     page when n > 0 (a BF16 pool stores S_n rounded to nearest even);
+ *  2. the window is verified from S_n (the FP32 value, before any rounding to
+ *     the pool's type) exactly as kda_verify does;
  *  3. r >= 0: the records of row r are rewritten for t < tokens, after every
  *     old record of the item was read.
  * pending is read only (the defer step of the next step rewrites it). Each
@@ -184,8 +189,9 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             const uint16_t* k, const uint16_t* v, const uint16_t* raw_g,
                             const uint16_t* raw_beta, const float* a_log, const float* dt_bias,
-                            float lower_bound, float* state, int64_t state_slot_stride,
-                            const int32_t* state_indices, int null_slot, float* corr,
+                            float lower_bound, int state_dtype, void* state,
+                            int64_t state_slot_stride, const int32_t* state_indices,
+                            int null_slot, float* corr,
                             uint16_t* kg, int record_tokens, const int32_t* record_rows,
                             const int32_t* pending, const uint16_t* gate,
                             const float* norm_weight, float norm_eps, uint16_t* out,

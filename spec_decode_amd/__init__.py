@@ -48,9 +48,9 @@ _SIGS = {
     "kda_decay": (_i, [_p, _i64, _i, _p, _p, _f, _p, _p]),
     "kda_commit": (_i, [_i, _i, _i, _i, _i, _u64a, _i64a, _u64a, _i64a, _u64a, _i64a,
                         _p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p]),
-    "kda_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i64, _p, _i,
+    "kda_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _i64, _p, _i,
                         _p, _p, _i, _p, _p, _p, _f, _p, _p]),
-    "kda_fused_replay_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _p, _i64,
+    "kda_fused_replay_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _i64,
                                      _p, _i, _p, _p, _i, _p, _p, _p, _p, _f, _p, _p]),
     "kda_defer_commit": (_i, [_i, _p, _p, _p, _p, _p, _i, _p]),
     "kda_flush_plan": (_i, [_i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
@@ -155,9 +155,18 @@ def _verify_args(q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices,
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     return (_ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"), _ptr(raw_g, bf, "raw_g"),
             _ptr(raw_beta, bf, "raw_beta"), _ptr(a_log, f32, "a_log"),
-            _ptr(dt_bias, f32, "dt_bias"), _ptr(state, f32, "state"),
+            _ptr(dt_bias, f32, "dt_bias"), _ptr(state, None, "state"),
             _ptr(state_indices, i32, "state_indices"), _ptr(corr, f32, "corr"),
             _ptr(kg, bf, "kg"), _ptr(record_rows, i32, "record_rows"), _ptr(out, bf, "out"))
+
+
+def _state_dtype(state) -> int:
+    """KDA_STATE_F32 for a float32 pool, KDA_STATE_BF16 for a bfloat16 one."""
+    if state.dtype == torch.float32:
+        return KDA_STATE_F32
+    if state.dtype == torch.bfloat16:
+        return KDA_STATE_BF16
+    raise TypeError(f"state must be float32 or bfloat16 (got {state.dtype})")
 
 
 def _gate_args(gate, norm_weight):
@@ -169,12 +178,14 @@ def kda_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta,
                corr, kg, record_tokens: int, out, record_rows=None, null_slot: int = 0,
                gate=None, norm_weight=None, norm_eps: float = 1e-5, stream=None):
     """Stock verify: writes out (o, or its gated RMSNorm with gate and
-    norm_weight) and the records, never the state."""
+    norm_weight) and the records, never the state. The pool's element type
+    (float32 or bfloat16) is that of ``state``."""
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
         q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
         record_rows, out)
     _check(_lib.kda_verify(heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd,
-                           float(lower_bound), ps, int(state_slot_stride), psi, int(null_slot),
+                           float(lower_bound), _state_dtype(state), ps, int(state_slot_stride),
+                           psi, int(null_slot),
                            pc, pkg, int(record_tokens), prr, *_gate_args(gate, norm_weight),
                            float(norm_eps), po, _stream(stream, state)))
     return out
@@ -185,12 +196,14 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
                             state_indices, corr, kg, record_tokens: int, record_rows, pending,
                             out, null_slot: int = 0, gate=None, norm_weight=None,
                             norm_eps: float = 1e-5, stream=None):
-    """Replay each request's pending tokens into its page, then verify the window."""
+    """Replay each request's pending tokens into its page, then verify the
+    window. The pool's element type (float32 or bfloat16) is that of ``state``."""
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
         q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
         record_rows, out)
     _check(_lib.kda_fused_replay_verify(
-        heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd, float(lower_bound), ps,
+        heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd, float(lower_bound),
+        _state_dtype(state), ps,
         int(state_slot_stride), psi, int(null_slot), pc, pkg, int(record_tokens), prr,
         _ptr(pending, torch.int32, "pending"), *_gate_args(gate, norm_weight),
         float(norm_eps), po, _stream(stream, state)))

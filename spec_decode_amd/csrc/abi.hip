@@ -150,8 +150,8 @@ int kda_commit(int layers, int heads, int window, int batch, int state_dtype,
 static int verify_common(const char* who, bool fused, int heads, int tokens, int batch,
                          const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* raw_g, const uint16_t* raw_beta, const float* a_log,
-                         const float* dt_bias, float lower_bound, float* state,
-                         int64_t state_slot_stride, const int32_t* state_indices,
+                         const float* dt_bias, float lower_bound, int state_dtype,
+                         void* state, int64_t state_slot_stride, const int32_t* state_indices,
                          int null_slot, float* corr, uint16_t* kg, int record_tokens,
                          const int32_t* record_rows, const int32_t* pending,
                          const uint16_t* gate, const float* norm_weight, float norm_eps,
@@ -166,6 +166,8 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
               "%s: record_tokens must be in tokens..8 (got %d with tokens %d)", who,
               record_tokens, tokens);
   KDA_REQUIRE(std::isfinite(lower_bound), "%s: lower_bound must be finite", who);
+  KDA_REQUIRE(state_dtype == KDA_STATE_F32 || state_dtype == KDA_STATE_BF16,
+              "%s: state_dtype must be KDA_STATE_F32 or KDA_STATE_BF16", who);
   KDA_REQUIRE((gate == nullptr) == (norm_weight == nullptr),
               "%s: gate and norm_weight must be given together", who);
   KDA_REQUIRE(gate == nullptr || (std::isfinite(norm_eps) && norm_eps >= 0.f),
@@ -178,9 +180,12 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
     KDA_REQUIRE(record_rows && pending, "%s: record_rows and pending are required", who);
   KDA_REQUIRE(aligned16(state) && aligned16(out),
               "%s: state and out must be 16-byte aligned", who);
-  KDA_REQUIRE(state_slot_stride >= heads * kPage && state_slot_stride % 4 == 0,
-              "%s: state_slot_stride %lld must be >= heads*128*128 and a multiple of 4", who,
-              (long long)state_slot_stride);
+  const bool bf16 = state_dtype == KDA_STATE_BF16;
+  const int64_t es = bf16 ? 2 : 4;
+  KDA_REQUIRE(state_slot_stride >= heads * kPage && (state_slot_stride * es) % 16 == 0,
+              "%s: state_slot_stride %lld must be >= heads*128*128 and keep slots 16-byte "
+              "aligned",
+              who, (long long)state_slot_stride);
   kda::VerifyParams p{};
   p.q = q;
   p.k = k;
@@ -205,18 +210,19 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
   p.null_slot = null_slot;
   p.lb = lower_bound;
   return launched(
-      kda::launch_verify(p, tokens, fused, batch, reinterpret_cast<hipStream_t>(stream)), who);
+      kda::launch_verify(p, tokens, fused, bf16, batch, reinterpret_cast<hipStream_t>(stream)),
+      who);
 }
 
 int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16_t* k,
                const uint16_t* v, const uint16_t* raw_g, const uint16_t* raw_beta,
-               const float* a_log, const float* dt_bias, float lower_bound, const float* state,
-               int64_t state_slot_stride, const int32_t* state_indices, int null_slot,
-               float* corr, uint16_t* kg, int record_tokens, const int32_t* record_rows,
-               const uint16_t* gate, const float* norm_weight, float norm_eps, uint16_t* out,
-               void* stream) {
+               const float* a_log, const float* dt_bias, float lower_bound, int state_dtype,
+               const void* state, int64_t state_slot_stride, const int32_t* state_indices,
+               int null_slot, float* corr, uint16_t* kg, int record_tokens,
+               const int32_t* record_rows, const uint16_t* gate, const float* norm_weight,
+               float norm_eps, uint16_t* out, void* stream) {
   return verify_common("kda_verify", false, heads, tokens, batch, q, k, v, raw_g, raw_beta,
-                       a_log, dt_bias, lower_bound, const_cast<float*>(state),
+                       a_log, dt_bias, lower_bound, state_dtype, const_cast<void*>(state),
                        state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
                        record_rows, nullptr, gate, norm_weight, norm_eps, out, stream);
 }
@@ -224,14 +230,16 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             const uint16_t* k, const uint16_t* v, const uint16_t* raw_g,
                             const uint16_t* raw_beta, const float* a_log, const float* dt_bias,
-                            float lower_bound, float* state, int64_t state_slot_stride,
-                            const int32_t* state_indices, int null_slot, float* corr,
+                            float lower_bound, int state_dtype, void* state,
+                            int64_t state_slot_stride, const int32_t* state_indices,
+                            int null_slot, float* corr,
                             uint16_t* kg, int record_tokens, const int32_t* record_rows,
                             const int32_t* pending, const uint16_t* gate,
                             const float* norm_weight, float norm_eps, uint16_t* out,
                             void* stream) {
   return verify_common("kda_fused_replay_verify", true, heads, tokens, batch, q, k, v, raw_g,
-                       raw_beta, a_log, dt_bias, lower_bound, state, state_slot_stride,
+                       raw_beta, a_log, dt_bias, lower_bound, state_dtype, state,
+                       state_slot_stride,
                        state_indices, null_slot, corr, kg, record_tokens, record_rows, pending,
                        gate, norm_weight, norm_eps, out, stream);
 }

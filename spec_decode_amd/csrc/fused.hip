@@ -1,4 +1,4 @@
-// Fused replay+verify and the stock verify over FP32 state pages.
+// Fused replay+verify and the stock verify over FP32 or BF16 state pages.
 //
 // Method (the vLLM page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.
 // kda.fused", module docstring and KdaFused): per (request, head) item,
@@ -25,6 +25,14 @@
 //    with M = j (2T <= 16 rows of X, zero above 2T), N = v, and the 4 values of a
 //    lane as 4 consecutive K steps (key channels 16cb + 4(l/16) + i);
 // so no lane ever exchanges state values and every state byte is read once.
+//
+// BF16 pages hold the same register layout after conversion, with the key
+// channels permuted inside each group of 32: one 16-byte load brings 8 channels
+// of a row, 32j + 8(l/16) .. +7, whose first 4 serve as tile 2j and last 4 as
+// tile 2j+1. A channel permutation leaves every contraction over channels
+// unchanged, so only the LDS reads of X, kp and D_n follow it (chan0 below).
+// S_n is stored rounded to nearest even; the verify continues from the FP32
+// value, before that rounding.
 //
 // Prologue (while the page loads are in flight): threads 0..127 (channel c) do
 // the new tokens (decays, key norms, Gamma, X, the T^2 pair products reduced
@@ -118,7 +126,14 @@ __device__ __forceinline__ void pair_stage_one(const float (&kn)[T], const float
   for (int i = 0; i < PS::R; ++i) part[(i + PS::R * sel) * PS::PARTS + group] = pv[i];
 }
 
-template <int T, bool FUSED, bool GATED>
+// First key channel of lane group g (= lane / 16) in tile cb: values i = 0..3
+// of the lane are channels chan0 + i.
+template <bool SB16>
+__device__ __forceinline__ constexpr int chan0(int cb, int g) {
+  return SB16 ? 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) : 16 * cb + 4 * g;
+}
+
+template <int T, bool FUSED, bool GATED, bool SB16>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   using PI = Pairs<T>;
   const int h = blockIdx.x;
@@ -190,11 +205,17 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   uint32_t okb[MAX_T], ogb[MAX_T];
   float ou[MAX_T];
   uint32_t rbb = 0;
-  float* page = p.state + (int64_t)slot * p.slot_stride + (int64_t)h * PAGE;
+  // Page tiles: 16-byte loads, one per tile (FP32) or per pair of tiles (BF16),
+  // kept as loaded until the state pass converts them.
+  constexpr int ES = SB16 ? 2 : 4;        // bytes per state element
+  constexpr int NLD = SB16 ? 4 : 8;       // 16-byte loads per row block
+  constexpr int LDC = 16 / ES;            // channels per load
   const int lr = lane & 15;  // row within a tile
-  const int lq = lane >> 4;  // 4-channel group within a tile
-  floatx4 st[2][8];
-  const float* tile0 = page + (16 * (2 * wave) + lr) * K + 4 * lq;
+  const int lq = lane >> 4;  // channel group within a tile
+  char* const page = static_cast<char*>(p.state) +
+                     ((int64_t)slot * p.slot_stride + (int64_t)h * PAGE) * ES;
+  char* const tile0 = page + ((16 * (2 * wave) + lr) * K + LDC * lq) * ES;
+  u32x4 st[2][NLD];
   if (lower) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -207,14 +228,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-        st[r][cb] = *reinterpret_cast<const floatx4*>(tile0 + 16 * r * K + 16 * cb);
+      for (int j = 0; j < NLD; ++j)
+        st[r][j] = *reinterpret_cast<const u32x4*>(tile0 + (16 * r * K + 4 * LDC * j) * ES);
   } else {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-        st[r][cb] = *reinterpret_cast<const floatx4*>(tile0 + 16 * r * K + 16 * cb);
+      for (int j = 0; j < NLD; ++j)
+        st[r][j] = *reinterpret_cast<const u32x4*>(tile0 + (16 * r * K + 4 * LDC * j) * ES);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + t) * H * V + head_row];
@@ -338,24 +359,43 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
   }
   floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  u32x4 sn[2];  // BF16 pages: S_n of the even tile, stored with the odd one
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
-    const floatx4 xa = *reinterpret_cast<const floatx4*>(&x_s[lr][16 * cb + 4 * lq]);
+    const int c0 = chan0<SB16>(cb, lq);
+    const floatx4 xa = *reinterpret_cast<const floatx4*>(&x_s[lr][c0]);
     floatx4 dn4 = {1.f, 1.f, 1.f, 1.f};
     float ka0 = 0.f, ka1 = 0.f;
     if (replay) {
-      dn4 = *reinterpret_cast<const floatx4*>(&dn_s[16 * cb + 4 * lq]);
-      ka0 = kp_s[lq][16 * cb + lr];
-      ka1 = kp_s[4 + lq][16 * cb + lr];
+      // A operand row lr of the replay MFMA is the channel of accumulator row lr.
+      const int ca = chan0<SB16>(cb, lr >> 2) + (lr & 3);
+      dn4 = *reinterpret_cast<const floatx4*>(&dn_s[c0]);
+      ka0 = kp_s[lq][ca];
+      ka1 = kp_s[4 + lq][ca];
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      floatx4 s = st[r][cb];
+      floatx4 s;
+      if constexpr (SB16) {
+        const u32x4 w = st[r][cb >> 1];
+        const uint32_t w0 = (cb & 1) ? w[2] : w[0];
+        const uint32_t w1 = (cb & 1) ? w[3] : w[1];
+        s = floatx4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+      } else {
+        s = __builtin_bit_cast(floatx4, st[r][cb]);
+      }
       if (replay) {
         s = s * dn4;
         s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka0, ub[r][0], s, 0, 0, 0);
         if (n > 4) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka1, ub[r][1], s, 0, 0, 0);
-        *reinterpret_cast<floatx4*>(page + (16 * (2 * wave + r) + lr) * K + 16 * cb + 4 * lq) = s;
+        char* const dst = tile0 + (16 * r * K + 4 * LDC * (SB16 ? cb >> 1 : cb)) * ES;
+        if constexpr (SB16) {
+          sn[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
+          sn[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);
+          if (cb & 1) *reinterpret_cast<u32x4*>(dst) = sn[r];
+        } else {
+          *reinterpret_cast<floatx4*>(dst) = s;
+        }
       }
       acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[0], s[0], acc[r], 0, 0, 0);
       acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[1], s[1], acc[r], 0, 0, 0);
@@ -427,12 +467,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
 }
 
-template <bool FUSED, bool GATED>
+template <bool FUSED, bool GATED, bool SB16>
 static hipError_t launch_t(const VerifyParams& p, int tokens, dim3 grid, hipStream_t stream) {
   switch (tokens) {
 #define KDA_VERIFY_CASE(TT)                                                                  \
   case TT:                                                                                  \
-    hipLaunchKernelGGL((verify_kernel<TT, FUSED, GATED>), grid, dim3(256), 0, stream, p);    \
+    hipLaunchKernelGGL((verify_kernel<TT, FUSED, GATED, SB16>), grid, dim3(256), 0, stream, p);    \
     break;
     KDA_VERIFY_CASE(1)
     KDA_VERIFY_CASE(2)
@@ -449,15 +489,22 @@ static hipError_t launch_t(const VerifyParams& p, int tokens, dim3 grid, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, int batch,
+template <bool FUSED, bool GATED>
+static hipError_t launch_page(const VerifyParams& p, int tokens, bool bf16, dim3 grid,
+                              hipStream_t stream) {
+  return bf16 ? launch_t<FUSED, GATED, true>(p, tokens, grid, stream)
+              : launch_t<FUSED, GATED, false>(p, tokens, grid, stream);
+}
+
+hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, bool bf16, int batch,
                          hipStream_t stream) {
   const dim3 grid(p.heads, batch);
   const bool gated = p.gate != nullptr;
   if (fused)
-    return gated ? launch_t<true, true>(p, tokens, grid, stream)
-                 : launch_t<true, false>(p, tokens, grid, stream);
-  return gated ? launch_t<false, true>(p, tokens, grid, stream)
-               : launch_t<false, false>(p, tokens, grid, stream);
+    return gated ? launch_page<true, true>(p, tokens, bf16, grid, stream)
+                 : launch_page<true, false>(p, tokens, bf16, grid, stream);
+  return gated ? launch_page<false, true>(p, tokens, bf16, grid, stream)
+               : launch_page<false, false>(p, tokens, bf16, grid, stream);
 }
 
 }  // namespace kda

@@ -14,6 +14,7 @@ constexpr int MAX_T = 8;  // largest verify window / record capacity
 constexpr int WAVE = 64;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- conversions
 
@@ -143,8 +144,8 @@ struct VerifyParams {
   const uint16_t* rb;
   const float* a_log;
   const float* dt_bias;
-  float* state;
-  int64_t slot_stride;
+  void* state;             // pool base [slots][H][V][K], FP32 or BF16 bits
+  int64_t slot_stride;     // elements between slots
   const int32_t* slots;
   const int32_t* rows;     // NULL (verify only): row b
   const int32_t* pending;  // fused only
@@ -164,7 +165,7 @@ hipError_t launch_decay(const uint16_t* raw_g, int64_t tokens, int heads, const 
                         const float* dt_bias, float lb, float* out, hipStream_t stream);
 hipError_t launch_commit(const CommitParams& p, int window, bool bf16, bool align, int batch,
                          int layers, hipStream_t stream);
-hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, int batch,
+hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, bool bf16, int batch,
                          hipStream_t stream);
 hipError_t launch_page_rw(float* state, int64_t slot_stride, const int32_t* slots, int batch,
                           int heads, int null_slot, hipStream_t stream);

@@ -119,13 +119,14 @@ def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_lay
 def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, win,
                     rows=None, pending=None, lb=W.LOWER_BOUND, null_slot=0, label="verify",
                     stride=None, check=True, gate=None, norm_weight=None, norm_eps=1e-5):
-    """All host arrays: state float32 flat, corr float32 [rows,H,RQ,V], kg uint16
+    """All host arrays: state flat, float32 or uint16 BF16 bits (the pool's
+    type), corr float32 [rows,H,RQ,V], kg uint16
     [rows,H,RQ,2K], win a dict of uint16 arrays (q, k, v, raw_g, raw_beta).
     Returns (gpu results, oracle results) as dicts of host arrays."""
     stride = H * V * K if stride is None else stride
-    announce(f"{label}: fused={fused} H={H} B={B} T={T} RQ={RQ}")
+    announce(f"{label}: fused={fused} H={H} B={B} T={T} RQ={RQ} state={state.dtype}")
     import spec_decode_amd as kda
-    d = dict(state=dev(state), corr=dev(corr), kg=dev_bf16(kg),
+    d = dict(state=to_dev(state), corr=dev(corr), kg=dev_bf16(kg),
              out=torch.full((B * T, H * V), 0, dtype=torch.bfloat16, device=DEV))
     d["out"].view(torch.int16).fill_(0x7FFF)  # a sentinel: every element must be written
     args = dict(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]), k=dev_bf16(win["k"]),
@@ -193,7 +194,10 @@ def compare_verify(gpu, ref, orig, *, fused, H, B, T, RQ, slots, rows, pending, 
     assert_exact(f"{label} key/gate records", gpu["kg"], ref["kg"])
     assert_f32_close(f"{label} corrections (written)", gpu["corr"][cmask], ref["corr"][cmask])
     assert_exact(f"{label} corrections (untouched)", gpu["corr"][~cmask], orig["corr"][~cmask])
-    assert_f32_close(f"{label} state (replayed)", gpu["state"][smask], ref["state"][smask])
+    if orig["state"].dtype == np.uint16:  # a BF16 pool
+        assert_bf16_close(f"{label} state (replayed)", gpu["state"][smask], ref["state"][smask])
+    else:
+        assert_f32_close(f"{label} state (replayed)", gpu["state"][smask], ref["state"][smask])
     assert_exact(f"{label} state (untouched)", gpu["state"][~smask], orig["state"][~smask])
 
 

@@ -49,45 +49,51 @@ def _err(lib):
     return lib.kda_last_error().decode()
 
 
-def test_rejects_bad_arguments_without_launch(lib):
+def _verify_args(tokens, *, state=None, dtype=0, stride=4 * 128 * 128, rq=8, rows=None,
+                 pending=None, gate=None, norm_weight=None, fused=False):
+    """kda_verify / kda_fused_replay_verify arguments in declaration order."""
     P = ctypes.c_void_p
     fake = P(0x1000)  # never dereferenced: validation fails first
+    args = [ctypes.c_int(4), ctypes.c_int(tokens), ctypes.c_int(2)] + [fake] * 7 + [
+        ctypes.c_float(-5.0), ctypes.c_int(dtype), fake if state is None else P(state),
+        ctypes.c_int64(stride), fake, ctypes.c_int(0), fake, fake, ctypes.c_int(rq), P(rows)]
+    if fused:
+        args.append(P(pending))
+    return args + [P(gate), P(norm_weight), ctypes.c_float(1e-5), fake, P(None)]
+
+
+def test_rejects_bad_arguments_without_launch(lib):
     lib.kda_verify.restype = ctypes.c_int
-    args = [ctypes.c_int(4), ctypes.c_int(9), ctypes.c_int(2)] + [fake] * 7 + [
-        ctypes.c_float(-5.0), fake, ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
-        fake, fake, ctypes.c_int(8), P(None), P(None), P(None), ctypes.c_float(1e-5), fake,
-        P(None)]
-    assert lib.kda_verify(*args) == 1
+    lib.kda_fused_replay_verify.restype = ctypes.c_int
+    assert lib.kda_verify(*_verify_args(9)) == 1
     assert "tokens must be in 1..8" in _err(lib)
 
-    lib.kda_fused_replay_verify.restype = ctypes.c_int
-    args = [ctypes.c_int(4), ctypes.c_int(4), ctypes.c_int(2)] + [fake] * 7 + [
-        ctypes.c_float(-5.0), fake, ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
-        fake, fake, ctypes.c_int(4), P(None), P(None), P(None), P(None), ctypes.c_float(1e-5),
-        fake, P(None)]
-    assert lib.kda_fused_replay_verify(*args) == 1
+    assert lib.kda_fused_replay_verify(*_verify_args(4, rq=4, fused=True)) == 1
     assert "record_rows and pending are required" in _err(lib)
 
     # gate without norm_weight
-    args2 = list(args)
-    args2[18], args2[19], args2[20], args2[21] = fake, fake, fake, P(None)
-    assert lib.kda_fused_replay_verify(*args2) == 1
+    assert lib.kda_fused_replay_verify(*_verify_args(4, rq=4, rows=0x1000, pending=0x1000,
+                                                     gate=0x1000, fused=True)) == 1
     assert "gate and norm_weight" in _err(lib)
 
     # record_tokens below tokens
-    args[17] = ctypes.c_int(3)
-    assert lib.kda_fused_replay_verify(*args) == 1
+    assert lib.kda_fused_replay_verify(*_verify_args(4, rq=3, fused=True)) == 1
     assert "record_tokens" in _err(lib)
 
     # a misaligned state base
-    args = [ctypes.c_int(4), ctypes.c_int(4), ctypes.c_int(2)] + [fake] * 7 + [
-        ctypes.c_float(-5.0), P(0x1004), ctypes.c_int64(4 * 128 * 128), fake, ctypes.c_int(0),
-        fake, fake, ctypes.c_int(4), fake, fake, P(None), P(None), ctypes.c_float(1e-5), fake,
-        P(None)]
-    assert lib.kda_fused_replay_verify(*args) == 1
+    assert lib.kda_fused_replay_verify(*_verify_args(4, rq=4, rows=0x1000, pending=0x1000,
+                                                     state=0x1004, fused=True)) == 1
     assert "16-byte aligned" in _err(lib)
 
+    # an unknown state type; a BF16 slot stride that breaks 16-byte alignment
+    assert lib.kda_verify(*_verify_args(4, dtype=2)) == 1
+    assert "state_dtype" in _err(lib)
+    assert lib.kda_verify(*_verify_args(4, dtype=1, stride=4 * 128 * 128 + 4)) == 1
+    assert "state_slot_stride" in _err(lib)
+
     # a non-finite lower bound
+    P = ctypes.c_void_p
+    fake = P(0x1000)
     lib.kda_decay.restype = ctypes.c_int
     assert lib.kda_decay(fake, ctypes.c_int64(3), ctypes.c_int(2), fake, fake,
                          ctypes.c_float(float("nan")), fake, P(None)) == 1

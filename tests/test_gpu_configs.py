@@ -108,11 +108,14 @@ def test_config1_commit_bf16():
 
 # ---------------------------------------------------------------- config 2
 
-def test_config2_fused_full():
+@pytest.mark.parametrize("bf16", [False, True])
+def test_config2_fused_full(bf16):
+    """The fused workload at full size against the full oracle; bf16 runs it
+    on the same pool rounded to a BF16 pool."""
     w = W.config2()
     H, B, T, RQ = w.heads, w.batch, w.tokens, w.record_tokens
     a = w.arrays
-    state = a["state"].numpy().copy()
+    state = W.bits(a["state"].to(torch.bfloat16)) if bf16 else a["state"].numpy().copy()
     slots, rows = a["state_indices"].numpy(), a["record_rows"].numpy()
     corr, kg = a["corr"].numpy().copy(), W.bits(a["kg"])
     announce("config2: oracle verify of the prior window (records)")
@@ -122,7 +125,7 @@ def test_config2_fused_full():
     run_verify_case(fused=True, H=H, B=B, T=T, RQ=RQ, state=state, slots=slots, corr=corr,
                     kg=kg, a_log=a["a_log"][0].numpy(), dt_bias=a["dt_bias"][0].numpy(),
                     win=window_np(w.windows["new"]), rows=rows, pending=pending,
-                    lb=w.lower_bound, label="config2 fused")
+                    lb=w.lower_bound, label=f"config2 fused bf16={bf16}")
 
 
 def test_config2_fused_full_gated_output():

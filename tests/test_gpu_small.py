@@ -161,34 +161,39 @@ def test_commit_more_layers_than_one_launch():
 
 # ---------------------------------------------------------------- verify / fused
 
-def _vf_case(seed, H, B, T, RQ, S, null_rows=(), norec_rows=()):
+def _vf_case(seed, H, B, T, RQ, S, null_rows=(), norec_rows=(), bf16=False):
+    """A small verify/fused case; bf16 gives the pool as BF16 bits (the FP32
+    draw rounded to nearest even)."""
     c = W.small_fused_case(seed, H, B, T, RQ, S, null_rows=null_rows, no_record_rows=norec_rows)
-    return dict(state=c["state"].numpy().copy(), slots=c["state_indices"].numpy().copy(),
+    state = W.bits(c["state"].to(torch.bfloat16)) if bf16 else c["state"].numpy().copy()
+    return dict(state=state, slots=c["state_indices"].numpy().copy(),
                 rows=c["record_rows"].numpy().copy(), corr=c["corr"].numpy().copy(),
                 kg=W.bits(c["kg"]), a_log=c["a_log"][0].numpy(), dt_bias=c["dt_bias"][0].numpy(),
                 win=window_np(c["window"]))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_verify_windows(T):
+def test_verify_windows(T, bf16):
     H, B = 3, 5
     for RQ in sorted({T, 8}):
-        c = _vf_case(200 + T, H, B, T, RQ, 9, null_rows=(1,), norec_rows=(3,))
+        c = _vf_case(200 + T, H, B, T, RQ, 9, null_rows=(1,), norec_rows=(3,), bf16=bf16)
         run_verify_case(fused=False, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
                         corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
                         win=c["win"], rows=c["rows"], label=f"verify T={T} RQ={RQ}")
     # record_rows = NULL: request b writes row b
-    c = _vf_case(300 + T, H, B, T, T, 9)
+    c = _vf_case(300 + T, H, B, T, T, 9, bf16=bf16)
     run_verify_case(fused=False, H=H, B=B, T=T, RQ=T, state=c["state"], slots=c["slots"],
                     corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
                     win=c["win"], rows=None, label=f"verify T={T} rows=NULL")
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_fused_windows(T):
+def test_fused_windows(T, bf16):
     H, B = 3, 6
     for RQ in sorted({T, 8}):
-        c = _vf_case(400 + T, H, B, T, RQ, 10, null_rows=(1,), norec_rows=(3,))
+        c = _vf_case(400 + T, H, B, T, RQ, 10, null_rows=(1,), norec_rows=(3,), bf16=bf16)
         rng = np.random.default_rng(T * 10 + RQ)
         pending = rng.integers(0, RQ + 1, B).astype(np.int32)
         rows = c["rows"]
@@ -202,10 +207,11 @@ def test_fused_windows(T):
                         win=c["win"], rows=rows, pending=pending, label=f"fused T={T} RQ={RQ}")
 
 
-def test_fused_every_pending_count():
+@pytest.mark.parametrize("bf16", [False, True])
+def test_fused_every_pending_count(bf16):
     """One request per n = 0..8 (the replay's one- and two-MFMA paths)."""
     H, B, T, RQ = 2, 9, 4, 8
-    c = _vf_case(77, H, B, T, RQ, 12)
+    c = _vf_case(77, H, B, T, RQ, 12, bf16=bf16)
     pending = np.zeros(B, np.int32)
     for b in range(B):
         pending[c["rows"][b]] = b
@@ -214,11 +220,13 @@ def test_fused_every_pending_count():
                     win=c["win"], rows=c["rows"], pending=pending, label="fused n=0..8")
 
 
-def test_fused_padded_slot_stride():
+@pytest.mark.parametrize("bf16", [False, True])
+def test_fused_padded_slot_stride(bf16):
     H, B, T, RQ, S = 2, 4, 3, 4, 6
-    stride = H * V * K + 256
+    stride = H * V * K + 264 if bf16 else H * V * K + 260  # 16-byte slots, not 256-byte
     g = W._gen(55)
-    state = W.draw_state(56, S * stride, torch.float32).numpy().copy()
+    state = W.draw_state(56, S * stride, torch.float32)
+    state = W.bits(state.to(torch.bfloat16)) if bf16 else state.numpy().copy()
     a_log, dtb = W.draw_gate_params(g, 1, H)
     corr, kg = W.draw_records(g, B, H, RQ)
     win = window_np(W.draw_window(g, B, T, H))
@@ -246,11 +254,12 @@ def test_page_rw_probe_leaves_pool_unchanged():
     assert torch.equal(state.view(torch.int32), before.view(torch.int32))
 
 
-@pytest.mark.parametrize("T", [1, 3, 4, 8])
+@pytest.mark.parametrize("T,bf16", [(1, False), (3, False), (4, False), (8, False), (3, True),
+                                    (8, True)])
 @pytest.mark.parametrize("fused", [False, True])
-def test_gated_output_stage(T, fused):
+def test_gated_output_stage(T, fused, bf16):
     H, B, RQ = 3, 5, 8
-    c = _vf_case(500 + T, H, B, T, RQ, 9, null_rows=(1,), norec_rows=(3,))
+    c = _vf_case(500 + T, H, B, T, RQ, 9, null_rows=(1,), norec_rows=(3,), bf16=bf16)
     gate, weight, eps = W.draw_output_stage(W._gen(600 + T), B, T, H)
     rng = np.random.default_rng(T)
     pending = rng.integers(0, RQ + 1, B).astype(np.int32)

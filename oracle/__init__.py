@@ -61,7 +61,13 @@ def _load():
                              d, i, _i64p, l, i]),
         "kda_o_verify": (i, [i, i, i, i, i, _u16p, _u16p, _u16p, _u16p, _u16p, _fp, _fp,
                              d, _vp, ctypes.c_int64, _i32p, i, _fp, _u16p, i, _i32p,
-                             _i32p, i, _u16p, _i64p, l, i, _u16p, _fp, d, i]),
+                             _i32p, i, _u16p, _i64p, l, i, _u16p, _fp, d, i, _u16p,
+                             ctypes.c_int64, _u16p, _u16p, _u16p, ctypes.c_int64,
+                             ctypes.c_int64, ctypes.c_int64, d]),
+        "kda_o_exp_f32": (ctypes.c_float, [ctypes.c_float]),
+        "kda_o_silu_bf16": (ctypes.c_uint16, [ctypes.c_float]),
+        "kda_o_conv_silu": (None, [i, _fp, _fp, ctypes.c_float, _u16p]),
+        "kda_o_conv_offset": (i, [i]),
         "kda_o_decay_buf": (None, [l, i, i, _u16p, _fp, _fp, d, _fp]),
         "kda_o_defer": (None, [i, _i32p, _i32p, _i32p, _i32p, _i32p, i]),
         "kda_o_flush_plan": (None, [i, i, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
@@ -251,13 +257,27 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
                 dt_bias, lower_bound, state, state_slot_stride, state_indices,
                 corr, kg, record_tokens, record_rows, pending, out, null_slot,
                 key_dim, value_dim, items, threads, gate=None, norm_weight=None,
-                norm_eps=1e-5):
+                norm_eps=1e-5, conv=None):
     state_bf16 = isinstance(state, np.ndarray) and state.dtype == np.uint16
     _check_inplace(state, np.uint16 if state_bf16 else np.float32, "state")
     _check_inplace(corr, np.float32, "corr")
     _check_inplace(kg, np.uint16, "kg")
     _check_inplace(out, np.uint16, "out")
-    q, k, v, g = (_c(x, np.uint16) for x in (q, k, v, raw_g))
+    q, k, v, g = (None if x is None else _c(x, np.uint16) for x in (q, k, v, raw_g))
+    if conv is None:
+        cx = cw = cb = cs = None
+        cxs = css = ccs = cts = 0
+        qsc = 0.0
+    else:
+        cx = _c(conv["x"], np.uint16)
+        cxs = int(conv["x_row_stride"])
+        cw = _c(conv["weight"], np.uint16)
+        cb = None if conv.get("bias") is None else _c(conv["bias"], np.uint16)
+        cs = conv["state"]
+        _check_inplace(cs, np.uint16, "conv state")
+        css, ccs, cts = (int(conv[n]) for n in ("slot_stride", "channel_stride",
+                                                "tap_stride"))
+        qsc = float(conv["q_scale"])
     rb = _c(raw_beta, np.uint16)
     a_log = _c(a_log, np.float32)
     dt_bias = _c(dt_bias, np.float32)
@@ -275,7 +295,9 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
         _ptr(slots, _i32p), int(null_slot), _ptr(corr, _fp), _ptr(kg, _u16p),
         int(record_tokens), _ptr(rows, _i32p), _ptr(pend, _i32p), int(fused),
         _ptr(out, _u16p), ip, ni, default_threads() if threads is None else int(threads),
-        _ptr(gt, _u16p), _ptr(nw, _fp), float(norm_eps), int(state_bf16))
+        _ptr(gt, _u16p), _ptr(nw, _fp), float(norm_eps), int(state_bf16),
+        _ptr(cx, _u16p), cxs, _ptr(cw, _u16p), _ptr(cb, _u16p), _ptr(cs, _u16p), css, ccs,
+        cts, qsc)
 
 
 def verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log, dt_bias,
@@ -311,6 +333,61 @@ def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log
                 record_rows=record_rows, pending=pending, out=out, null_slot=null_slot,
                 key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
                 gate=gate, norm_weight=norm_weight, norm_eps=norm_eps)
+
+
+def fused_conv_replay_verify(*, heads, tokens, batch, x, x_row_stride, conv_weight,
+                             conv_state, conv_slot_stride, conv_channel_stride,
+                             conv_tap_stride, q_scale, raw_g, raw_beta, a_log, dt_bias,
+                             lower_bound, state, state_slot_stride, state_indices, corr, kg,
+                             record_tokens, record_rows, pending, out, conv_bias=None,
+                             null_slot=0, key_dim=128, value_dim=128, items=None,
+                             threads=None, gate=None, norm_weight=None, norm_eps=1e-5):
+    """The fused step with the convolution prologue: q, k, v are the SiLU of a
+    4-tap causal convolution of x (rows of ``x_row_stride``: q | k | v parts of
+    H*K channels each) over each channel's window in ``conv_state`` (uint16 BF16,
+    element [slot*slot_stride + channel*channel_stride + i*tap_stride], i < RQ+2)
+    read at offset max(n - 1, 0); q is then L2-normalised and scaled by
+    ``q_scale``; the window is rewritten in place. ``conv_weight`` is [3, 4, H*K]
+    BF16 bits, ``conv_bias`` [3*H*K] or None."""
+    if record_rows is None or pending is None:
+        raise ValueError("fused replay+verify needs record_rows and pending")
+    conv = dict(x=x, x_row_stride=x_row_stride, weight=conv_weight, bias=conv_bias,
+                state=conv_state, slot_stride=conv_slot_stride,
+                channel_stride=conv_channel_stride, tap_stride=conv_tap_stride,
+                q_scale=q_scale)
+    _verify_buf(True, heads=heads, tokens=tokens, batch=batch, q=None, k=None, v=None,
+                raw_g=raw_g, raw_beta=raw_beta, a_log=a_log, dt_bias=dt_bias,
+                lower_bound=lower_bound, state=state, state_slot_stride=state_slot_stride,
+                state_indices=state_indices, corr=corr, kg=kg, record_tokens=record_tokens,
+                record_rows=record_rows, pending=pending, out=out, null_slot=null_slot,
+                key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
+                gate=gate, norm_weight=norm_weight, norm_eps=norm_eps, conv=conv)
+
+
+def exp_f32(x):
+    """The prologue's FP32 exp (Cody-Waite reduction, degree-7 Taylor)."""
+    return float(_load().kda_o_exp_f32(ctypes.c_float(x)))
+
+
+def silu_bf16(acc):
+    """BF16 bits of SiLU of an FP32 pre-activation, by the prologue's fixed steps."""
+    return int(_load().kda_o_silu_bf16(ctypes.c_float(acc)))
+
+
+def conv_silu(seq, w, bias=0.0):
+    """One channel's causal convolution + SiLU: seq = 3 taps then T inputs (BF16
+    values as float32), w the 4 weights; returns T BF16 bit patterns."""
+    seq = _c(seq, np.float32)
+    w = _c(w, np.float32)
+    T = seq.size - 3
+    y = np.zeros(T, np.uint16)
+    _load().kda_o_conv_silu(T, _ptr(seq, _fp), _ptr(w, _fp), ctypes.c_float(bias),
+                            _ptr(y, _u16p))
+    return y
+
+
+def conv_offset(n):
+    return int(_load().kda_o_conv_offset(int(n)))
 
 
 def decay_buf(raw_g, a_log, dt_bias, lower_bound):

@@ -13,7 +13,9 @@
  *
  * Precision: every input is converted exactly to double (BF16 and FP32 are
  * subsets of FP64); all arithmetic is FP64 in the order the definitions give;
- * each stored output is rounded once, round-to-nearest-even, to its dtype.
+ * each stored output is rounded once, round-to-nearest-even, to its dtype. The
+ * one exception is the convolution prologue's SiLU, whose BF16 rounding is a
+ * decision taken in FP32 by fixed steps (see "Convolution prologue").
  *
  * Shapes are runtime parameters (K key channels, V value channels) so that the
  * same code runs at K = V = 128 and on tiny brute-force cases.
@@ -88,6 +90,74 @@ void kda_o_knorm(int K, const double* k, double* out) {
   double inv = 1.0 / sqrt(s + 1e-6);
   for (int c = 0; c < K; ++c) out[c] = k[c] * inv;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Convolution prologue ([fused page] KdaFused.kernel: the convolution, its    */
+/* SiLU, and the q/k normalisation)                                           */
+/* ------------------------------------------------------------------------- */
+/*
+ * The SiLU output is stored in BF16 and is then used everywhere (the recorded
+ * key is its bit pattern). Its BF16 rounding is therefore a decision that both
+ * sides must take identically, and it is taken in FP32, the page's precision,
+ * by these fixed steps (the GPU kernel implements the same steps on its own):
+ *   acc = bias; acc = fma(seq_{t+i}, w_i, acc) for i = 0, 1, 2, 3;
+ *   e   = exp_f32(-acc)   (below);
+ *   y   = BF16_rne(acc / (1 + e))   (IEEE FP32 add and divide).
+ * Everything after the rounding is FP64 again.
+ */
+
+/* exp in FP32 by Cody and Waite's two-constant argument reduction and a
+ * degree-7 Taylor polynomial (Horner form, each step one fused multiply-add):
+ *   x is clamped to [-80, 80];  k = rint(x * log2(e));
+ *   r = fma(-k, LN2_HI, x);  r = fma(-k, LN2_LO, r);
+ *   p = 1 + r + r^2/2! + ... + r^7/7!;  exp(x) = p * 2^k.
+ * LN2_HI is ln 2 rounded to 16 fraction bits (so k * LN2_HI is exact for
+ * |k| < 256), LN2_LO the FP32 value of ln 2 - LN2_HI; the Taylor coefficients
+ * are the FP32 quotients 1/j!. Error: |r| <= ln2/2, so the truncation is below
+ * 2e-9 relative, and the result is within a few FP32 ulps of exp(x). */
+static const float kda_o_ln2_hi = 45426.0f / 65536.0f;
+
+float kda_o_exp_f32(float x) {
+  const float ln2_lo = (float)(0.69314718055994530942 - (double)kda_o_ln2_hi);
+  const float log2e = 1.44269504088896340736f;
+  float c[8];
+  float f = 1.0f;
+  for (int j = 0; j < 8; ++j) {
+    if (j > 1) f *= (float)j; /* j! is exact in FP32 for j <= 7 */
+    c[j] = 1.0f / f;
+  }
+  if (x > 80.0f) x = 80.0f;
+  if (x < -80.0f) x = -80.0f;
+  float k = rintf(x * log2e);
+  float r = fmaf(-k, kda_o_ln2_hi, x);
+  r = fmaf(-k, ln2_lo, r);
+  float p = c[7];
+  for (int j = 6; j >= 0; --j) p = fmaf(p, r, c[j]);
+  return ldexpf(p, (int)k);
+}
+
+/* SiLU of an FP32 pre-activation, rounded to BF16 (the steps above). */
+uint16_t kda_o_silu_bf16(float acc) {
+  float e = kda_o_exp_f32(-acc);
+  float y = acc / (1.0f + e);
+  return kda_o_double_to_bf16((double)y);
+}
+
+/* One channel's causal convolution over a window of T tokens: seq holds the 3
+ * history taps then the T inputs (BF16 values), w the 4 weights (w[0] meets the
+ * oldest tap, w[3] the current input), bias 0 when there is none. Writes the
+ * BF16 bits of SiLU(bias + sum_i w_i seq_{t+i}) for t < T. */
+void kda_o_conv_silu(int T, const float* seq, const float* w, float bias, uint16_t* y) {
+  for (int t = 0; t < T; ++t) {
+    float acc = bias;
+    for (int i = 0; i < 4; ++i) acc = fmaf(seq[t + i], w[i], acc);
+    y[t] = kda_o_silu_bf16(acc);
+  }
+}
+
+/* The window offset of a fused step: the history after n accepted tokens of the
+ * previous window starts at n - 1 (at 0 when nothing is pending). */
+int kda_o_conv_offset(int n) { return n > 0 ? n - 1 : 0; }
 
 /* ------------------------------------------------------------------------- */
 /* Item-level cores (double in, double out). Layouts: S is [V][K] row-major   */
@@ -439,7 +509,51 @@ struct verify_ctx {
   const uint16_t* gate;  /* optional gated RMSNorm epilogue */
   const float* norm_w;
   double norm_eps;
+  /* optional convolution prologue (x != NULL): q, k, v are its outputs */
+  const uint16_t* x;      /* [B*T] rows of x_stride: q | k | v pre-activations */
+  int64_t x_stride;
+  const uint16_t* conv_w; /* BF16 [3][4][H*K] */
+  const uint16_t* conv_b; /* BF16 [3*H*K] or NULL */
+  uint16_t* conv;         /* BF16 window pool */
+  int64_t conv_ss, conv_cs, conv_ts; /* slot, channel, tap strides (elements) */
+  double q_scale;
 };
+
+/* The prologue of one item: per part p (0 q, 1 k, 2 v) and channel, the window
+ * taps at the replay-aware offset, the convolution and SiLU of the T inputs, and
+ * the window write-back [tap 1, tap 2, x_0 .. x_{T-1}] (entries past T + 1 keep
+ * their values). y is [3][T][K] BF16 bits. */
+static void conv_prologue(const struct verify_ctx* c, int b, int h, int slot, int n,
+                          uint16_t* y) {
+  const int K = c->K, T = c->T, d = c->H * c->K;
+  const int off = kda_o_conv_offset(n);
+  float seq[3 + 8];
+  float w[4];
+  uint16_t yt[8];
+  for (int p = 0; p < 3; ++p) {
+    for (int ch = 0; ch < K; ++ch) {
+      const int64_t col = (int64_t)p * d + (int64_t)h * K + ch;
+      uint16_t* win = c->conv + (int64_t)slot * c->conv_ss + col * c->conv_cs;
+      uint16_t taps[3];
+      for (int i = 0; i < 3; ++i) taps[i] = win[(int64_t)(off + i) * c->conv_ts];
+      for (int i = 0; i < 3; ++i) seq[i] = (float)kda_o_bf16_to_double(taps[i]);
+      uint16_t xin[8];
+      for (int t = 0; t < T; ++t) {
+        xin[t] = c->x[((int64_t)b * T + t) * c->x_stride + col];
+        seq[3 + t] = (float)kda_o_bf16_to_double(xin[t]);
+      }
+      for (int i = 0; i < 4; ++i)
+        w[i] = (float)kda_o_bf16_to_double(c->conv_w[((int64_t)p * 4 + i) * d + (int64_t)h * K + ch]);
+      float bias = c->conv_b ? (float)kda_o_bf16_to_double(c->conv_b[col]) : 0.0f;
+      kda_o_conv_silu(T, seq, w, bias, yt);
+      for (int t = 0; t < T; ++t) y[((int64_t)p * T + t) * K + ch] = yt[t];
+      /* write-back, after this channel's window was read */
+      win[0] = taps[1];
+      win[c->conv_ts] = taps[2];
+      for (int t = 0; t < T; ++t) win[(int64_t)(2 + t) * c->conv_ts] = xin[t];
+    }
+  }
+}
 
 /* Gated RMSNorm of one token's outputs ([fused page] KdaFused.kernel, the
  * output stage): o is first rounded to BF16 (a stock rounding point); then
@@ -517,17 +631,29 @@ static void verify_item(void* p, long it) {
     memcpy(S, S0, sizeof(double) * VK);
   }
 
-  /* The new window. */
+  /* The new window: q, k, v given, or the convolution prologue's outputs (then
+   * q is L2-normalised with 1e-6 inside the root and scaled by q_scale). */
+  uint16_t* ycv = NULL;
+  if (c->x) {
+    ycv = (uint16_t*)malloc(sizeof(uint16_t) * 3 * (size_t)T * (size_t)K);
+    conv_prologue(c, b, h, slot, n, ycv);
+  }
   for (int t = 0; t < T; ++t) {
     int64_t tok = (int64_t)b * T + t;
-    const uint16_t* qt = c->q + (tok * H + h) * K;
-    const uint16_t* kt = c->k + (tok * H + h) * K;
+    const uint16_t* qt = ycv ? ycv + (0 * T + t) * K : c->q + (tok * H + h) * K;
+    const uint16_t* kt = ycv ? ycv + (1 * T + t) * K : c->k + (tok * H + h) * K;
+    const uint16_t* vt = ycv ? ycv + (2 * T + t) * K : c->v + (tok * H + h) * V;
     const uint16_t* gt = c->g + (tok * H + h) * K;
-    const uint16_t* vt = c->v + (tok * H + h) * V;
     for (int ch = 0; ch < K; ++ch) {
       qq[t * K + ch] = kda_o_bf16_to_double(qt[ch]);
       kr[ch] = kda_o_bf16_to_double(kt[ch]);
       d[t * K + ch] = kda_o_decay(kda_o_bf16_to_double(gt[ch]), a, (double)dtb[ch], c->lb);
+    }
+    if (ycv) {
+      double sq = 0.0;
+      for (int ch = 0; ch < K; ++ch) sq += qq[t * K + ch] * qq[t * K + ch];
+      double f = c->q_scale / sqrt(sq + 1e-6);
+      for (int ch = 0; ch < K; ++ch) qq[t * K + ch] *= f;
     }
     kda_o_knorm(K, kr, kn + t * K);
     for (int v = 0; v < V; ++v) vv[t * V + v] = kda_o_bf16_to_double(vt[v]);
@@ -551,11 +677,12 @@ static void verify_item(void* p, long it) {
       int64_t tok = (int64_t)b * T + t;
       for (int v = 0; v < V; ++v) corr[t * V + v] = to_f32(u[t * V + v]);
       for (int ch = 0; ch < K; ++ch) {
-        kg[t * 2 * K + ch] = c->k[(tok * H + h) * K + ch];
+        kg[t * 2 * K + ch] = ycv ? ycv[(1 * T + t) * K + ch] : c->k[(tok * H + h) * K + ch];
         kg[t * 2 * K + K + ch] = c->g[(tok * H + h) * K + ch];
       }
     }
   }
+  free(ycv);
   free(S0);
   free(S);
   free(u);
@@ -575,13 +702,17 @@ int kda_o_verify(int H, int T, int B, int K, int V, const uint16_t* q, const uin
                  float* corr, uint16_t* kg, int RQ, const int32_t* record_rows,
                  const int32_t* pending, int fused, uint16_t* out, const int64_t* items,
                  long n_items, int threads, const uint16_t* gate, const float* norm_w,
-                 double norm_eps, int state_bf16) {
+                 double norm_eps, int state_bf16, const uint16_t* x, int64_t x_stride,
+                 const uint16_t* conv_w, const uint16_t* conv_b, uint16_t* conv,
+                 int64_t conv_ss, int64_t conv_cs, int64_t conv_ts, double q_scale) {
   struct verify_ctx c = {H,          T,          B,       K,          V,
                          RQ,         fused,      state_bf16, q,       k,          v,
                          raw_g,      raw_beta,   a_log,   dt_bias,    lower_bound,
                          state,      state_slot_stride, state_indices, null_slot, corr,
                          kg,         record_rows, pending, out,       items,
-                         gate,       norm_w,     norm_eps};
+                         gate,       norm_w,     norm_eps, x,         x_stride,
+                         conv_w,     conv_b,     conv,    conv_ss,    conv_cs,
+                         conv_ts,    q_scale};
   long count = items ? n_items : (long)B * H;
   parallel_for(count, threads, verify_item, &c);
   return 0;

@@ -82,6 +82,40 @@ def draw_window(gen, B: int, T: int, H: int) -> Window:
     return Window(q, k, v, raw_g, raw_beta)
 
 
+@dataclass
+class ConvInputs:
+    """Inputs of the convolution prologue for B requests of T tokens and H heads:
+
+    * x [B*T, pitch] BF16: a packed projection row per token whose columns
+      [0, 3HK) are the q | k | v pre-activations (HK = H*128 channels each); the
+      rest of the row holds the projection's other outputs and is drawn too;
+    * weight [3, 4, HK] BF16 (part, tap, channel), tap 3 meeting the current
+      token; bias [3*HK] BF16;
+    * window pool [slots, 3*HK, W] BF16, W = RQ + 2 values per channel.
+    """
+    x: torch.Tensor
+    weight: torch.Tensor
+    bias: torch.Tensor
+    window: torch.Tensor
+
+    @property
+    def pitch(self) -> int:
+        return self.x.shape[1]
+
+
+def draw_conv_inputs(gen, B: int, T: int, H: int, RQ: int, slots: int) -> ConvInputs:
+    """x = BF16(N(0, 1)); weight = BF16(N(0, 0.5)); bias = BF16(N(0, 0.1));
+    every window value = BF16(N(0, 1)). pitch = 4HK + 128 + H rounded up to a
+    multiple of 8 (16-byte rows)."""
+    hk = H * K
+    pitch = (4 * hk + 128 + H + 7) // 8 * 8
+    x = bf16(normal(gen, (B * T, pitch)))
+    weight = bf16(normal(gen, (3, 4, hk), 0.5))
+    bias = bf16(normal(gen, (3 * hk,), 0.1))
+    window = bf16(normal(gen, (slots, 3 * hk, RQ + 2)))
+    return ConvInputs(x, weight, bias, window)
+
+
 def draw_gate_params(gen, L: int, H: int):
     a_log = normal(gen, (L, H), 0.5)
     dt_bias = normal(gen, (L, H, K), 0.1)

@@ -51,6 +51,9 @@ def parse_args():
     ap.add_argument("--state-dtype", choices=("f32", "bf16"), default="f32",
                     help="element type of the state pool (the workload's is f32; bf16 "
                          "rounds the same pool to BF16 and commits in BF16)")
+    ap.add_argument("--conv", action="store_true",
+                    help="run the fused step with its convolution prologue (q, k, v from "
+                         "packed pre-activations and a window pool)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 2 GiB device copy (streaming ceiling)")
     return ap.parse_args()
@@ -64,7 +67,8 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-FUSED_SOURCES = ["spec_decode_amd/csrc/fused.hip", "spec_decode_amd/csrc/kda_device.h"]
+FUSED_SOURCES = ["spec_decode_amd/csrc/fused.hip", "spec_decode_amd/csrc/verify_kernel.h",
+                 "spec_decode_amd/csrc/kda_device.h"]
 COMMIT_SOURCES = ["spec_decode_amd/csrc/commit.hip", "spec_decode_amd/csrc/kda_device.h"]
 
 
@@ -84,10 +88,12 @@ def measured_traffic(name, digest):
 
 # ----------------------------------------------------------------- accounting
 
-def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False, es=4):
+def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False, es=4, conv=False):
     """Algorithmic bytes of one fused launch: (state bytes, total bytes). The
     gated output stage reads q*256 B of gates per live item; es is the state
-    element size."""
+    element size. With the convolution prologue, q, k, v are read as the same
+    bytes of pre-activations, plus each live item's windows (3*128 channels,
+    RQ + 2 values read, q + 2 written, BF16) and the weights once."""
     page = V * K * es
     state = total = 0
     for b in range(len(slots)):
@@ -102,8 +108,11 @@ def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False, es=4):
         t += T * (3 * K * 2 + V * 2) + T * 2        # q, k, raw_g, v, raw_beta
         t += T * V * 2                              # o
         t += T * V * 2 if gated else 0              # gate
+        t += (3 * K * (RQ + 2) * 2 + 3 * K * (T + 2) * 2) if conv else 0  # windows
         state += H * s
         total += H * t
+    if conv:
+        total += 3 * 4 * H * K * 2 + 3 * H * K * 2  # convolution weights and bias
     return state, total
 
 
@@ -250,6 +259,13 @@ def main():
     if args.gated_output:
         gate, norm_w, norm_eps = W.draw_output_stage(W._gen(4 + 200), B, T, H)
         gate, norm_w = gate.to(dev), norm_w.to(dev)
+    conv = None
+    if args.conv:
+        cv = W.draw_conv_inputs(W._gen(4 + 300), B, T, H, RQ, w.slots)
+        conv = dict(x=cv.x.to(dev), pitch=cv.pitch, weight=cv.weight.to(dev),
+                    bias=cv.bias.to(dev), pool=cv.window.to(dev).reshape(-1))
+        hk3 = 3 * H * K
+        conv["strides"] = (hk3 * (RQ + 2), RQ + 2, 1)
     commit_lens = torch.empty(B, dtype=torch.int32, device=dev)
     flush = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
 
@@ -292,13 +308,24 @@ def main():
         e = ev[i]
         commit_lens.copy_(accepted)
         e[0].record()
-        kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v,
-                                    raw_g=new.raw_g, raw_beta=new.raw_beta, a_log=a_log,
-                                    dt_bias=dt_bias, lower_bound=lb, state=state,
-                                    state_slot_stride=state_stride, state_indices=slots,
-                                    corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
-                                    pending=pending, out=out, gate=gate, norm_weight=norm_w,
-                                    norm_eps=norm_eps)
+        if conv is None:
+            kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v,
+                                        raw_g=new.raw_g, raw_beta=new.raw_beta, a_log=a_log,
+                                        dt_bias=dt_bias, lower_bound=lb, state=state,
+                                        state_slot_stride=state_stride, state_indices=slots,
+                                        corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
+                                        pending=pending, out=out, gate=gate,
+                                        norm_weight=norm_w, norm_eps=norm_eps)
+        else:
+            cs = conv["strides"]
+            kda.kda_fused_conv_replay_verify(
+                heads=H, tokens=T, batch=B, x=conv["x"], x_row_stride=conv["pitch"],
+                conv_weight=conv["weight"], conv_bias=conv["bias"], conv_state=conv["pool"],
+                conv_slot_stride=cs[0], conv_channel_stride=cs[1], conv_tap_stride=cs[2],
+                q_scale=K ** -0.5, raw_g=new.raw_g, raw_beta=new.raw_beta, a_log=a_log,
+                dt_bias=dt_bias, lower_bound=lb, state=state, state_slot_stride=state_stride,
+                state_indices=slots, corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
+                pending=pending, out=out, gate=gate, norm_weight=norm_w, norm_eps=norm_eps)
         e[1].record()
         kda.kda_defer_commit(batch=B, state_indices=slots, commit_lens=commit_lens,
                              record_rows=rows, pending=pending)
@@ -328,7 +355,8 @@ def main():
     # Algorithmic bytes from the plan of each step.
     sl_h, rr_h = slots.cpu().numpy(), rows.cpu().numpy()
     plan = simulate_plan(sl_h, rr_h, a["pending"].numpy(), a["accepted"].numpy(), total, T)
-    fb = [fused_bytes(sl_h, rr_h, p, T, RQ, H, gated=args.gated_output, es=es)
+    fb = [fused_bytes(sl_h, rr_h, p, T, RQ, H, gated=args.gated_output, es=es,
+                      conv=args.conv)
           for p, _ in plan[args.warmup:]]
     cb = [commit_bytes(sl_h, l, rr_h, H, RQ, es=es) for _, l in plan[args.warmup:]]
     state_bytes = sum(f[0] + c[0] for f, c in zip(fb, cb))
@@ -342,8 +370,10 @@ def main():
     commit_total = sum(c[1] for c in cb) / len(cb)
     commit_state = sum(c[0] for c in cb) / len(cb)
     achieved = fused_total / (fused_mean_ms * 1e-3) / 1e9
-    traffic = measured_traffic("fused_replay_verify/large_decode" + ("_bf16" if bf16 else ""),
-                               source_digest(FUSED_SOURCES))
+    traffic = None
+    if not (bf16 or args.conv or args.gated_output):
+        traffic = measured_traffic("fused_replay_verify/large_decode",
+                                   source_digest(FUSED_SOURCES))
 
     result = {
         "metric": "state GB/s (% of HBM peak) + (req,head) items/s, KDA commit & fused verify",
@@ -368,6 +398,7 @@ def main():
             "global_batch": B, "seq_len": T, "heads": H, "parallelism": "none",
             "gated_output": bool(args.gated_output),
             "state_dtype": args.state_dtype,
+            "conv_prologue": bool(args.conv),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "items_per_s": round(items / (wall / args.steps), 1),

@@ -1,7 +1,8 @@
 /*
  * kda.h — C ABI of the MI355X (gfx950) KDA gated delta-rule state-update library
  * (libkda.so): the bounded gate decay, the RecoverSSM commit, the stock verify,
- * the fused replay+verify, and the two plan steps of deferred RecoverSSM.
+ * the fused replay+verify (optionally with its convolution prologue), and the
+ * two plan steps of deferred RecoverSSM.
  *
  * Sources are the vLLM API pages on Kimi-K3 KDA, cited by page title:
  *   [commit page]  vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.commit
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 #define KDA_OK 0
 #define KDA_EINVAL 1
@@ -196,6 +197,62 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             const int32_t* pending, const uint16_t* gate,
                             const float* norm_weight, float norm_eps, uint16_t* out,
                             void* stream);
+
+/*
+ * kda_fused_conv_replay_verify — kda_fused_replay_verify with its convolution
+ * prologue ([fused page], KdaFused: the convolution, its SiLU and the q/k
+ * normalisation): q, k and v are computed from pre-activations instead of
+ * being passed. For every (request b, head h) with slot > null_slot, part p
+ * (0 q, 1 k, 2 v) and head channel c, with column j = p*heads*128 + h*128 + c:
+ *  - the window w[i] = conv_state[slot*conv_slot_stride + j*conv_channel_stride
+ *    + i*conv_tap_stride], i < record_tokens + 2, holds the previous step's
+ *    [2 history values, its inputs]; the 3 taps are w[o..o+2] with
+ *    o = max(n - 1, 0), n the item's replay count (step 1 of the fused step);
+ *  - seq = [taps, x[b*tokens + t][j] for t < tokens];
+ *    pre_t = conv_bias[j] + sum_{i<4} conv_weight[p][i][h*128 + c] * seq[t + i]
+ *    (0 for a NULL bias; weight 3 meets the current input), and the part's
+ *    output is y_t = BF16(SiLU(pre_t)), SiLU(a) = a / (1 + exp(-a));
+ *    this rounding is decided in FP32 by fixed steps: an fma chain in tap order
+ *    from the bias, exp by Cody-Waite reduction (ln 2 split at 16 fraction
+ *    bits) and the degree-7 Taylor polynomial in Horner form on [-80, 80], an
+ *    IEEE divide, round to nearest even;
+ *  - q_t = y_q * (sum_c y_q^2 + 1e-6)^-1/2 * q_scale; k_t = y_k (normalised at
+ *    use, as always; the record keeps y_k's bits); v_t = y_v;
+ *  - the window is rewritten as [tap 1, tap 2, x_0 .. x_{tokens-1}]; entries
+ *    past tokens + 1 keep their values.
+ * The rest is kda_fused_replay_verify. Null-slot items write only their zero
+ * outputs.
+ *
+ *   x                    BF16 [batch*tokens] rows of x_row_stride elements
+ *                        (>= 3*heads*128): the q | k | v pre-activations in
+ *                        columns [0, 3*heads*128); other columns are not read
+ *   conv_weight          BF16 [3][4][heads*128]
+ *   conv_bias            BF16 [3*heads*128], or NULL for none
+ *   conv_state           BF16 window pool, read and written; strides >= 1 in
+ *                        elements. Windows of distinct (slot, column) pairs
+ *                        must not overlap. Dim-first [slots][3*heads*128][W]:
+ *                        strides (3*heads*128*W, W, 1); window-major
+ *                        [slots][W][3*heads*128]: (3*heads*128*W, 1, 3*heads*128);
+ *                        W >= record_tokens + 2
+ *   q_scale              finite (the pages use 128^-1/2)
+ *   raw_g, raw_beta, a_log, dt_bias, lower_bound, state_dtype, state,
+ *   state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
+ *   record_rows, pending, gate, norm_weight, norm_eps, out
+ *                        as kda_fused_replay_verify
+ */
+int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_t* x,
+                                 int64_t x_row_stride, const uint16_t* conv_weight,
+                                 const uint16_t* conv_bias, uint16_t* conv_state,
+                                 int64_t conv_slot_stride, int64_t conv_channel_stride,
+                                 int64_t conv_tap_stride, float q_scale, const uint16_t* raw_g,
+                                 const uint16_t* raw_beta, const float* a_log,
+                                 const float* dt_bias, float lower_bound, int state_dtype,
+                                 void* state, int64_t state_slot_stride,
+                                 const int32_t* state_indices, int null_slot, float* corr,
+                                 uint16_t* kg, int record_tokens, const int32_t* record_rows,
+                                 const int32_t* pending, const uint16_t* gate,
+                                 const float* norm_weight, float norm_eps, uint16_t* out,
+                                 void* stream);
 
 /*
  * kda_defer_commit — the defer step of deferred RecoverSSM ([kernels page],

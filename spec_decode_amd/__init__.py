@@ -17,6 +17,7 @@ import torch
 
 __all__ = [
     "kda_decay", "kda_commit", "kda_verify", "kda_fused_replay_verify",
+    "kda_fused_conv_replay_verify",
     "kda_defer_commit", "kda_flush_plan", "kda_last_error", "kda_abi_version",
     "kda_page_rw_probe",
     "library_path", "KdaError", "KDA_STATE_F32", "KDA_STATE_BF16",
@@ -52,6 +53,9 @@ _SIGS = {
                         _p, _p, _i, _p, _p, _p, _f, _p, _p]),
     "kda_fused_replay_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _i64,
                                      _p, _i, _p, _p, _i, _p, _p, _p, _p, _f, _p, _p]),
+    "kda_fused_conv_replay_verify": (_i, [_i, _i, _i, _p, _i64, _p, _p, _p, _i64, _i64, _i64,
+                                          _f, _p, _p, _p, _p, _f, _i, _p, _i64, _p, _i, _p,
+                                          _p, _i, _p, _p, _p, _p, _f, _p, _p]),
     "kda_defer_commit": (_i, [_i, _p, _p, _p, _p, _p, _i, _p]),
     "kda_flush_plan": (_i, [_i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
     "kda_page_rw_probe": (_i, [_i, _i, _p, _i64, _p, _i, _p]),
@@ -95,6 +99,19 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if not t.is_contiguous():
         raise TypeError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr_rows(t: torch.Tensor, dtype, row_stride: int, name: str):
+    """Device address of a row-major 2-D view whose rows are ``row_stride``
+    elements apart (e.g. a column slice of a wider tensor)."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a tensor on a ROCm device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != 2 or t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) != row_stride):
+        raise TypeError(f"{name} must be 2-D with unit column stride and row stride "
+                        f"{row_stride}")
     return t.data_ptr()
 
 
@@ -207,6 +224,32 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
         int(state_slot_stride), psi, int(null_slot), pc, pkg, int(record_tokens), prr,
         _ptr(pending, torch.int32, "pending"), *_gate_args(gate, norm_weight),
         float(norm_eps), po, _stream(stream, state)))
+    return out
+
+
+def kda_fused_conv_replay_verify(*, heads: int, tokens: int, batch: int, x, x_row_stride: int,
+                                 conv_weight, conv_state, conv_slot_stride: int,
+                                 conv_channel_stride: int, conv_tap_stride: int,
+                                 q_scale: float, raw_g, raw_beta, a_log, dt_bias,
+                                 lower_bound: float, state, state_slot_stride: int,
+                                 state_indices, corr, kg, record_tokens: int, record_rows,
+                                 pending, out, conv_bias=None, null_slot: int = 0, gate=None,
+                                 norm_weight=None, norm_eps: float = 1e-5, stream=None):
+    """The fused step with its convolution prologue: q, k, v from the packed
+    pre-activations ``x`` (rows of ``x_row_stride`` elements) and each channel's
+    window in ``conv_state`` (BF16, rewritten in place). Strides in elements."""
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _check(_lib.kda_fused_conv_replay_verify(
+        heads, tokens, batch, _ptr_rows(x, bf, int(x_row_stride), "x"), int(x_row_stride), _ptr(conv_weight, bf, "conv_weight"),
+        _ptr(conv_bias, bf, "conv_bias"), _ptr(conv_state, bf, "conv_state"),
+        int(conv_slot_stride), int(conv_channel_stride), int(conv_tap_stride),
+        float(q_scale), _ptr(raw_g, bf, "raw_g"), _ptr(raw_beta, bf, "raw_beta"),
+        _ptr(a_log, f32, "a_log"), _ptr(dt_bias, f32, "dt_bias"), float(lower_bound),
+        _state_dtype(state), _ptr(state, None, "state"), int(state_slot_stride),
+        _ptr(state_indices, i32, "state_indices"), int(null_slot), _ptr(corr, f32, "corr"),
+        _ptr(kg, bf, "kg"), int(record_tokens), _ptr(record_rows, i32, "record_rows"),
+        _ptr(pending, i32, "pending"), *_gate_args(gate, norm_weight), float(norm_eps),
+        _ptr(out, bf, "out"), _stream(stream, state)))
     return out
 
 

@@ -43,6 +43,17 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kPage = (int64_t)kda::K * kda::V;
 
+// The convolution prologue's operands (kda_fused_conv_replay_verify).
+struct ConvArgs {
+  const uint16_t* x;
+  int64_t x_row_stride;
+  const uint16_t* weight;
+  const uint16_t* bias;
+  uint16_t* state;
+  int64_t slot_stride, channel_stride, tap_stride;
+  float q_scale;
+};
+
 }  // namespace
 
 extern "C" {
@@ -155,7 +166,7 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
                          int null_slot, float* corr, uint16_t* kg, int record_tokens,
                          const int32_t* record_rows, const int32_t* pending,
                          const uint16_t* gate, const float* norm_weight, float norm_eps,
-                         uint16_t* out, void* stream) {
+                         uint16_t* out, void* stream, const ConvArgs* conv = nullptr) {
   KDA_REQUIRE(heads >= 1 && heads <= 65535, "%s: heads must be in 1..65535 (got %d)", who,
               heads);
   KDA_REQUIRE(tokens >= 1 && tokens <= KDA_MAX_WINDOW, "%s: tokens must be in 1..8 (got %d)",
@@ -172,9 +183,22 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
               "%s: gate and norm_weight must be given together", who);
   KDA_REQUIRE(gate == nullptr || (std::isfinite(norm_eps) && norm_eps >= 0.f),
               "%s: norm_eps must be finite and >= 0", who);
+  if (conv != nullptr) {
+    KDA_REQUIRE(std::isfinite(conv->q_scale), "%s: q_scale must be finite", who);
+    KDA_REQUIRE(conv->x_row_stride >= 3 * (int64_t)heads * kda::K,
+                "%s: x_row_stride %lld must be >= 3*heads*128", who,
+                (long long)conv->x_row_stride);
+    KDA_REQUIRE(conv->slot_stride >= 1 && conv->channel_stride >= 1 && conv->tap_stride >= 1,
+                "%s: convolution window strides must be >= 1", who);
+  }
   if (batch == 0) return ok();
-  KDA_REQUIRE(q && k && v && raw_g && raw_beta && a_log && dt_bias && state && state_indices &&
-                  corr && kg && out,
+  if (conv != nullptr) {
+    KDA_REQUIRE(conv->x && conv->weight && conv->state, "%s: null pointer argument", who);
+  } else {
+    KDA_REQUIRE(q && k && v, "%s: null pointer argument", who);
+  }
+  KDA_REQUIRE(raw_g && raw_beta && a_log && dt_bias && state && state_indices && corr && kg &&
+                  out,
               "%s: null pointer argument", who);
   if (fused)
     KDA_REQUIRE(record_rows && pending, "%s: record_rows and pending are required", who);
@@ -209,6 +233,17 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
   p.heads = heads;
   p.null_slot = null_slot;
   p.lb = lower_bound;
+  if (conv != nullptr) {
+    p.x = conv->x;
+    p.x_stride = conv->x_row_stride;
+    p.conv_w = conv->weight;
+    p.conv_b = conv->bias;
+    p.conv = conv->state;
+    p.conv_ss = conv->slot_stride;
+    p.conv_cs = conv->channel_stride;
+    p.conv_ts = conv->tap_stride;
+    p.q_scale = conv->q_scale;
+  }
   return launched(
       kda::launch_verify(p, tokens, fused, bf16, batch, reinterpret_cast<hipStream_t>(stream)),
       who);
@@ -242,6 +277,28 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                        state_slot_stride,
                        state_indices, null_slot, corr, kg, record_tokens, record_rows, pending,
                        gate, norm_weight, norm_eps, out, stream);
+}
+
+int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_t* x,
+                                 int64_t x_row_stride, const uint16_t* conv_weight,
+                                 const uint16_t* conv_bias, uint16_t* conv_state,
+                                 int64_t conv_slot_stride, int64_t conv_channel_stride,
+                                 int64_t conv_tap_stride, float q_scale, const uint16_t* raw_g,
+                                 const uint16_t* raw_beta, const float* a_log,
+                                 const float* dt_bias, float lower_bound, int state_dtype,
+                                 void* state, int64_t state_slot_stride,
+                                 const int32_t* state_indices, int null_slot, float* corr,
+                                 uint16_t* kg, int record_tokens, const int32_t* record_rows,
+                                 const int32_t* pending, const uint16_t* gate,
+                                 const float* norm_weight, float norm_eps, uint16_t* out,
+                                 void* stream) {
+  const ConvArgs conv{x,          x_row_stride,     conv_weight,         conv_bias, conv_state,
+                      conv_slot_stride, conv_channel_stride, conv_tap_stride, q_scale};
+  return verify_common("kda_fused_conv_replay_verify", true, heads, tokens, batch, nullptr,
+                       nullptr, nullptr, raw_g, raw_beta, a_log, dt_bias, lower_bound,
+                       state_dtype, state, state_slot_stride, state_indices, null_slot, corr, kg,
+                       record_tokens, record_rows, pending, gate, norm_weight, norm_eps, out,
+                       stream, &conv);
 }
 
 int kda_defer_commit(int batch, const int32_t* state_indices, int32_t* commit_lens,

@@ -155,6 +155,15 @@ struct VerifyParams {
   const uint16_t* gate;    // optional gated RMSNorm output stage: [B*T][H*V] BF16
   const float* norm_w;     // [V] FP32 (with gate)
   float norm_eps;
+  // Optional convolution prologue (fused only; x != NULL): q, k, v computed from
+  // x, replacing the q, k, v inputs.
+  const uint16_t* x;       // [B*T] rows of x_stride elements: q | k | v parts of H*K
+  const uint16_t* conv_w;  // [3][4][H*K] BF16
+  const uint16_t* conv_b;  // [3*H*K] BF16 or NULL
+  uint16_t* conv;          // window pool, element slot*conv_ss + channel*conv_cs + i*conv_ts
+  int64_t x_stride;
+  int64_t conv_ss, conv_cs, conv_ts;
+  float q_scale;
   int rq;
   int heads;
   int null_slot;
@@ -167,6 +176,8 @@ hipError_t launch_commit(const CommitParams& p, int window, bool bf16, bool alig
                          int layers, hipStream_t stream);
 hipError_t launch_verify(const VerifyParams& p, int tokens, bool fused, bool bf16, int batch,
                          hipStream_t stream);
+hipError_t launch_verify_conv(const VerifyParams& p, int tokens, bool bf16, int batch,
+                              hipStream_t stream);
 hipError_t launch_page_rw(float* state, int64_t slot_stride, const int32_t* slots, int batch,
                           int heads, int null_slot, hipStream_t stream);
 hipError_t launch_defer(int batch, const int32_t* state_indices, int32_t* commit_lens,

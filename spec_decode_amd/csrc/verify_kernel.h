@@ -1,0 +1,639 @@
+// The verify kernel template: fused replay+verify and the stock verify over
+// FP32 or BF16 state pages, with the optional convolution prologue and gated
+// RMSNorm output stage. Instantiated by fused.hip and fused_conv.hip.
+//
+// Method (the vLLM page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.
+// kda.fused", module docstring and KdaFused): per (request, head) item,
+//  1. replay the n pending tokens from the old records in the commit's closed
+//     form, S_n = S_0 diag(D_n) + sum_{t<n} u_t (kn_t * P_t)^T, writing S_n back
+//     when n > 0 (the stock verify, on the page "vllm.models.kimi_k3.nvidia.
+//     specialized_decode.recoverssm.kernels", is this kernel with no replay);
+//  2. verify the window's T tokens from S_n in chunked (WY) form:
+//     w_t = S_n (Gamma_t * kn_t), y_t = S_n (Gamma_t * q_t) (2T dots per row),
+//     A_ts, B_ts pair products, then per state row
+//     u_t = beta_t (v_t - w_t - sum_{s<t} A_ts u_s), o_t = y_t + sum_{s<=t} B_ts u_s;
+//  3. rewrite the item's records (u_t, raw key, raw gate), after every old
+//     record of the item was read.
+//
+// gfx950 mapping. One workgroup of 256 threads (4 wave64) per item. The page is
+// held in VGPRs as 16x16 tiles, wave w owning row blocks 2w and 2w+1 (all 8
+// column blocks each, 64 VGPRs). Within a tile (rows 16rb.., columns 16cb..),
+// lane l holds S[16rb + l%16][16cb + 4(l/16) + i], i = 0..3: one 16-byte load
+// per tile, and exactly the accumulator layout of V_MFMA_F32_16X16X4_F32 for
+// the transposed tile S^T (M = key channel, N = state row). So
+//  - the replay is S^T <- diag(D_n) S^T + KP U^T: 4 multiplies and one or two
+//    MFMAs (K = replayed tokens, zero-padded to 4 or 8) per tile, in place;
+//  - the same registers are the B operand of the dots: D2[j][v] += X[j][c] S[v][c]
+//    with M = j (2T <= 16 rows of X, zero above 2T), N = v, and the 4 values of a
+//    lane as 4 consecutive K steps (key channels 16cb + 4(l/16) + i);
+// so no lane ever exchanges state values and every state byte is read once.
+//
+// BF16 pages hold the same register layout after conversion, with the key
+// channels permuted inside each group of 32: one 16-byte load brings 8 channels
+// of a row, 32j + 8(l/16) .. +7, whose first 4 serve as tile 2j and last 4 as
+// tile 2j+1. A channel permutation leaves every contraction over channels
+// unchanged, so only the LDS reads of X, kp and D_n follow it (chan0 below).
+// S_n is stored rounded to nearest even; the verify continues from the FP32
+// value, before that rounding.
+//
+// Convolution prologue (fused page, KdaFused.kernel; template flag CONV): q, k
+// and v are computed in the kernel from a packed row x of pre-activations, each
+// channel's 4-tap causal convolution over its window in the conv pool followed
+// by SiLU. The window holds the previous step's [2 history values, its T
+// inputs]; after n accepted tokens the 3 taps start at max(n - 1, 0). The SiLU
+// output is rounded to BF16 and is the value used everywhere (the recorded key
+// is its bit pattern), so that rounding is taken by fixed FP32 steps: an fma
+// chain in tap order from the bias, exp by a Cody-Waite reduction and a degree-7
+// Taylor polynomial, an IEEE divide, round to nearest even. q is then
+// L2-normalised (1e-6 inside the root) and scaled by q_scale; the window is
+// rewritten as [tap 1, tap 2, x_0 .. x_{T-1}]. Threads 0..127 convolve the q and
+// k parts of channel c, threads 128..255 the v part.
+//
+// Prologue (while the page loads are in flight): threads 0..127 (channel c) do
+// the new tokens (decays, key norms, Gamma, X, the T^2 pair products reduced
+// over channels by a transposing wave reduction); threads 128..255 do the old
+// records (decays, norms, kp_t = kn_t * prod_{t<s<n} d_s, D_n), the
+// corrections, v and beta. The small loads are issued before the page loads so
+// that the in-order return of loads lets the prologue start early.
+#pragma once
+
+#include <utility>
+
+#include "kda_device.h"
+
+namespace kda {
+
+template <int T>
+struct Pairs {
+  static constexpr int NA = T * (T - 1) / 2;  // A_ts, s < t
+  static constexpr int NP = T * T;            // then B_ts, s <= t
+  static constexpr int P2 = NP <= 1 ? 1 : NP <= 2 ? 2 : NP <= 4 ? 4 : NP <= 8 ? 8
+                          : NP <= 16 ? 16 : NP <= 32 ? 32 : 64;
+  static constexpr int G = P2 < 16 ? P2 : 16;  // values reduced per exchange group
+  __device__ static constexpr int a(int t, int s) { return t * (t - 1) / 2 + s; }
+  __device__ static constexpr int b(int t, int s) { return NA + t * (t + 1) / 2 + s; }
+};
+
+// Which pair product sits at index i: A_ts (s < t) at t(t-1)/2 + s, then B_ts
+// (s <= t) at NA + t(t+1)/2 + s. Built at compile time so that every register
+// index below folds to a constant.
+template <int T>
+struct PairTable {
+  int s[64], t[64], is_a[64];
+  constexpr PairTable() : s(), t(), is_a() {
+    int i = 0;
+    for (int tt = 1; tt < T; ++tt)
+      for (int ss = 0; ss < tt; ++ss) { s[i] = ss; t[i] = tt; is_a[i] = 1; ++i; }
+    for (int tt = 0; tt < T; ++tt)
+      for (int ss = 0; ss <= tt; ++ss) { s[i] = ss; t[i] = tt; is_a[i] = 0; ++i; }
+    for (; i < 64; ++i) { s[i] = 0; t[i] = 0; is_a[i] = -1; }
+  }
+};
+
+// This channel's share of pair product I: A_ts = kn_s * P(s,t) * kn_t or
+// B_ts = kn_s * P(s,t) * q_t with P(s,t) = prod_{s<r<=t} d_r; zero past T^2.
+template <int T, int I>
+__device__ __forceinline__ float pair_share(const float (&kn)[T], const float (&q)[T],
+                                            const float (&d)[T]) {
+  constexpr PairTable<T> tab{};
+  constexpr int s = tab.s[I], t = tab.t[I], kind = tab.is_a[I];
+  if constexpr (kind < 0) {
+    return 0.f;
+  } else {
+    float pr = kn[s];
+#pragma unroll
+    for (int r = s + 1; r <= t; ++r) pr *= d[r];
+    return pr * (kind == 1 ? kn[t] : q[t]);
+  }
+}
+
+template <int T, int G0, int... Is>
+__device__ __forceinline__ void pair_group(float (&pv)[sizeof...(Is)], const float (&kn)[T],
+                                           const float (&q)[T], const float (&d)[T],
+                                           std::integer_sequence<int, Is...>) {
+  ((pv[Is] = pair_share<T, G0 + Is>(kn, q, d)), ...);
+}
+
+// The pair products summed over the 128 channels, stage one (lower waves, one
+// channel per lane): two in-register transposing steps over the lane quads
+// leave each lane P2/4 partial sums of 4 channels (for P2 >= 4), which go to
+// part[pair][quad of the half] in LDS; stage two sums those per pair.
+template <int T>
+struct PairStage {
+  static constexpr int P2 = Pairs<T>::P2;
+  static constexpr int STEPS = P2 >= 4 ? 2 : (P2 == 2 ? 1 : 0);
+  static constexpr int R = P2 >> STEPS;           // values a lane keeps
+  static constexpr int PARTS = 128 >> STEPS;      // partials per pair (both waves)
+};
+
+template <int T, int... Is>
+__device__ __forceinline__ void pair_stage_one(const float (&kn)[T], const float (&q)[T],
+                                               const float (&d)[T], int lane, int wave,
+                                               float* part, std::integer_sequence<int, Is...>) {
+  using PS = PairStage<T>;
+  float pv[PS::P2];
+  ((pv[Is] = pair_share<T, Is>(kn, q, d)), ...);
+  if constexpr (PS::STEPS >= 1) quad_transpose_step<PS::P2, 1>(pv);
+  if constexpr (PS::STEPS >= 2) quad_transpose_step<PS::P2 / 2, 2>(pv);
+  // Lane l now holds, in slot i, pair i + R*(bit1 of l) + 2R*(bit0 of l)
+  // (only the bits the steps used), summed over its 2^STEPS lanes.
+  const int sel = PS::STEPS == 2 ? ((lane & 1) * 2 + ((lane >> 1) & 1)) : (PS::STEPS == 1 ? (lane & 1) : 0);
+  const int group = wave * (64 >> PS::STEPS) + (lane >> PS::STEPS);
+#pragma unroll
+  for (int i = 0; i < PS::R; ++i) part[(i + PS::R * sel) * PS::PARTS + group] = pv[i];
+}
+
+// exp in FP32 for the convolution's SiLU: x clamped to [-80, 80],
+// k = rint(x log2 e), r = x - k ln2 by two fmas (ln2 split into its value
+// rounded to 16 fraction bits and the FP32 remainder), then the Taylor
+// polynomial sum_{j<=7} r^j / j! in Horner form (fma), scaled by 2^k.
+__device__ __forceinline__ float conv_exp(float x) {
+  constexpr float kLn2Hi = 45426.0f / 65536.0f;
+  constexpr float kLn2Lo = (float)(0.69314718055994530942 - (double)kLn2Hi);
+  constexpr float kLog2e = 1.44269504088896340736f;
+  x = fminf(fmaxf(x, -80.0f), 80.0f);
+  const float k = rintf(x * kLog2e);
+  float r = __builtin_fmaf(-k, kLn2Hi, x);
+  r = __builtin_fmaf(-k, kLn2Lo, r);
+  float p = 1.0f / 5040.0f;                 // 1/7!
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);  // 1/6!
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 2.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)k);
+}
+
+// One channel's convolution outputs: seq = 3 taps then T inputs, w the 4
+// weights (w[3] meets the current input). Returns the BF16 bits of SiLU.
+template <int T>
+__device__ __forceinline__ void conv_silu(const float (&seq)[3 + T], const float (&w)[4],
+                                          float bias, uint32_t (&y)[T]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float acc = bias;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(seq[t + i], w[i], acc);
+    const float e = conv_exp(-acc);
+    y[t] = f32_to_bf16_bits(__fdiv_rn(acc, 1.0f + e));
+  }
+}
+
+// c ? a : b for a wave-uniform c, as one opaque v_cndmask: a plain select
+// between two array elements would be folded into an indexed access, which
+// forces the array out of registers.
+__device__ __forceinline__ uint32_t uniform_pick(uint64_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(mask));
+  return r;
+}
+
+// The window's 3 taps at a wave-uniform offset off in 0..MAX_T-1 (entries
+// loaded as raw bits, index i at position i): a barrel shift by the bits of
+// off, each stage a choice between two constant positions.
+__device__ __forceinline__ void window_taps(const uint32_t (&wn)[MAX_T + 2], int off,
+                                            uint32_t (&taps)[3]) {
+  static_assert(MAX_T == 8, "three shift stages cover offsets 0..7");
+  const int o = __builtin_amdgcn_readfirstlane(off);
+  const uint64_t m4 = (o & 4) ? ~0ull : 0ull, m2 = (o & 2) ? ~0ull : 0ull,
+                 m1 = (o & 1) ? ~0ull : 0ull;
+  uint32_t s1[6], s2[4];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) s1[j] = uniform_pick(m4, wn[j + 4], wn[j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s2[j] = uniform_pick(m2, s1[j + 2], s1[j]);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) taps[j] = uniform_pick(m1, s2[j + 1], s2[j]);
+}
+
+// One channel's convolution operands as raw BF16 bits: the window entries
+// (index i at position i, clamped to the window so every load is in bounds),
+// the T inputs, the 4 weights and the bias.
+template <int T>
+struct ConvIn {
+  uint32_t win[MAX_T + 2];
+  uint32_t x[T];
+  uint32_t w[4];
+  uint32_t bias;
+};
+
+// Loads of channel col (= part * H*K + head channel) of the conv operands.
+template <int T>
+__device__ __forceinline__ void conv_load(const VerifyParams& p, ConvIn<T>& ci, int slot,
+                                          int64_t col, int64_t head_row, int part,
+                                          int64_t dim, int64_t tok0) {
+  const uint16_t* wp = p.conv + (int64_t)slot * p.conv_ss + col * p.conv_cs;
+#pragma unroll
+  for (int i = 0; i < MAX_T + 2; ++i)
+    ci.win[i] = wp[(int64_t)(i < p.rq + 2 ? i : p.rq + 1) * p.conv_ts];
+#pragma unroll
+  for (int t = 0; t < T; ++t) ci.x[t] = p.x[(tok0 + t) * p.x_stride + col];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ci.w[i] = p.conv_w[(part * 4 + i) * dim + head_row];
+  ci.bias = p.conv_b != nullptr ? p.conv_b[col] : 0u;
+}
+
+// The channel's taps at the offset, its convolution + SiLU (BF16 bits into y),
+// then the window write-back [tap 1, tap 2, x_0 .. x_{T-1}]: the thread
+// rewrites only entries of its own channel, which it has read.
+template <int T>
+__device__ __forceinline__ void conv_part(const VerifyParams& p, const ConvIn<T>& ci, int slot,
+                                          int64_t col, int off, uint32_t (&y)[T]) {
+  uint32_t taps[3];
+  window_taps(ci.win, off, taps);
+  float seq[3 + T];
+  float w[4];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) seq[i] = bf16_bits_to_f32(taps[i]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) seq[3 + t] = bf16_bits_to_f32(ci.x[t]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = bf16_bits_to_f32(ci.w[i]);
+  conv_silu<T>(seq, w, bf16_bits_to_f32(ci.bias), y);
+  uint16_t* wp = p.conv + (int64_t)slot * p.conv_ss + col * p.conv_cs;
+  wp[0] = (uint16_t)taps[1];
+  wp[p.conv_ts] = (uint16_t)taps[2];
+#pragma unroll
+  for (int t = 0; t < T; ++t) wp[(int64_t)(2 + t) * p.conv_ts] = (uint16_t)ci.x[t];
+}
+
+// First key channel of lane group g (= lane / 16) in tile cb: values i = 0..3
+// of the lane are channels chan0 + i.
+template <bool SB16>
+__device__ __forceinline__ constexpr int chan0(int cb, int g) {
+  return SB16 ? 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) : 16 * cb + 4 * g;
+}
+
+template <int T, bool FUSED, bool GATED, bool SB16, bool CONV>
+__global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
+  static_assert(FUSED || !CONV, "the convolution prologue is a fused-step prologue");
+  using PI = Pairs<T>;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int H = p.heads;
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  // The wave index as a scalar: branches on it are uniform (s_cbranch), so a
+  // wave runs only its own half's code and waits only on its own loads.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int64_t tok0 = (int64_t)b * T;
+
+  const int slot = p.slots[b];
+  if (slot <= p.null_slot) {
+    // No state: the item's outputs are zero and nothing else is written.
+    if (tid < T * (V / 8)) {
+      const int t = tid / (V / 8);
+      const int c = (tid % (V / 8)) * 8;
+      *reinterpret_cast<uint4*>(p.out + ((tok0 + t) * H + h) * V + c) = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  const int rec = p.rows != nullptr ? p.rows[b] : b;
+  int n = 0;
+  if constexpr (FUSED) {
+    if (rec >= 0) {
+      n = p.pending[rec];
+      n = n < 0 ? 0 : (n > p.rq ? p.rq : n);
+    }
+  }
+  const bool replay = FUSED && n > 0;
+
+  __shared__ __attribute__((aligned(16))) float x_s[16][K];    // Gamma_t kn_t | Gamma_t q_t | 0
+  __shared__ __attribute__((aligned(16))) float kp_s[MAX_T][K];  // replay kn_t P_t (0 past n)
+  __shared__ __attribute__((aligned(16))) float u_s[MAX_T][V];   // replay u_t (0 past n)
+  __shared__ __attribute__((aligned(16))) float dn_s[K];
+  __shared__ __attribute__((aligned(16))) float v_s[T][V];
+  __shared__ __attribute__((aligned(16))) float dots_s[V][16];   // w_t | y_t per state row
+  __shared__ float pair_s[PI::P2];
+  __shared__ __attribute__((aligned(16))) float part_s[PI::P2][PairStage<T>::PARTS];
+  __shared__ float ssq_s[2][2][MAX_T];  // [new | old keys][wave of the half][token]
+  __shared__ float qsq_s[2][MAX_T];     // convolution prologue: q sums of squares
+  __shared__ float beta_s[MAX_T];
+  __shared__ uint32_t kg_s[T][K];
+  __shared__ float osq_s[2][T];  // output stage: per-wave sums of o_bf^2  // raw key | raw gate << 16 of the window, for the records
+
+  const int c = tid & (K - 1);   // channel / state row of this thread's half
+  const bool lower = wave < 2;   // threads 0..127: new tokens; 128..255: records, v, beta
+  const int64_t head_row = (int64_t)h * K + c;
+
+  // ---- 1-2. Loads. Loads return in order, so a wave's first use of a small
+  // input waits for every load issued before it. The new-token waves (0, 1)
+  // issue their small loads first and the page after, so their prologue starts
+  // while the page streams in; the record waves (2, 3) issue the page first,
+  // then theirs (their prologue needs the records, which arrive after).
+  const float a_log_h = p.a_log[h];
+  const float dtb = p.dt_bias[head_row];
+  // Output stage inputs (compiled in only for the gated instances).
+  constexpr bool gated = GATED;
+  float nw = 1.f;
+  uint32_t gtb[T];
+  if constexpr (GATED) {
+    nw = p.norm_w[c];
+#pragma unroll
+    for (int t = 0; t < T; ++t) gtb[t] = p.gate[(tok0 + t) * H * V + head_row];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t kb[T], gb[T], qb[T];  // lower: new raw key, gate, q bits
+  uint32_t vb[T];                // upper: new v bits
+  // Convolution prologue: per part this thread convolves (lower: q, k; upper:
+  // v), the window entries (clamped to the window, so every load is in bounds),
+  // the T inputs, the 4 weights and the bias, all as raw BF16 bits.
+  ConvIn<T> cin0, cin1;  // lower: q part, k part; upper: v part in cin0
+  const int64_t dim = (int64_t)H * K;
+  uint32_t okb[MAX_T], ogb[MAX_T];
+  float ou[MAX_T];
+  uint32_t rbb = 0;
+  // Page tiles: 16-byte loads, one per tile (FP32) or per pair of tiles (BF16),
+  // kept as loaded until the state pass converts them.
+  constexpr int ES = SB16 ? 2 : 4;        // bytes per state element
+  constexpr int NLD = SB16 ? 4 : 8;       // 16-byte loads per row block
+  constexpr int LDC = 16 / ES;            // channels per load
+  const int lr = lane & 15;  // row within a tile
+  const int lq = lane >> 4;  // channel group within a tile
+  char* const page = static_cast<char*>(p.state) +
+                     ((int64_t)slot * p.slot_stride + (int64_t)h * PAGE) * ES;
+  char* const tile0 = page + ((16 * (2 * wave) + lr) * K + LDC * lq) * ES;
+  u32x4 st[2][NLD];
+  if (lower) {
+    if constexpr (CONV) {
+      conv_load<T>(p, cin0, slot, 0 * dim + head_row, head_row, 0, dim, tok0);
+      conv_load<T>(p, cin1, slot, 1 * dim + head_row, head_row, 1, dim, tok0);
+#pragma unroll
+      for (int t = 0; t < T; ++t) gb[t] = p.g[(tok0 + t) * H * K + head_row];
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int64_t idx = (tok0 + t) * H * K + head_row;
+        kb[t] = p.k[idx];
+        gb[t] = p.g[idx];
+        qb[t] = p.q[idx];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        st[r][j] = *reinterpret_cast<const u32x4*>(tile0 + (16 * r * K + 4 * LDC * j) * ES);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        st[r][j] = *reinterpret_cast<const u32x4*>(tile0 + (16 * r * K + 4 * LDC * j) * ES);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (CONV) {
+      conv_load<T>(p, cin0, slot, 2 * dim + head_row, head_row, 2, dim, tok0);
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + t) * H * V + head_row];
+    }
+    rbb = p.rb[(tok0 + (c < T ? c : T - 1)) * H + h];  // unconditional: no divergent load
+    if constexpr (FUSED) {
+      const int64_t rbase = ((int64_t)(rec < 0 ? 0 : rec) * H + h) * p.rq;
+#pragma unroll
+      for (int t = 0; t < MAX_T; ++t) {
+        okb[t] = 0;
+        ogb[t] = 0;
+        ou[t] = 0.f;
+        if (t < n) {
+          okb[t] = p.kg[(rbase + t) * 2 * K + c];
+          ogb[t] = p.kg[(rbase + t) * 2 * K + K + c];
+          ou[t] = p.corr[(rbase + t) * V + c];
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. Prologue, part one: decays, key sums of squares, staging.
+  const float ea = __expf(a_log_h);
+  float kf[T], qf[T], dnew[T];
+  float okf[MAX_T], od[MAX_T];
+  // Convolution prologue: taps at the replay-aware offset, convolution + SiLU,
+  // then the window write-back (each thread rewrites only the entries of its
+  // own channels, which it has read).
+  const int conv_off = n > 0 ? n - 1 : 0;
+  if (lower) {
+    if constexpr (CONV) {
+      conv_part<T>(p, cin0, slot, 0 * dim + head_row, conv_off, qb);
+      conv_part<T>(p, cin1, slot, 1 * dim + head_row, conv_off, kb);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      kf[t] = bf16_bits_to_f32(kb[t]);
+      qf[t] = bf16_bits_to_f32(qb[t]);
+      if constexpr (CONV) {
+        const float sq = wave_sum(qf[t] * qf[t]);
+        if (lane == 0) qsq_s[wave][t] = sq;
+      }
+      dnew[t] = gate_decay(bf16_bits_to_f32(gb[t]), ea, dtb, p.lb);
+      kg_s[t][c] = kb[t] | (gb[t] << 16);  // raw bits for the record write-back
+      const float s = wave_sum(kf[t] * kf[t]);
+      if (lane == 0) ssq_s[0][wave][t] = s;
+    }
+  } else {
+    if constexpr (CONV) conv_part<T>(p, cin0, slot, 2 * dim + head_row, conv_off, vb);
+#pragma unroll
+    for (int t = 0; t < T; ++t) v_s[t][c] = bf16_bits_to_f32(vb[t]);
+    if (c < T) beta_s[c] = sigmoidf_fast(bf16_bits_to_f32(rbb));
+    if constexpr (FUSED) {
+      if (replay) {
+#pragma unroll
+        for (int t = 0; t < MAX_T; ++t) {
+          okf[t] = bf16_bits_to_f32(okb[t]);
+          od[t] = gate_decay(bf16_bits_to_f32(ogb[t]), ea, dtb, p.lb);
+          u_s[t][c] = ou[t];  // zero past n
+          if (t < n) {
+            const float s = wave_sum(okf[t] * okf[t]);
+            if (lane == 0) ssq_s[1][wave - 2][t] = s;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. Prologue, part two: X, pair products, replay coefficients.
+  if (lower) {
+    float kn[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      kn[t] = kf[t] * __builtin_amdgcn_rsqf(ssq_s[0][0][t] + ssq_s[0][1][t] + 1e-6f);
+    if constexpr (CONV) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        qf[t] = qf[t] * __builtin_amdgcn_rsqf(qsq_s[0][t] + qsq_s[1][t] + 1e-6f) * p.q_scale;
+    }
+    float gam = 1.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      gam *= dnew[t];
+      x_s[t][c] = gam * kn[t];
+      x_s[T + t][c] = gam * qf[t];
+    }
+#pragma unroll
+    for (int j = 2 * T; j < 16; ++j) x_s[j][c] = 0.f;
+    // A_ts, B_ts summed over the 128 channels: each wave reduces groups of G
+    // values with the transposing exchange, then the two waves' sums meet in LDS.
+    pair_stage_one<T>(kn, qf, dnew, lane, wave, &part_s[0][0],
+                      std::make_integer_sequence<int, PI::P2>{});
+  } else {
+    if constexpr (FUSED) {
+      if (replay) {
+        float pp = 1.f;
+#pragma unroll
+        for (int t = MAX_T - 1; t >= 0; --t) {
+          float w = 0.f;
+          if (t < n) {
+            const float kn =
+                okf[t] * __builtin_amdgcn_rsqf(ssq_s[1][0][t] + ssq_s[1][1][t] + 1e-6f);
+            w = kn * pp;
+            pp *= od[t];
+          }
+          kp_s[t][c] = w;
+        }
+        dn_s[c] = pp;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- Pair products, stage two: 4 threads per pair add its partials.
+  {
+    using PS = PairStage<T>;
+    constexpr int PER = PS::PARTS / 4;
+    if (tid < PS::P2 * 4) {
+      const int pr = tid >> 2;
+      const float* src = &part_s[pr][(tid & 3) * PER];
+      float acc2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc2 += src[i];
+      acc2 += dpp_f<DPP_XOR1>(acc2);
+      acc2 += dpp_f<DPP_XOR2>(acc2);
+      if ((tid & 3) == 0) pair_s[pr] = acc2;
+    }
+  }
+
+  // ---- 5. The state pass: replay in place (MFMA), store S_n, 2T dots (MFMA).
+  float ub[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  if (replay) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int vrow = 16 * (2 * wave + r) + lr;
+      ub[r][0] = u_s[lq][vrow];
+      ub[r][1] = u_s[4 + lq][vrow];
+    }
+  }
+  floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  u32x4 sn[2];  // BF16 pages: S_n of the even tile, stored with the odd one
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const int c0 = chan0<SB16>(cb, lq);
+    const floatx4 xa = *reinterpret_cast<const floatx4*>(&x_s[lr][c0]);
+    floatx4 dn4 = {1.f, 1.f, 1.f, 1.f};
+    float ka0 = 0.f, ka1 = 0.f;
+    if (replay) {
+      // A operand row lr of the replay MFMA is the channel of accumulator row lr.
+      const int ca = chan0<SB16>(cb, lr >> 2) + (lr & 3);
+      dn4 = *reinterpret_cast<const floatx4*>(&dn_s[c0]);
+      ka0 = kp_s[lq][ca];
+      ka1 = kp_s[4 + lq][ca];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      floatx4 s;
+      if constexpr (SB16) {
+        const u32x4 w = st[r][cb >> 1];
+        const uint32_t w0 = (cb & 1) ? w[2] : w[0];
+        const uint32_t w1 = (cb & 1) ? w[3] : w[1];
+        s = floatx4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+      } else {
+        s = __builtin_bit_cast(floatx4, st[r][cb]);
+      }
+      if (replay) {
+        s = s * dn4;
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka0, ub[r][0], s, 0, 0, 0);
+        if (n > 4) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka1, ub[r][1], s, 0, 0, 0);
+        char* const dst = tile0 + (16 * r * K + 4 * LDC * (SB16 ? cb >> 1 : cb)) * ES;
+        if constexpr (SB16) {
+          sn[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
+          sn[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);
+          if (cb & 1) *reinterpret_cast<u32x4*>(dst) = sn[r];
+        } else {
+          *reinterpret_cast<floatx4*>(dst) = s;
+        }
+      }
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[0], s[0], acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[1], s[1], acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[2], s[2], acc[r], 0, 0, 0);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[3], s[3], acc[r], 0, 0, 0);
+    }
+  }
+  // acc[r], lane l, value i: column j = 4(l/16) + i of state row 16(2w+r) + l%16.
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    *reinterpret_cast<floatx4*>(&dots_s[16 * (2 * wave + r) + lr][4 * lq]) = acc[r];
+  __syncthreads();
+
+  // ---- 6. Per state row: the T x T forward substitution, outputs, records.
+  float ob[T];
+  if (lower) {
+    const int vrow = c;
+    float us[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float a = v_s[t][vrow] - dots_s[vrow][t];
+#pragma unroll
+      for (int s = 0; s < t; ++s) {
+        const int ia = PI::a(t, s);
+        a = fmaf(-pair_s[ia], us[s], a);
+      }
+      us[t] = beta_s[t] * a;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float o = dots_s[vrow][T + t];
+#pragma unroll
+      for (int s = 0; s <= t; ++s) {
+        const int ib = PI::b(t, s);
+        o = fmaf(pair_s[ib], us[s], o);
+      }
+      if constexpr (GATED) {
+        // The output stage normalises the BF16-rounded o over the head's rows.
+        ob[t] = bf16_bits_to_f32(f32_to_bf16_bits(o));
+        const float sq = wave_sum(ob[t] * ob[t]);
+        if (lane == 0) osq_s[wave][t] = sq;
+      } else {
+        p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
+      }
+    }
+    if (rec >= 0) {
+      const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        p.corr[(rbase + t) * V + vrow] = us[t];
+        const uint32_t bits = kg_s[t][c];
+        p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(bits & 0xffffu);
+        p.kg[(rbase + t) * 2 * K + K + c] = (uint16_t)(bits >> 16);
+      }
+    }
+  }
+  if constexpr (GATED) {
+    __syncthreads();
+    if (lower) {
+      const float inv_v = 1.0f / V;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float rstd =
+            __builtin_amdgcn_rsqf((osq_s[0][t] + osq_s[1][t]) * inv_v + p.norm_eps);
+        const float sg = sigmoidf_fast(bf16_bits_to_f32(gtb[t]));
+        p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(ob[t] * rstd * nw * sg);
+      }
+    }
+  }
+}
+
+}  // namespace kda

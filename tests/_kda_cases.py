@@ -203,3 +203,75 @@ def compare_verify(gpu, ref, orig, *, fused, H, B, T, RQ, slots, rows, pending, 
 
 def window_np(win: "W.Window"):
     return {name: np_of(getattr(win, name)) for name in ("q", "k", "v", "raw_g", "raw_beta")}
+
+
+# ---------------------------------------------------------------- fused + convolution
+
+def conv_pool_layout(S, H, W, dim_first=True):
+    """Strides (slot, channel, tap) of a [S, 3HK, W] (dim-first) or [S, W, 3HK]
+    (window-major) window pool, in elements."""
+    hk3 = 3 * H * K
+    return (hk3 * W, W, 1) if dim_first else (hk3 * W, 1, hk3)
+
+
+def conv_written(slots, H, RQ, T, strides, null_slot, n_elems):
+    """Mask of the window entries a call rewrites: 2 + T per (live slot, column)."""
+    m = np.zeros(n_elems, dtype=bool)
+    ss, cs, ts = strides
+    cols = np.arange(3 * H * K)
+    for s in slots:
+        if s <= null_slot:
+            continue
+        for i in range(2 + T):
+            m[int(s) * ss + cols * cs + i * ts] = True
+    return m
+
+
+def run_conv_case(*, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, raw_g, raw_beta,
+                  x, pitch, conv_w, conv_b, pool, strides, rows, pending,
+                  lb=W.LOWER_BOUND, null_slot=0, label="fused conv", gate=None,
+                  norm_weight=None, norm_eps=1e-5, q_scale=K ** -0.5):
+    """kda_fused_conv_replay_verify on the GPU and the oracle on host copies.
+    Host arrays: x uint16 [B*T, pitch], conv_w uint16 [3, 4, HK], conv_b uint16
+    [3HK] or None, pool uint16 flat window pool with the given strides; the
+    rest as run_verify_case."""
+    import spec_decode_amd as kda
+    stride = H * V * K
+    announce(f"{label}: H={H} B={B} T={T} RQ={RQ} state={state.dtype} strides={strides}")
+    d = dict(state=to_dev(state), corr=dev(corr), kg=dev_bf16(kg), pool=dev_bf16(pool),
+             out=torch.zeros((B * T, H * V), dtype=torch.bfloat16, device=DEV))
+    d["out"].view(torch.int16).fill_(0x7FFF)
+    kda.kda_fused_conv_replay_verify(
+        heads=H, tokens=T, batch=B, x=dev_bf16(x), x_row_stride=pitch,
+        conv_weight=dev_bf16(conv_w), conv_bias=None if conv_b is None else dev_bf16(conv_b),
+        conv_state=d["pool"], conv_slot_stride=strides[0], conv_channel_stride=strides[1],
+        conv_tap_stride=strides[2], q_scale=q_scale, raw_g=dev_bf16(raw_g),
+        raw_beta=dev_bf16(raw_beta), a_log=dev(np.asarray(a_log, np.float32)),
+        dt_bias=dev(np.asarray(dt_bias, np.float32)), lower_bound=lb, state=d["state"],
+        state_slot_stride=stride, state_indices=dev(np.asarray(slots, np.int32)),
+        corr=d["corr"], kg=d["kg"], record_tokens=RQ,
+        record_rows=dev(np.asarray(rows, np.int32)),
+        pending=dev(np.asarray(pending, np.int32)), out=d["out"], null_slot=null_slot,
+        gate=None if gate is None else dev_bf16(gate),
+        norm_weight=None if norm_weight is None else dev(np.asarray(norm_weight, np.float32)),
+        norm_eps=norm_eps)
+    torch.cuda.synchronize()
+    gpu = {k: np_of(v) for k, v in d.items()}
+    ref = dict(state=state.copy(), corr=corr.copy(), kg=kg.copy(), pool=pool.copy(),
+               out=np.full((B * T, H * V), 0x7FFF, np.uint16))
+    oracle.fused_conv_replay_verify(
+        heads=H, tokens=T, batch=B, x=x, x_row_stride=pitch, conv_weight=conv_w,
+        conv_bias=conv_b, conv_state=ref["pool"], conv_slot_stride=strides[0],
+        conv_channel_stride=strides[1], conv_tap_stride=strides[2], q_scale=q_scale,
+        raw_g=raw_g, raw_beta=raw_beta, a_log=a_log, dt_bias=dt_bias, lower_bound=lb,
+        state=ref["state"], state_slot_stride=stride, state_indices=slots, corr=ref["corr"],
+        kg=ref["kg"], record_tokens=RQ, record_rows=rows, pending=pending, out=ref["out"],
+        null_slot=null_slot, gate=gate, norm_weight=norm_weight, norm_eps=norm_eps)
+    compare_verify(gpu, ref, dict(state=state, corr=corr, kg=kg), fused=True, H=H, B=B, T=T,
+                   RQ=RQ, slots=slots, rows=rows, pending=pending, stride=stride,
+                   null_slot=null_slot, label=label,
+                   out_ulps=GATED_OUT_ULPS if gate is not None else 1)
+    cm = conv_written(slots, H, RQ, T, strides, null_slot, pool.size)
+    assert_exact(f"{label} windows (written)", gpu["pool"][cm], ref["pool"][cm])
+    assert_exact(f"{label} windows (untouched)", gpu["pool"][~cm], pool[~cm])
+    return gpu, ref

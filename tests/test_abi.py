@@ -28,6 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_decay", "kda_commit", "kda_verify", "kda_fused_replay_verify",
+                 "kda_fused_conv_replay_verify",
                  "kda_defer_commit", "kda_flush_plan", "kda_last_error", "kda_abi_version"):
         assert want in names
 
@@ -98,6 +99,29 @@ def test_rejects_bad_arguments_without_launch(lib):
     assert lib.kda_decay(fake, ctypes.c_int64(3), ctypes.c_int(2), fake, fake,
                          ctypes.c_float(float("nan")), fake, P(None)) == 1
     assert "finite" in _err(lib)
+
+
+def test_conv_entry_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    f = lib.kda_fused_conv_replay_verify
+    f.restype = ctypes.c_int
+
+    def call(x_stride=3 * 4 * 128, q_scale=128 ** -0.5, strides=(100, 10, 1), x=0x1000,
+             tokens=4):
+        I64 = ctypes.c_int64
+        return f(ctypes.c_int(4), ctypes.c_int(tokens), ctypes.c_int(2), P(x), I64(x_stride),
+                 fake, P(None), fake, I64(strides[0]), I64(strides[1]), I64(strides[2]),
+                 ctypes.c_float(q_scale), fake, fake, fake, fake, ctypes.c_float(-5.0),
+                 ctypes.c_int(0), fake, I64(4 * 128 * 128), fake, ctypes.c_int(0), fake, fake,
+                 ctypes.c_int(4), fake, fake, P(None), P(None), ctypes.c_float(1e-5), fake,
+                 P(None))
+
+    assert call(x_stride=3 * 4 * 128 - 1) == 1 and "x_row_stride" in _err(lib)
+    assert call(q_scale=float("inf")) == 1 and "q_scale" in _err(lib)
+    assert call(strides=(100, 0, 1)) == 1 and "strides" in _err(lib)
+    assert call(x=0) == 1 and "null pointer" in _err(lib)
+    assert call(tokens=9) == 1 and "tokens" in _err(lib)
 
 
 def test_commit_rejects_bad_tables(lib):

@@ -147,6 +147,31 @@ def test_config2_fused_full_gated_output():
                     norm_eps=eps, label="config2 fused gated output")
 
 
+def test_config2_fused_conv_full():
+    """The fused workload with the convolution prologue at full size (H=32,
+    B=128, q=4): q, k, v from packed pre-activations and a dim-first window pool
+    of 256 slots, against the full oracle, windows compared bit for bit."""
+    from _kda_cases import conv_pool_layout, run_conv_case
+
+    w = W.config2()
+    H, B, T, RQ, S = w.heads, w.batch, w.tokens, w.record_tokens, w.slots
+    a = w.arrays
+    state = a["state"].numpy().copy()
+    slots, rows = a["state_indices"].numpy(), a["record_rows"].numpy()
+    corr, kg = a["corr"].numpy().copy(), W.bits(a["kg"])
+    _oracle_prior_records(w, state, corr, kg, slots, rows, T, RQ, H, B)
+    pending = np.zeros(B, np.int32)
+    pending[rows] = a["pending"].numpy()
+    cv = W.draw_conv_inputs(W._gen(2 + 300), B, T, H, RQ, S)
+    win = window_np(w.windows["new"])
+    run_conv_case(H=H, B=B, T=T, RQ=RQ, state=state, slots=slots, corr=corr, kg=kg,
+                  a_log=a["a_log"][0].numpy(), dt_bias=a["dt_bias"][0].numpy(),
+                  raw_g=win["raw_g"], raw_beta=win["raw_beta"], x=W.bits(cv.x), pitch=cv.pitch,
+                  conv_w=W.bits(cv.weight), conv_b=W.bits(cv.bias),
+                  pool=W.bits(cv.window).reshape(-1), strides=conv_pool_layout(S, H, RQ + 2),
+                  rows=rows, pending=pending, lb=w.lower_bound, label="config2 fused conv")
+
+
 # ---------------------------------------------------------------- config 3
 
 def test_config3_align_commit_full_size_sampled():

@@ -10,8 +10,8 @@ import torch
 import oracle
 import workloads as W
 from _compare import assert_exact, assert_f32_close
-from _kda_cases import (DEV, announce, dev, dev_bf16, np_of, run_commit_case,
-                        run_verify_case, window_np)
+from _kda_cases import (DEV, announce, conv_pool_layout, dev, dev_bf16, np_of,
+                        run_commit_case, run_conv_case, run_verify_case, window_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -268,3 +268,61 @@ def test_gated_output_stage(T, fused, bf16):
                     win=c["win"], rows=c["rows"], pending=pending if fused else None,
                     gate=W.bits(gate), norm_weight=weight.numpy(), norm_eps=eps,
                     label=f"gated output fused={fused} T={T}")
+
+
+# ---------------------------------------------------------------- fused + convolution
+
+def _conv_case(seed, H, B, T, RQ, S, bf16=False, dim_first=True, null_rows=(), norec_rows=()):
+    c = _vf_case(seed, H, B, T, RQ, S, null_rows=null_rows, norec_rows=norec_rows, bf16=bf16)
+    cv = W.draw_conv_inputs(W._gen(seed + 7), B, T, H, RQ, S)
+    win = W.bits(cv.window)  # [S, 3HK, RQ + 2]
+    c["strides"] = conv_pool_layout(S, H, RQ + 2, dim_first)
+    c["pool"] = (win if dim_first else win.transpose(0, 2, 1)).reshape(-1).copy()
+    c.update(x=W.bits(cv.x), pitch=cv.pitch, conv_w=W.bits(cv.weight), conv_b=W.bits(cv.bias))
+    return c
+
+
+def _run_conv(c, H, B, T, RQ, pending, label, bias=True, **kw):
+    return run_conv_case(H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
+                         corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                         raw_g=c["win"]["raw_g"], raw_beta=c["win"]["raw_beta"], x=c["x"],
+                         pitch=c["pitch"], conv_w=c["conv_w"],
+                         conv_b=c["conv_b"] if bias else None, pool=c["pool"],
+                         strides=c["strides"], rows=c["rows"], pending=pending, label=label,
+                         **kw)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_fused_conv_windows(T, bf16):
+    H, B = 3, 6
+    for RQ in sorted({T, 8}):
+        c = _conv_case(700 + T, H, B, T, RQ, 10, bf16=bf16, dim_first=(T + RQ) % 2 == 0,
+                       null_rows=(1,), norec_rows=(3,))
+        rng = np.random.default_rng(T * 10 + RQ)
+        pending = rng.integers(0, RQ + 1, B).astype(np.int32)
+        live = [b for b in range(B) if b not in (1, 3)]
+        for b, e in zip(live, [0, RQ, RQ + 3, -2]):
+            pending[c["rows"][b]] = e
+        _run_conv(c, H, B, T, RQ, pending, f"fused conv T={T} RQ={RQ}")
+
+
+@pytest.mark.parametrize("dim_first", [True, False])
+def test_fused_conv_every_pending_count(dim_first):
+    """One request per n = 0..8: every window offset 0..7, no convolution bias."""
+    H, B, T, RQ = 2, 9, 4, 8
+    c = _conv_case(777, H, B, T, RQ, 12, dim_first=dim_first)
+    pending = np.zeros(B, np.int32)
+    for b in range(B):
+        pending[c["rows"][b]] = b
+    _run_conv(c, H, B, T, RQ, pending, "fused conv n=0..8", bias=False)
+
+
+@pytest.mark.parametrize("T,bf16", [(3, False), (8, False), (4, True)])
+def test_fused_conv_gated_output(T, bf16):
+    H, B, RQ = 3, 5, 8
+    c = _conv_case(800 + T, H, B, T, RQ, 9, bf16=bf16, null_rows=(2,), norec_rows=(4,))
+    gate, weight, eps = W.draw_output_stage(W._gen(900 + T), B, T, H)
+    pending = np.random.default_rng(T).integers(0, RQ + 1, B).astype(np.int32)
+    _run_conv(c, H, B, T, RQ, pending, f"fused conv gated T={T}", gate=W.bits(gate),
+              norm_weight=weight.numpy(), norm_eps=eps)

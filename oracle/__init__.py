@@ -68,6 +68,7 @@ def _load():
         "kda_o_silu_bf16": (ctypes.c_uint16, [ctypes.c_float]),
         "kda_o_conv_silu": (None, [i, _fp, _fp, ctypes.c_float, _u16p]),
         "kda_o_conv_offset": (i, [i]),
+        "kda_o_gate_projection": (None, [l, i, i, _u16p, ctypes.c_int64, _u16p, _u16p]),
         "kda_o_decay_buf": (None, [l, i, i, _u16p, _fp, _fp, d, _fp]),
         "kda_o_defer": (None, [i, _i32p, _i32p, _i32p, _i32p, _i32p, i]),
         "kda_o_flush_plan": (None, [i, i, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
@@ -384,6 +385,26 @@ def conv_silu(seq, w, bias=0.0):
     _load().kda_o_conv_silu(T, _ptr(seq, _fp), _ptr(w, _fp), ctypes.c_float(bias),
                             _ptr(y, _u16p))
     return y
+
+
+def gate_projection(f_a, f_b, f_a_row_stride=None, tokens=None):
+    """raw_g [N, D] BF16 bits = BF16(F_A F_B^T), f_b uint16 [D, R]. f_a is either
+    a uint16 [N, R] array, or a flat uint16 buffer whose row t starts at
+    t * f_a_row_stride (then ``tokens`` gives N)."""
+    f_b = _c(f_b, np.uint16)
+    D, R = f_b.shape
+    f_a = _c(f_a, np.uint16)
+    if f_a.ndim == 2:
+        N, sa = f_a.shape[0], f_a.shape[1]
+        assert sa >= R
+    else:
+        N, sa = int(tokens), int(f_a_row_stride)
+        assert f_a.size >= (N - 1) * sa + R
+    flat = f_a.reshape(-1)
+    out = np.zeros((N, D), np.uint16)
+    _load().kda_o_gate_projection(N, D, R, _ptr(flat, _u16p), sa, _ptr(f_b, _u16p),
+                                  _ptr(out, _u16p))
+    return out
 
 
 def conv_offset(n):

@@ -155,6 +155,26 @@ void kda_o_conv_silu(int T, const float* seq, const float* w, float bias, uint16
   }
 }
 
+/* ------------------------------------------------------------------------- */
+/* Low-rank gate projection ([fused page] KdaFused.kernel, the gate           */
+/* projection)                                                                */
+/* ------------------------------------------------------------------------- */
+
+/* raw_g[t][f] = BF16(sum_j F_A[t][j] * F_B[f][j]), j < R (R = 128 on the page):
+ * F_A row t at f_a + t * sa (BF16 bits), F_B row f at f_b + f * R, out row t at
+ * out + t * D. FP64 sum, rounded once. */
+void kda_o_gate_projection(long N, int D, int R, const uint16_t* f_a, int64_t sa,
+                           const uint16_t* f_b, uint16_t* out) {
+  for (long t = 0; t < N; ++t)
+    for (int f = 0; f < D; ++f) {
+      double acc = 0.0;
+      for (int j = 0; j < R; ++j)
+        acc += kda_o_bf16_to_double(f_a[t * sa + j]) *
+               kda_o_bf16_to_double(f_b[(int64_t)f * R + j]);
+      out[t * (int64_t)D + f] = kda_o_double_to_bf16(acc);
+    }
+}
+
 /* The window offset of a fused step: the history after n accepted tokens of the
  * previous window starts at n - 1 (at 0 when nothing is pending). */
 int kda_o_conv_offset(int n) { return n > 0 ? n - 1 : 0; }

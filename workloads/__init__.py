@@ -116,6 +116,23 @@ def draw_conv_inputs(gen, B: int, T: int, H: int, RQ: int, slots: int) -> ConvIn
     return ConvInputs(x, weight, bias, window)
 
 
+def draw_gate_factors(gen, N: int, H: int, exact: bool = True, rank: int = 128):
+    """Factors of the low-rank gate projection raw_g = F_A F_B^T: F_A [N, rank]
+    and F_B [H*128, rank], BF16.
+
+    exact (default): values on a grid, F_A = m * 2^-6 and F_B = m' * 2^-7 with
+    m, m' = round(N(0, 24)) clipped to [-127, 127]. Every product and every
+    partial sum of a row is then an integer multiple of 2^-13 below 2^21 * 2^-13,
+    so an FP32 accumulation is exact in any order and raw_g's BF16 rounding is
+    the same decision on every implementation; raw_g ~ N(0, 0.8).
+    Otherwise F_A = BF16(N(0, 1)), F_B = BF16(N(0, 1) / sqrt(rank))."""
+    if exact:
+        ma = torch.clamp(torch.round(normal(gen, (N, rank), 24.0)), -127, 127)
+        mb = torch.clamp(torch.round(normal(gen, (H * K, rank), 24.0)), -127, 127)
+        return bf16(ma * 2.0 ** -6), bf16(mb * 2.0 ** -7)
+    return bf16(normal(gen, (N, rank))), bf16(normal(gen, (H * K, rank), rank ** -0.5))
+
+
 def draw_gate_params(gen, L: int, H: int):
     a_log = normal(gen, (L, H), 0.5)
     dt_bias = normal(gen, (L, H, K), 0.1)

@@ -54,6 +54,9 @@ def parse_args():
     ap.add_argument("--conv", action="store_true",
                     help="run the fused step with its convolution prologue (q, k, v from "
                          "packed pre-activations and a window pool)")
+    ap.add_argument("--gate-proj", action="store_true",
+                    help="compute raw_g in the step with kda_gate_projection (F_A a column "
+                         "slice of packed projection rows, F_B [H*128, 128])")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 2 GiB device copy (streaming ceiling)")
     return ap.parse_args()
@@ -266,6 +269,16 @@ def main():
                     bias=cv.bias.to(dev), pool=cv.window.to(dev).reshape(-1))
         hk3 = 3 * H * K
         conv["strides"] = (hk3 * (RQ + 2), RQ + 2, 1)
+    gp = None
+    if args.gate_proj:
+        hk = H * K
+        pitch = (4 * hk + 128 + H + 7) // 8 * 8
+        packed = conv["x"] if conv is not None else W.bf16(
+            W.normal(W._gen(4 + 500), (B * T, pitch))).to(dev)
+        gp = dict(f_a=packed[:, 4 * hk:], pitch=packed.shape[1],
+                  f_b=W.draw_gate_factors(W._gen(4 + 501), 1, H, exact=False)[1].to(dev),
+                  raw_g=torch.empty((B * T, H, K), dtype=torch.bfloat16, device=dev))
+    raw_g = new.raw_g if gp is None else gp["raw_g"]
     commit_lens = torch.empty(B, dtype=torch.int32, device=dev)
     flush = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
 
@@ -302,15 +315,20 @@ def main():
                        destinations=flush[1], record_rows=rows, lower_bound=lb)
 
     total = args.warmup + args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
 
     def step(i):
         e = ev[i]
         commit_lens.copy_(accepted)
+        e[4].record()
+        if gp is not None:
+            kda.kda_gate_projection(tokens=B * T, heads=H, f_a=gp["f_a"],
+                                    f_a_row_stride=gp["pitch"], f_b=gp["f_b"],
+                                    raw_g=gp["raw_g"])
         e[0].record()
         if conv is None:
             kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v,
-                                        raw_g=new.raw_g, raw_beta=new.raw_beta, a_log=a_log,
+                                        raw_g=raw_g, raw_beta=new.raw_beta, a_log=a_log,
                                         dt_bias=dt_bias, lower_bound=lb, state=state,
                                         state_slot_stride=state_stride, state_indices=slots,
                                         corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
@@ -322,7 +340,7 @@ def main():
                 heads=H, tokens=T, batch=B, x=conv["x"], x_row_stride=conv["pitch"],
                 conv_weight=conv["weight"], conv_bias=conv["bias"], conv_state=conv["pool"],
                 conv_slot_stride=cs[0], conv_channel_stride=cs[1], conv_tap_stride=cs[2],
-                q_scale=K ** -0.5, raw_g=new.raw_g, raw_beta=new.raw_beta, a_log=a_log,
+                q_scale=K ** -0.5, raw_g=raw_g, raw_beta=new.raw_beta, a_log=a_log,
                 dt_bias=dt_bias, lower_bound=lb, state=state, state_slot_stride=state_stride,
                 state_indices=slots, corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
                 pending=pending, out=out, gate=gate, norm_weight=norm_w, norm_eps=norm_eps)
@@ -350,7 +368,8 @@ def main():
     timed = ev[args.warmup:]
     fused_ms = [e[0].elapsed_time(e[1]) for e in timed]
     commit_ms = [e[2].elapsed_time(e[3]) for e in timed]
-    step_ms = [e[0].elapsed_time(e[3]) for e in timed]
+    step_ms = [e[4].elapsed_time(e[3]) for e in timed]
+    gp_ms = [e[4].elapsed_time(e[0]) for e in timed]
 
     # Algorithmic bytes from the plan of each step.
     sl_h, rr_h = slots.cpu().numpy(), rows.cpu().numpy()
@@ -371,7 +390,7 @@ def main():
     commit_state = sum(c[0] for c in cb) / len(cb)
     achieved = fused_total / (fused_mean_ms * 1e-3) / 1e9
     traffic = None
-    if not (bf16 or args.conv or args.gated_output):
+    if not (bf16 or args.conv or args.gated_output or args.gate_proj):
         traffic = measured_traffic("fused_replay_verify/large_decode",
                                    source_digest(FUSED_SOURCES))
 
@@ -399,6 +418,7 @@ def main():
             "gated_output": bool(args.gated_output),
             "state_dtype": args.state_dtype,
             "conv_prologue": bool(args.conv),
+            "gate_projection": bool(args.gate_proj),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "items_per_s": round(items / (wall / args.steps), 1),
@@ -414,6 +434,11 @@ def main():
                 "total_gbs": round(commit_total / (commit_mean_ms * 1e-3) / 1e9, 1),
                 "items_per_s": round(items / (commit_mean_ms * 1e-3), 1)},
             "step_event_ms": round(sum(step_ms) / len(step_ms), 4),
+            **({"gate_projection": {
+                "mean_ms": round(sum(gp_ms) / len(gp_ms), 4),
+                "total_gbs": round((B * T * (256 + H * K * 2) + H * K * 256)
+                                   / (sum(gp_ms) / len(gp_ms) * 1e-3) / 1e9, 1)}}
+               if gp is not None else {}),
         },
         "roofline": {
             "kernel": "fused_replay_verify",

@@ -1,8 +1,8 @@
 /*
  * kda.h — C ABI of the MI355X (gfx950) KDA gated delta-rule state-update library
  * (libkda.so): the bounded gate decay, the RecoverSSM commit, the stock verify,
- * the fused replay+verify (optionally with its convolution prologue), and the
- * two plan steps of deferred RecoverSSM.
+ * the fused replay+verify (optionally with its convolution prologue), the
+ * low-rank gate projection, and the two plan steps of deferred RecoverSSM.
  *
  * Sources are the vLLM API pages on Kimi-K3 KDA, cited by page title:
  *   [commit page]  vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.commit
@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 #define KDA_OK 0
 #define KDA_EINVAL 1
@@ -253,6 +253,29 @@ int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_
                                  const int32_t* pending, const uint16_t* gate,
                                  const float* norm_weight, float norm_eps, uint16_t* out,
                                  void* stream);
+
+/*
+ * kda_gate_projection — the low-rank gate projection that produces raw_g
+ * ([fused page], KdaFused: the gate projection):
+ *     raw_g[t][f] = BF16(sum_{j<128} f_a[t][j] * f_b[f][j]),  f < heads*128,
+ * FP32 accumulation (BF16 matrix cores), rounded to nearest even. The result
+ * is the raw_g operand of kda_verify / kda_fused_replay_verify /
+ * kda_fused_conv_replay_verify and of the records. The FP32 sum's order is the
+ * hardware's: where the exact sum lies within FP32 rounding of a BF16 rounding
+ * boundary, the result can be the neighbouring BF16 value.
+ *
+ *   tokens               >= 0 (0: no launch)
+ *   heads                1..65535
+ *   f_a                  BF16 [tokens] rows of f_a_row_stride elements (>= 128,
+ *                        a multiple of 8); columns 0..127 are read (e.g. a column
+ *                        slice of a packed projection row)
+ *   f_b                  BF16 [heads*128][128], row-major
+ *   raw_g                BF16 [tokens][heads][128]; written
+ * All three 16-byte aligned.
+ */
+int kda_gate_projection(int64_t tokens, int heads, const uint16_t* f_a,
+                        int64_t f_a_row_stride, const uint16_t* f_b, uint16_t* raw_g,
+                        void* stream);
 
 /*
  * kda_defer_commit — the defer step of deferred RecoverSSM ([kernels page],

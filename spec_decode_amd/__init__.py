@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "kda_decay", "kda_commit", "kda_verify", "kda_fused_replay_verify",
-    "kda_fused_conv_replay_verify",
+    "kda_fused_conv_replay_verify", "kda_gate_projection",
     "kda_defer_commit", "kda_flush_plan", "kda_last_error", "kda_abi_version",
     "kda_page_rw_probe",
     "library_path", "KdaError", "KDA_STATE_F32", "KDA_STATE_BF16",
@@ -56,6 +56,7 @@ _SIGS = {
     "kda_fused_conv_replay_verify": (_i, [_i, _i, _i, _p, _i64, _p, _p, _p, _i64, _i64, _i64,
                                           _f, _p, _p, _p, _p, _f, _i, _p, _i64, _p, _i, _p,
                                           _p, _i, _p, _p, _p, _p, _f, _p, _p]),
+    "kda_gate_projection": (_i, [_i64, _i, _p, _i64, _p, _p, _p]),
     "kda_defer_commit": (_i, [_i, _p, _p, _p, _p, _p, _i, _p]),
     "kda_flush_plan": (_i, [_i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
     "kda_page_rw_probe": (_i, [_i, _i, _p, _i64, _p, _i, _p]),
@@ -251,6 +252,18 @@ def kda_fused_conv_replay_verify(*, heads: int, tokens: int, batch: int, x, x_ro
         _ptr(pending, i32, "pending"), *_gate_args(gate, norm_weight), float(norm_eps),
         _ptr(out, bf, "out"), _stream(stream, state)))
     return out
+
+
+def kda_gate_projection(*, tokens: int, heads: int, f_a, f_a_row_stride: int, f_b, raw_g,
+                        stream=None):
+    """raw_g [tokens, heads*128] = BF16(F_A F_B^T): f_a rows of ``f_a_row_stride``
+    elements (columns 0..127 read), f_b [heads*128, 128]."""
+    bf = torch.bfloat16
+    _check(_lib.kda_gate_projection(int(tokens), int(heads),
+                                    _ptr_rows(f_a, bf, int(f_a_row_stride), "f_a"),
+                                    int(f_a_row_stride), _ptr(f_b, bf, "f_b"),
+                                    _ptr(raw_g, bf, "raw_g"), _stream(stream, f_b)))
+    return raw_g
 
 
 def kda_defer_commit(*, batch: int, state_indices, commit_lens, record_rows, pending,

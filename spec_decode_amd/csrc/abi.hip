@@ -301,6 +301,26 @@ int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_
                        stream, &conv);
 }
 
+int kda_gate_projection(int64_t tokens, int heads, const uint16_t* f_a,
+                        int64_t f_a_row_stride, const uint16_t* f_b, uint16_t* raw_g,
+                        void* stream) {
+  KDA_REQUIRE(tokens >= 0, "kda_gate_projection: tokens must be >= 0 (got %lld)",
+              (long long)tokens);
+  KDA_REQUIRE(heads >= 1 && heads <= 65535,
+              "kda_gate_projection: heads must be in 1..65535 (got %d)", heads);
+  KDA_REQUIRE(f_a_row_stride >= kda::K && f_a_row_stride % 8 == 0,
+              "kda_gate_projection: f_a_row_stride %lld must be >= 128 and a multiple of 8",
+              (long long)f_a_row_stride);
+  KDA_REQUIRE((tokens + 63) / 64 < ((int64_t)1 << 31), "kda_gate_projection: too many tokens");
+  if (tokens == 0) return ok();
+  KDA_REQUIRE(f_a && f_b && raw_g, "kda_gate_projection: null pointer argument");
+  KDA_REQUIRE(aligned16(f_a) && aligned16(f_b) && aligned16(raw_g),
+              "kda_gate_projection: f_a, f_b and raw_g must be 16-byte aligned");
+  return launched(kda::launch_gate_projection(f_a, f_a_row_stride, f_b, raw_g, tokens, heads,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                  "kda_gate_projection");
+}
+
 int kda_defer_commit(int batch, const int32_t* state_indices, int32_t* commit_lens,
                      const int32_t* record_rows, int32_t* pending, const int32_t* eager,
                      int null_slot, void* stream) {

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_decay", "kda_commit", "kda_verify", "kda_fused_replay_verify",
-                 "kda_fused_conv_replay_verify",
+                 "kda_fused_conv_replay_verify", "kda_gate_projection",
                  "kda_defer_commit", "kda_flush_plan", "kda_last_error", "kda_abi_version"):
         assert want in names
 
@@ -122,6 +122,24 @@ def test_conv_entry_rejects_bad_arguments(lib):
     assert call(strides=(100, 0, 1)) == 1 and "strides" in _err(lib)
     assert call(x=0) == 1 and "null pointer" in _err(lib)
     assert call(tokens=9) == 1 and "tokens" in _err(lib)
+
+
+def test_gate_projection_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    f = lib.kda_gate_projection
+    f.restype = ctypes.c_int
+    I64 = ctypes.c_int64
+
+    def call(tokens=10, heads=2, stride=136, fa=0x1000, fb=0x2000, out=0x3000):
+        return f(I64(tokens), ctypes.c_int(heads), P(fa), I64(stride), P(fb), P(out), P(None))
+
+    assert call(stride=100) == 1 and "f_a_row_stride" in _err(lib)
+    assert call(stride=130) == 1 and "f_a_row_stride" in _err(lib)
+    assert call(heads=0) == 1 and "heads" in _err(lib)
+    assert call(tokens=-1) == 1 and "tokens" in _err(lib)
+    assert call(fa=0x1008) == 1 and "aligned" in _err(lib)
+    assert call(out=0) == 1 and "null" in _err(lib)
+    assert call(tokens=0, fa=0, fb=0, out=0) == 0
 
 
 def test_commit_rejects_bad_tables(lib):

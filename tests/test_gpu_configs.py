@@ -172,6 +172,31 @@ def test_config2_fused_conv_full():
                   rows=rows, pending=pending, lb=w.lower_bound, label="config2 fused conv")
 
 
+def test_large_decode_gate_projection_sampled():
+    """The gate projection at the large decode batch's size (4096 tokens, 64
+    heads, F_A a column slice of packed projection rows): 64 sampled tokens
+    bit-exact against the oracle (exact-grid factors), every element written."""
+    import spec_decode_amd as kda
+    N, H = 512 * 8, 64
+    hk = H * K
+    pitch = (4 * hk + 128 + H + 7) // 8 * 8
+    fa, fb = W.draw_gate_factors(W._gen(4 + 400), N, H)
+    packed = W.bf16(W.normal(W._gen(4 + 401), (N, pitch))).to(DEV)
+    packed[:, 4 * hk:4 * hk + K] = fa.to(DEV)
+    out = torch.zeros((N, hk), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(0x7FFF)
+    announce("large decode gate projection")
+    kda.kda_gate_projection(tokens=N, heads=H, f_a=packed[:, 4 * hk:], f_a_row_stride=pitch,
+                            f_b=fb.to(DEV), raw_g=out)
+    torch.cuda.synchronize()
+    got = np_of(out)
+    pick = np.random.default_rng(7).choice(N, 64, replace=False)
+    want = oracle.gate_projection(W.bits(fa)[pick], W.bits(fb))
+    assert_exact("raw_g (sampled tokens)", got[pick], want)
+    # the sentinel 0x7FFF is NaN: an unwritten element would show as one
+    assert not np.any(got == 0x7FFF)
+
+
 # ---------------------------------------------------------------- config 3
 
 def test_config3_align_commit_full_size_sampled():

@@ -326,3 +326,46 @@ def test_fused_conv_gated_output(T, bf16):
     pending = np.random.default_rng(T).integers(0, RQ + 1, B).astype(np.int32)
     _run_conv(c, H, B, T, RQ, pending, f"fused conv gated T={T}", gate=W.bits(gate),
               norm_weight=weight.numpy(), norm_eps=eps)
+
+
+# ---------------------------------------------------------------- gate projection
+
+def _gate_proj_gpu(fa_bits, pitch, col0, fb_bits, N, H):
+    """Runs kda_gate_projection with F_A as columns col0.. of packed rows of
+    width pitch; returns raw_g bits [N, H*128]."""
+    import spec_decode_amd as kda
+    packed = np.zeros((N, pitch), np.uint16)
+    packed[:, col0:col0 + K] = fa_bits
+    d_packed = dev_bf16(packed)
+    out = torch.zeros((N, H * K), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(0x7FFF)
+    kda.kda_gate_projection(tokens=N, heads=H, f_a=d_packed[:, col0:], f_a_row_stride=pitch,
+                            f_b=dev_bf16(fb_bits), raw_g=out)
+    torch.cuda.synchronize()
+    return np_of(out)
+
+
+@pytest.mark.parametrize("N,H,pitch,col0", [(1, 1, 128, 0), (17, 3, 136, 8), (64, 2, 128, 0),
+                                            (100, 3, 1000, 600), (257, 2, 264, 128)])
+def test_gate_projection_exact_grid(N, H, pitch, col0):
+    """On the generator's exact grid every FP32 partial sum is exact, so the
+    BF16 result is bit-identical to the oracle's."""
+    announce(f"gate projection exact N={N} H={H} pitch={pitch}")
+    fa, fb = W.draw_gate_factors(W._gen(1000 + N), N, H)
+    got = _gate_proj_gpu(W.bits(fa), pitch, col0, W.bits(fb), N, H)
+    want = oracle.gate_projection(W.bits(fa), W.bits(fb))
+    assert_exact("raw_g", got, want)
+
+
+def test_gate_projection_general_inputs():
+    """General BF16 factors: within one BF16 ulp of the FP64 product rounded
+    once (a different FP32 summation order can cross a rounding boundary),
+    and equal almost everywhere."""
+    from _compare import bf16_mismatch
+    N, H = 200, 4
+    announce(f"gate projection general N={N} H={H}")
+    fa, fb = W.draw_gate_factors(W._gen(2000), N, H, exact=False)
+    got = _gate_proj_gpu(W.bits(fa), 128, 0, W.bits(fb), N, H)
+    want = oracle.gate_projection(W.bits(fa), W.bits(fb))
+    assert not bf16_mismatch(got, want, ulps=1).any()
+    assert (got == want).mean() > 0.999

@@ -501,13 +501,16 @@ int kda_o_commit(int L, int H, int Q, int B, int K, int V, int state_bf16,
 
 /* kda_verify / kda_fused_replay_verify ([kernels page] kda_recoverssm_verify;
  * [fused page] module docstring and KdaFused.kernel). Items are (request, head).
- *  - state slot <= null: the item's T x V outputs are zero; nothing else.
+ *  - the item's window: rows tok0 + t, t < L, with tok0 = b*T and L = T, or
+ *    (query_start_loc given) tok0 = qsl[b], L = clamp(qsl[b+1] - qsl[b], 0, T);
+ *    L = 0 is padding: nothing is read or written.
+ *  - state slot <= null: the item's L x V outputs are zero; nothing else.
  *  - record row rec = record_rows[b] (or b when record_rows is NULL).
  *  - fused only: n = clamp(pending[rec], 0, RQ) when rec >= 0, else 0; the n
  *    recorded tokens are replayed onto S_0 and S_n is written back when n > 0.
- *  - the stock recurrence runs over the T new tokens from S_n (verify: S_0);
- *    o -> BF16 out[b*T + t][h*V + v].
- *  - rec >= 0: the records of tokens t < T are rewritten (u_t FP32, raw key and
+ *  - the stock recurrence runs over the L new tokens from S_n (verify: S_0);
+ *    o -> BF16 out[tok0 + t][h*V + v].
+ *  - rec >= 0: the records of tokens t < L are rewritten (u_t FP32, raw key and
  *    raw gate bit copies), after every old record of the item was read.
  * q is used as given; keys are normalised; beta = sigmoid(raw_beta). */
 struct verify_ctx {
@@ -529,6 +532,7 @@ struct verify_ctx {
   const uint16_t* gate;  /* optional gated RMSNorm epilogue */
   const float* norm_w;
   double norm_eps;
+  const int32_t* qsl;     /* optional [B+1] token offsets (variable-length windows) */
   /* optional convolution prologue (x != NULL): q, k, v are its outputs */
   const uint16_t* x;      /* [B*T] rows of x_stride: q | k | v pre-activations */
   int64_t x_stride;
@@ -599,11 +603,21 @@ static void verify_item(void* p, long it) {
   int K = c->K, V = c->V, T = c->T, H = c->H, RQ = c->RQ;
   int h = (int)(item % H);
   int b = (int)(item / H);
+  /* The item's tokens: rows tok0 .. tok0 + T - 1, with T its window length
+   * (query_start_loc: qsl[b+1] - qsl[b], clamped to 0..T). An empty window is
+   * padding: nothing is read or written. */
+  int64_t tok0 = (int64_t)b * T;
+  if (c->qsl) {
+    tok0 = c->qsl[b];
+    int L = c->qsl[b + 1] - c->qsl[b];
+    T = L < 0 ? 0 : (L > T ? T : L);
+  }
+  if (T == 0) return;
   int slot = c->slots[b];
   if (slot <= c->null_slot) {
     for (int t = 0; t < T; ++t)
       for (int v = 0; v < V; ++v)
-        c->out[((int64_t)b * T + t) * H * V + (int64_t)h * V + v] = kda_o_double_to_bf16(0.0);
+        c->out[(tok0 + t) * H * V + (int64_t)h * V + v] = kda_o_double_to_bf16(0.0);
     return;
   }
   int rec = c->rows ? c->rows[b] : b;
@@ -659,7 +673,7 @@ static void verify_item(void* p, long it) {
     conv_prologue(c, b, h, slot, n, ycv);
   }
   for (int t = 0; t < T; ++t) {
-    int64_t tok = (int64_t)b * T + t;
+    int64_t tok = tok0 + t;
     const uint16_t* qt = ycv ? ycv + (0 * T + t) * K : c->q + (tok * H + h) * K;
     const uint16_t* kt = ycv ? ycv + (1 * T + t) * K : c->k + (tok * H + h) * K;
     const uint16_t* vt = ycv ? ycv + (2 * T + t) * K : c->v + (tok * H + h) * V;
@@ -682,9 +696,9 @@ static void verify_item(void* p, long it) {
   kda_o_verify_seq(K, V, T, S, qq, kn, vv, d, beta, o, u);
 
   for (int t = 0; t < T; ++t) {
-    uint16_t* orow = c->out + ((int64_t)b * T + t) * H * V + (int64_t)h * V;
+    uint16_t* orow = c->out + (tok0 + t) * H * V + (int64_t)h * V;
     if (c->gate && c->norm_w) {
-      gated_rmsnorm(V, o + t * V, c->gate + ((int64_t)b * T + t) * H * V + (int64_t)h * V,
+      gated_rmsnorm(V, o + t * V, c->gate + (tok0 + t) * H * V + (int64_t)h * V,
                     c->norm_w, c->norm_eps, orow);
     } else {
       for (int v = 0; v < V; ++v) orow[v] = kda_o_double_to_bf16(o[t * V + v]);
@@ -694,7 +708,7 @@ static void verify_item(void* p, long it) {
     float* corr = c->corr + (((int64_t)rec * H + h) * RQ) * V;
     uint16_t* kg = c->kg + (((int64_t)rec * H + h) * RQ) * 2 * K;
     for (int t = 0; t < T; ++t) {
-      int64_t tok = (int64_t)b * T + t;
+      int64_t tok = tok0 + t;
       for (int v = 0; v < V; ++v) corr[t * V + v] = to_f32(u[t * V + v]);
       for (int ch = 0; ch < K; ++ch) {
         kg[t * 2 * K + ch] = ycv ? ycv[(1 * T + t) * K + ch] : c->k[(tok * H + h) * K + ch];
@@ -724,13 +738,14 @@ int kda_o_verify(int H, int T, int B, int K, int V, const uint16_t* q, const uin
                  long n_items, int threads, const uint16_t* gate, const float* norm_w,
                  double norm_eps, int state_bf16, const uint16_t* x, int64_t x_stride,
                  const uint16_t* conv_w, const uint16_t* conv_b, uint16_t* conv,
-                 int64_t conv_ss, int64_t conv_cs, int64_t conv_ts, double q_scale) {
+                 int64_t conv_ss, int64_t conv_cs, int64_t conv_ts, double q_scale,
+                 const int32_t* query_start_loc) {
   struct verify_ctx c = {H,          T,          B,       K,          V,
                          RQ,         fused,      state_bf16, q,       k,          v,
                          raw_g,      raw_beta,   a_log,   dt_bias,    lower_bound,
                          state,      state_slot_stride, state_indices, null_slot, corr,
                          kg,         record_rows, pending, out,       items,
-                         gate,       norm_w,     norm_eps, x,         x_stride,
+                         gate,       norm_w,     norm_eps, query_start_loc, x, x_stride,
                          conv_w,     conv_b,     conv,    conv_ss,    conv_cs,
                          conv_ts,    q_scale};
   long count = items ? n_items : (long)B * H;

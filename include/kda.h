@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 #define KDA_OK 0
 #define KDA_EINVAL 1
@@ -150,6 +150,14 @@ int kda_commit(int layers, int heads, int window, int batch, int state_dtype,
  *   kg                   BF16 records [rows][heads][record_tokens][256]
  *   record_tokens        RQ in tokens..8
  *   record_rows          int32 [batch] or NULL
+ *   query_start_loc      int32 [batch + 1] or NULL (variable-length windows,
+ *                        [kernels page] kda_recoverssm_verify's query metadata):
+ *                        request b's tokens are the rows qsl[b] .. qsl[b] + L - 1
+ *                        of q, k, v, raw_g, raw_beta, gate and out, with
+ *                        L = clamp(qsl[b+1] - qsl[b], 0, tokens). L = 0 is padding:
+ *                        nothing is read or written for the item. Records are
+ *                        rewritten for t < L; later record tokens keep their
+ *                        values. NULL: L = tokens and rows b*tokens + t
  *   gate, norm_weight    the optional gated RMSNorm output stage ([fused page],
  *                        KdaFused output stage), both NULL to write o itself:
  *                        gate BF16 [batch*tokens][heads*128], norm_weight FP32 [128]
@@ -164,8 +172,9 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
                const float* a_log, const float* dt_bias, float lower_bound, int state_dtype,
                const void* state, int64_t state_slot_stride, const int32_t* state_indices,
                int null_slot, float* corr, uint16_t* kg, int record_tokens,
-               const int32_t* record_rows, const uint16_t* gate, const float* norm_weight,
-               float norm_eps, uint16_t* out, void* stream);
+               const int32_t* record_rows, const int32_t* query_start_loc,
+               const uint16_t* gate, const float* norm_weight, float norm_eps, uint16_t* out,
+               void* stream);
 
 /*
  * kda_fused_replay_verify — deferred RecoverSSM: the previous step's commit and
@@ -185,6 +194,7 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
  *
  *   record_rows          int32 [batch], required (< 0: no record row)
  *   pending              int32 [rows], indexed by record row
+ *   query_start_loc      as kda_verify (an item with L = 0 does not replay)
  *   gate, norm_weight, norm_eps   the optional output stage, as kda_verify
  */
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
@@ -192,9 +202,9 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             const uint16_t* raw_beta, const float* a_log, const float* dt_bias,
                             float lower_bound, int state_dtype, void* state,
                             int64_t state_slot_stride, const int32_t* state_indices,
-                            int null_slot, float* corr,
-                            uint16_t* kg, int record_tokens, const int32_t* record_rows,
-                            const int32_t* pending, const uint16_t* gate,
+                            int null_slot, float* corr, uint16_t* kg, int record_tokens,
+                            const int32_t* record_rows, const int32_t* pending,
+                            const int32_t* query_start_loc, const uint16_t* gate,
                             const float* norm_weight, float norm_eps, uint16_t* out,
                             void* stream);
 
@@ -220,8 +230,8 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
  *    use, as always; the record keeps y_k's bits); v_t = y_v;
  *  - the window is rewritten as [tap 1, tap 2, x_0 .. x_{tokens-1}]; entries
  *    past tokens + 1 keep their values.
- * The rest is kda_fused_replay_verify. Null-slot items write only their zero
- * outputs.
+ * The rest is kda_fused_replay_verify with fixed windows (rows b*tokens + t; no
+ * query_start_loc). Null-slot items write only their zero outputs.
  *
  *   x                    BF16 [batch*tokens] rows of x_row_stride elements
  *                        (>= 3*heads*128): the q | k | v pre-activations in

@@ -50,9 +50,9 @@ _SIGS = {
     "kda_commit": (_i, [_i, _i, _i, _i, _i, _u64a, _i64a, _u64a, _i64a, _u64a, _i64a,
                         _p, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p]),
     "kda_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _i64, _p, _i,
-                        _p, _p, _i, _p, _p, _p, _f, _p, _p]),
+                        _p, _p, _i, _p, _p, _p, _p, _f, _p, _p]),
     "kda_fused_replay_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _i64,
-                                     _p, _i, _p, _p, _i, _p, _p, _p, _p, _f, _p, _p]),
+                                     _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _f, _p, _p]),
     "kda_fused_conv_replay_verify": (_i, [_i, _i, _i, _p, _i64, _p, _p, _p, _i64, _i64, _i64,
                                           _f, _p, _p, _p, _p, _f, _i, _p, _i64, _p, _i, _p,
                                           _p, _i, _p, _p, _p, _p, _f, _p, _p]),
@@ -194,7 +194,8 @@ def _gate_args(gate, norm_weight):
 def kda_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta, a_log,
                dt_bias, lower_bound: float, state, state_slot_stride: int, state_indices,
                corr, kg, record_tokens: int, out, record_rows=None, null_slot: int = 0,
-               gate=None, norm_weight=None, norm_eps: float = 1e-5, stream=None):
+               gate=None, norm_weight=None, norm_eps: float = 1e-5, query_start_loc=None,
+               stream=None):
     """Stock verify: writes out (o, or its gated RMSNorm with gate and
     norm_weight) and the records, never the state. The pool's element type
     (float32 or bfloat16) is that of ``state``."""
@@ -203,8 +204,9 @@ def kda_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta,
         record_rows, out)
     _check(_lib.kda_verify(heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd,
                            float(lower_bound), _state_dtype(state), ps, int(state_slot_stride),
-                           psi, int(null_slot),
-                           pc, pkg, int(record_tokens), prr, *_gate_args(gate, norm_weight),
+                           psi, int(null_slot), pc, pkg, int(record_tokens), prr,
+                           _ptr(query_start_loc, torch.int32, "query_start_loc"),
+                           *_gate_args(gate, norm_weight),
                            float(norm_eps), po, _stream(stream, state)))
     return out
 
@@ -213,7 +215,7 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
                             a_log, dt_bias, lower_bound: float, state, state_slot_stride: int,
                             state_indices, corr, kg, record_tokens: int, record_rows, pending,
                             out, null_slot: int = 0, gate=None, norm_weight=None,
-                            norm_eps: float = 1e-5, stream=None):
+                            norm_eps: float = 1e-5, query_start_loc=None, stream=None):
     """Replay each request's pending tokens into its page, then verify the
     window. The pool's element type (float32 or bfloat16) is that of ``state``."""
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
@@ -223,7 +225,8 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
         heads, tokens, batch, pq, pk, pv, pg, pb, pa, pd, float(lower_bound),
         _state_dtype(state), ps,
         int(state_slot_stride), psi, int(null_slot), pc, pkg, int(record_tokens), prr,
-        _ptr(pending, torch.int32, "pending"), *_gate_args(gate, norm_weight),
+        _ptr(pending, torch.int32, "pending"),
+        _ptr(query_start_loc, torch.int32, "query_start_loc"), *_gate_args(gate, norm_weight),
         float(norm_eps), po, _stream(stream, state)))
     return out
 

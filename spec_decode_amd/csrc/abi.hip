@@ -165,8 +165,9 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
                          void* state, int64_t state_slot_stride, const int32_t* state_indices,
                          int null_slot, float* corr, uint16_t* kg, int record_tokens,
                          const int32_t* record_rows, const int32_t* pending,
-                         const uint16_t* gate, const float* norm_weight, float norm_eps,
-                         uint16_t* out, void* stream, const ConvArgs* conv = nullptr) {
+                         const int32_t* query_start_loc, const uint16_t* gate,
+                         const float* norm_weight, float norm_eps, uint16_t* out,
+                         void* stream, const ConvArgs* conv = nullptr) {
   KDA_REQUIRE(heads >= 1 && heads <= 65535, "%s: heads must be in 1..65535 (got %d)", who,
               heads);
   KDA_REQUIRE(tokens >= 1 && tokens <= KDA_MAX_WINDOW, "%s: tokens must be in 1..8 (got %d)",
@@ -223,6 +224,7 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
   p.slots = state_indices;
   p.rows = record_rows;
   p.pending = pending;
+  p.qsl = query_start_loc;
   p.corr = corr;
   p.kg = kg;
   p.out = out;
@@ -254,12 +256,14 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
                const float* a_log, const float* dt_bias, float lower_bound, int state_dtype,
                const void* state, int64_t state_slot_stride, const int32_t* state_indices,
                int null_slot, float* corr, uint16_t* kg, int record_tokens,
-               const int32_t* record_rows, const uint16_t* gate, const float* norm_weight,
-               float norm_eps, uint16_t* out, void* stream) {
+               const int32_t* record_rows, const int32_t* query_start_loc,
+               const uint16_t* gate, const float* norm_weight, float norm_eps, uint16_t* out,
+               void* stream) {
   return verify_common("kda_verify", false, heads, tokens, batch, q, k, v, raw_g, raw_beta,
                        a_log, dt_bias, lower_bound, state_dtype, const_cast<void*>(state),
                        state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
-                       record_rows, nullptr, gate, norm_weight, norm_eps, out, stream);
+                       record_rows, nullptr, query_start_loc, gate, norm_weight, norm_eps, out,
+                       stream);
 }
 
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
@@ -267,16 +271,16 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             const uint16_t* raw_beta, const float* a_log, const float* dt_bias,
                             float lower_bound, int state_dtype, void* state,
                             int64_t state_slot_stride, const int32_t* state_indices,
-                            int null_slot, float* corr,
-                            uint16_t* kg, int record_tokens, const int32_t* record_rows,
-                            const int32_t* pending, const uint16_t* gate,
+                            int null_slot, float* corr, uint16_t* kg, int record_tokens,
+                            const int32_t* record_rows, const int32_t* pending,
+                            const int32_t* query_start_loc, const uint16_t* gate,
                             const float* norm_weight, float norm_eps, uint16_t* out,
                             void* stream) {
   return verify_common("kda_fused_replay_verify", true, heads, tokens, batch, q, k, v, raw_g,
                        raw_beta, a_log, dt_bias, lower_bound, state_dtype, state,
-                       state_slot_stride,
-                       state_indices, null_slot, corr, kg, record_tokens, record_rows, pending,
-                       gate, norm_weight, norm_eps, out, stream);
+                       state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
+                       record_rows, pending, query_start_loc, gate, norm_weight, norm_eps, out,
+                       stream);
 }
 
 int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_t* x,
@@ -297,8 +301,8 @@ int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_
   return verify_common("kda_fused_conv_replay_verify", true, heads, tokens, batch, nullptr,
                        nullptr, nullptr, raw_g, raw_beta, a_log, dt_bias, lower_bound,
                        state_dtype, state, state_slot_stride, state_indices, null_slot, corr, kg,
-                       record_tokens, record_rows, pending, gate, norm_weight, norm_eps, out,
-                       stream, &conv);
+                       record_tokens, record_rows, pending, nullptr, gate, norm_weight, norm_eps,
+                       out, stream, &conv);
 }
 
 int kda_gate_projection(int64_t tokens, int heads, const uint16_t* f_a,

@@ -149,6 +149,7 @@ struct VerifyParams {
   const int32_t* slots;
   const int32_t* rows;     // NULL (verify only): row b
   const int32_t* pending;  // fused only
+  const int32_t* qsl;      // NULL: request b's rows b*T..; else [B+1] token offsets
   float* corr;
   uint16_t* kg;
   uint16_t* out;

@@ -278,12 +278,26 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // The wave index as a scalar: branches on it are uniform (s_cbranch), so a
   // wave runs only its own half's code and waits only on its own loads.
   const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
-  const int64_t tok0 = (int64_t)b * T;
+  // The item's window: rows tok0 .. tok0 + L - 1. With query_start_loc the
+  // length is qsl[b+1] - qsl[b], clamped to 0..T; an empty window is padding
+  // and nothing is read or written. Tokens t >= L are masked below (zero key,
+  // q, v and beta), which leaves every result of the tokens t < L unchanged.
+  int64_t tok0 = (int64_t)b * T;
+  int L = T;
+  if (p.qsl != nullptr) {
+    const int q0 = __builtin_amdgcn_readfirstlane(p.qsl[b]);
+    const int q1 = __builtin_amdgcn_readfirstlane(p.qsl[b + 1]);
+    tok0 = q0;
+    L = q1 - q0;
+    L = L < 0 ? 0 : (L > T ? T : L);
+    if (L == 0) return;
+  }
+  const int last = L - 1;  // rows past the window read the last token (then masked)
 
   const int slot = p.slots[b];
   if (slot <= p.null_slot) {
     // No state: the item's outputs are zero and nothing else is written.
-    if (tid < T * (V / 8)) {
+    if (tid < L * (V / 8)) {
       const int t = tid / (V / 8);
       const int c = (tid % (V / 8)) * 8;
       *reinterpret_cast<uint4*>(p.out + ((tok0 + t) * H + h) * V + c) = make_uint4(0, 0, 0, 0);
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   if constexpr (GATED) {
     nw = p.norm_w[c];
 #pragma unroll
-    for (int t = 0; t < T; ++t) gtb[t] = p.gate[(tok0 + t) * H * V + head_row];
+    for (int t = 0; t < T; ++t) gtb[t] = p.gate[(tok0 + (t < L ? t : last)) * H * V + head_row];
   }
   __builtin_amdgcn_sched_barrier(0);
   uint32_t kb[T], gb[T], qb[T];  // lower: new raw key, gate, q bits
@@ -361,11 +375,11 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       conv_load<T>(p, cin0, slot, 0 * dim + head_row, head_row, 0, dim, tok0);
       conv_load<T>(p, cin1, slot, 1 * dim + head_row, head_row, 1, dim, tok0);
 #pragma unroll
-      for (int t = 0; t < T; ++t) gb[t] = p.g[(tok0 + t) * H * K + head_row];
+      for (int t = 0; t < T; ++t) gb[t] = p.g[(tok0 + (t < L ? t : last)) * H * K + head_row];
     } else {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const int64_t idx = (tok0 + t) * H * K + head_row;
+        const int64_t idx = (tok0 + (t < L ? t : last)) * H * K + head_row;
         kb[t] = p.k[idx];
         gb[t] = p.g[idx];
         qb[t] = p.q[idx];
@@ -388,9 +402,9 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       conv_load<T>(p, cin0, slot, 2 * dim + head_row, head_row, 2, dim, tok0);
     } else {
 #pragma unroll
-      for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + t) * H * V + head_row];
+      for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + (t < L ? t : last)) * H * V + head_row];
     }
-    rbb = p.rb[(tok0 + (c < T ? c : T - 1)) * H + h];  // unconditional: no divergent load
+    rbb = p.rb[(tok0 + (c < L ? c : last)) * H + h];  // unconditional: no divergent load
     if constexpr (FUSED) {
       const int64_t rbase = ((int64_t)(rec < 0 ? 0 : rec) * H + h) * p.rq;
 #pragma unroll
@@ -423,8 +437,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      kf[t] = bf16_bits_to_f32(kb[t]);
-      qf[t] = bf16_bits_to_f32(qb[t]);
+      kf[t] = t < L ? bf16_bits_to_f32(kb[t]) : 0.f;
+      qf[t] = t < L ? bf16_bits_to_f32(qb[t]) : 0.f;
       if constexpr (CONV) {
         const float sq = wave_sum(qf[t] * qf[t]);
         if (lane == 0) qsq_s[wave][t] = sq;
@@ -437,8 +451,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   } else {
     if constexpr (CONV) conv_part<T>(p, cin0, slot, 2 * dim + head_row, conv_off, vb);
 #pragma unroll
-    for (int t = 0; t < T; ++t) v_s[t][c] = bf16_bits_to_f32(vb[t]);
-    if (c < T) beta_s[c] = sigmoidf_fast(bf16_bits_to_f32(rbb));
+    for (int t = 0; t < T; ++t) v_s[t][c] = t < L ? bf16_bits_to_f32(vb[t]) : 0.f;
+    if (c < T) beta_s[c] = c < L ? sigmoidf_fast(bf16_bits_to_f32(rbb)) : 0.f;
     if constexpr (FUSED) {
       if (replay) {
 #pragma unroll
@@ -607,13 +621,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         const float sq = wave_sum(ob[t] * ob[t]);
         if (lane == 0) osq_s[wave][t] = sq;
       } else {
-        p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
+        if (t < L) p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
       }
     }
     if (rec >= 0) {
       const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
+        if (t >= L) break;  // uniform
         p.corr[(rbase + t) * V + vrow] = us[t];
         const uint32_t bits = kg_s[t][c];
         p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(bits & 0xffffu);
@@ -630,7 +645,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         const float rstd =
             __builtin_amdgcn_rsqf((osq_s[0][t] + osq_s[1][t]) * inv_v + p.norm_eps);
         const float sg = sigmoidf_fast(bf16_bits_to_f32(gtb[t]));
-        p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(ob[t] * rstd * nw * sg);
+        if (t < L) p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(ob[t] * rstd * nw * sg);
       }
     }
   }

@@ -118,16 +118,20 @@ def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_lay
 
 def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, win,
                     rows=None, pending=None, lb=W.LOWER_BOUND, null_slot=0, label="verify",
-                    stride=None, check=True, gate=None, norm_weight=None, norm_eps=1e-5):
+                    stride=None, check=True, gate=None, norm_weight=None, norm_eps=1e-5,
+                    qsl=None, out_rows=None):
     """All host arrays: state flat, float32 or uint16 BF16 bits (the pool's
     type), corr float32 [rows,H,RQ,V], kg uint16
     [rows,H,RQ,2K], win a dict of uint16 arrays (q, k, v, raw_g, raw_beta).
+    qsl: optional [B+1] token offsets (variable-length windows); out_rows the
+    row count of the activations and outputs (default B*T).
     Returns (gpu results, oracle results) as dicts of host arrays."""
     stride = H * V * K if stride is None else stride
+    out_rows = B * T if out_rows is None else out_rows
     announce(f"{label}: fused={fused} H={H} B={B} T={T} RQ={RQ} state={state.dtype}")
     import spec_decode_amd as kda
     d = dict(state=to_dev(state), corr=dev(corr), kg=dev_bf16(kg),
-             out=torch.full((B * T, H * V), 0, dtype=torch.bfloat16, device=DEV))
+             out=torch.full((out_rows, H * V), 0, dtype=torch.bfloat16, device=DEV))
     d["out"].view(torch.int16).fill_(0x7FFF)  # a sentinel: every element must be written
     args = dict(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]), k=dev_bf16(win["k"]),
                 v=dev_bf16(win["v"]), raw_g=dev_bf16(win["raw_g"]),
@@ -139,7 +143,8 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
                 record_rows=None if rows is None else dev(np.asarray(rows, np.int32)),
                 gate=None if gate is None else dev_bf16(gate),
                 norm_weight=None if norm_weight is None else dev(np.asarray(norm_weight, np.float32)),
-                norm_eps=norm_eps)
+                norm_eps=norm_eps,
+                query_start_loc=None if qsl is None else dev(np.asarray(qsl, np.int32)))
     if fused:
         kda.kda_fused_replay_verify(pending=dev(np.asarray(pending, np.int32)), **args)
     else:
@@ -147,13 +152,13 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
     torch.cuda.synchronize()
     gpu = {k: np_of(v) for k, v in d.items()}
     ref = dict(state=state.copy(), corr=corr.copy(), kg=kg.copy(),
-               out=np.full((B * T, H * V), 0x7FFF, np.uint16))
+               out=np.full((out_rows, H * V), 0x7FFF, np.uint16))
     oargs = dict(heads=H, tokens=T, batch=B, q=win["q"], k=win["k"], v=win["v"],
                  raw_g=win["raw_g"], raw_beta=win["raw_beta"], a_log=a_log, dt_bias=dt_bias,
                  lower_bound=lb, state=ref["state"], state_slot_stride=stride,
                  state_indices=slots, corr=ref["corr"], kg=ref["kg"], record_tokens=RQ,
                  out=ref["out"], record_rows=rows, null_slot=null_slot, gate=gate,
-                 norm_weight=norm_weight, norm_eps=norm_eps)
+                 norm_weight=norm_weight, norm_eps=norm_eps, query_start_loc=qsl)
     if fused:
         oracle.fused_replay_verify(pending=pending, **oargs)
     else:
@@ -162,20 +167,28 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
         compare_verify(gpu, ref, dict(state=state, corr=corr, kg=kg), fused=fused, H=H, B=B,
                        T=T, RQ=RQ, slots=slots, rows=rows, pending=pending, stride=stride,
                        null_slot=null_slot, label=label,
-                       out_ulps=GATED_OUT_ULPS if gate is not None else 1)
+                       out_ulps=GATED_OUT_ULPS if gate is not None else 1, qsl=qsl)
     return gpu, ref
 
 
+def window_lengths(B, T, qsl):
+    """Each request's window length: T, or clamp(qsl[b+1] - qsl[b], 0, T)."""
+    if qsl is None:
+        return [T] * B
+    return [min(max(int(qsl[b + 1]) - int(qsl[b]), 0), T) for b in range(B)]
+
+
 def verify_written(*, fused, H, B, T, RQ, slots, rows, pending, stride, null_slot, n_state,
-                   corr_shape):
+                   corr_shape, qsl=None):
     smask = np.zeros(n_state, dtype=bool)
     cmask = np.zeros(corr_shape, dtype=bool)
+    lens = window_lengths(B, T, qsl)
     for b in range(B):
-        if slots[b] <= null_slot:
+        if slots[b] <= null_slot or lens[b] == 0:
             continue
         r = b if rows is None else int(rows[b])
         if r >= 0:
-            cmask[r, :, :T, :] = True
+            cmask[r, :, :lens[b], :] = True
             if fused:
                 n = min(max(int(pending[r]), 0), RQ)
                 if n > 0:
@@ -186,10 +199,11 @@ def verify_written(*, fused, H, B, T, RQ, slots, rows, pending, stride, null_slo
 
 
 def compare_verify(gpu, ref, orig, *, fused, H, B, T, RQ, slots, rows, pending, stride,
-                   null_slot, label, out_ulps=1):
+                   null_slot, label, out_ulps=1, qsl=None):
     smask, cmask = verify_written(fused=fused, H=H, B=B, T=T, RQ=RQ, slots=slots, rows=rows,
                                   pending=pending, stride=stride, null_slot=null_slot,
-                                  n_state=orig["state"].size, corr_shape=orig["corr"].shape)
+                                  n_state=orig["state"].size, corr_shape=orig["corr"].shape,
+                                  qsl=qsl)
     assert_bf16_close(f"{label} out", gpu["out"], ref["out"], out_ulps)
     assert_exact(f"{label} key/gate records", gpu["kg"], ref["kg"])
     assert_f32_close(f"{label} corrections (written)", gpu["corr"][cmask], ref["corr"][cmask])

@@ -60,6 +60,7 @@ def _verify_args(tokens, *, state=None, dtype=0, stride=4 * 128 * 128, rq=8, row
         ctypes.c_int64(stride), fake, ctypes.c_int(0), fake, fake, ctypes.c_int(rq), P(rows)]
     if fused:
         args.append(P(pending))
+    args.append(P(None))  # query_start_loc
     return args + [P(gate), P(norm_weight), ctypes.c_float(1e-5), fake, P(None)]
 
 

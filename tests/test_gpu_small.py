@@ -369,3 +369,31 @@ def test_gate_projection_general_inputs():
     want = oracle.gate_projection(W.bits(fa), W.bits(fb))
     assert not bf16_mismatch(got, want, ulps=1).any()
     assert (got == want).mean() > 0.999
+
+
+# ---------------------------------------------------------------- variable-length windows
+
+@pytest.mark.parametrize("T,fused,bf16,gated", [(3, False, False, False), (8, False, True, False),
+                                                (4, True, False, False), (8, True, False, False),
+                                                (5, True, True, True), (2, True, False, True)])
+def test_variable_length_windows(T, fused, bf16, gated):
+    """Request lengths 0..T (one above T, clamped) through query_start_loc, with
+    a null slot, a request without a record row and rows nobody owns."""
+    H, B, RQ = 3, 7, 8
+    c = _vf_case(1100 + T, H, B, T, RQ, 10, null_rows=(5,), norec_rows=(4,), bf16=bf16)
+    lens = [T, 0, 1, T + 2, T - 1, 2, 0]
+    qsl = np.zeros(B + 1, np.int32)
+    qsl[1:] = np.cumsum(lens)
+    rows_total = int(qsl[-1]) + 2
+    win = {n: np.ascontiguousarray(a[:rows_total]) for n, a in c["win"].items()}
+    assert all(a.shape[0] == rows_total for a in win.values())
+    pending = np.random.default_rng(T).integers(0, RQ + 1, B).astype(np.int32)
+    kw = {}
+    if gated:
+        gate, weight, eps = W.draw_output_stage(W._gen(1200 + T), B, T, H)
+        kw = dict(gate=np.ascontiguousarray(W.bits(gate)[:rows_total]),
+                  norm_weight=weight.numpy(), norm_eps=eps)
+    run_verify_case(fused=fused, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
+                    corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                    win=win, rows=c["rows"], pending=pending if fused else None, qsl=qsl,
+                    out_rows=rows_total, label=f"varlen T={T} fused={fused}", **kw)

@@ -63,7 +63,7 @@ def _load():
                              d, _vp, ctypes.c_int64, _i32p, i, _fp, _u16p, i, _i32p,
                              _i32p, i, _u16p, _i64p, l, i, _u16p, _fp, d, i, _u16p,
                              ctypes.c_int64, _u16p, _u16p, _u16p, ctypes.c_int64,
-                             ctypes.c_int64, ctypes.c_int64, d, _i32p]),
+                             ctypes.c_int64, ctypes.c_int64, d, _i32p, _i32p, _i32p]),
         "kda_o_exp_f32": (ctypes.c_float, [ctypes.c_float]),
         "kda_o_silu_bf16": (ctypes.c_uint16, [ctypes.c_float]),
         "kda_o_conv_silu": (None, [i, _fp, _fp, ctypes.c_float, _u16p]),
@@ -258,9 +258,14 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
                 dt_bias, lower_bound, state, state_slot_stride, state_indices,
                 corr, kg, record_tokens, record_rows, pending, out, null_slot,
                 key_dim, value_dim, items, threads, gate=None, norm_weight=None,
-                norm_eps=1e-5, conv=None, query_start_loc=None):
+                norm_eps=1e-5, conv=None, query_start_loc=None, boundaries=None,
+                boundary_lens=None):
     state_bf16 = isinstance(state, np.ndarray) and state.dtype == np.uint16
     qsl = None if query_start_loc is None else _c(query_start_loc, np.int32)
+    if (boundaries is None) != (boundary_lens is None):
+        raise ValueError("boundaries and boundary_lens go together")
+    bnd = None if boundaries is None else _c(boundaries, np.int32)
+    blen = None if boundary_lens is None else _c(boundary_lens, np.int32)
     _check_inplace(state, np.uint16 if state_bf16 else np.float32, "state")
     _check_inplace(corr, np.float32, "corr")
     _check_inplace(kg, np.uint16, "kg")
@@ -299,7 +304,7 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
         _ptr(out, _u16p), ip, ni, default_threads() if threads is None else int(threads),
         _ptr(gt, _u16p), _ptr(nw, _fp), float(norm_eps), int(state_bf16),
         _ptr(cx, _u16p), cxs, _ptr(cw, _u16p), _ptr(cb, _u16p), _ptr(cs, _u16p), css, ccs,
-        cts, qsc, _ptr(qsl, _i32p))
+        cts, qsc, _ptr(qsl, _i32p), _ptr(bnd, _i32p), _ptr(blen, _i32p))
 
 
 def verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log, dt_bias,
@@ -324,9 +329,11 @@ def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log
                         dt_bias, lower_bound, state, state_slot_stride, state_indices,
                         corr, kg, record_tokens, record_rows, pending, out, null_slot=0,
                         key_dim=128, value_dim=128, items=None, threads=None, gate=None,
-                        norm_weight=None, norm_eps=1e-5, query_start_loc=None):
-    """Replay the pending tokens from the old records (writing S_n when n > 0),
-    then the stock verify from S_n, rewriting the records."""
+                        norm_weight=None, norm_eps=1e-5, query_start_loc=None,
+                        boundaries=None, boundary_lens=None):
+    """Replay the pending tokens from the old records (writing S_n when n > 0,
+    and S_min(m, n) to the boundary slot with boundaries), then the stock verify
+    from S_n, rewriting the records."""
     if record_rows is None or pending is None:
         raise ValueError("fused replay+verify needs record_rows and pending")
     _verify_buf(True, heads=heads, tokens=tokens, batch=batch, q=q, k=k, v=v,
@@ -336,7 +343,8 @@ def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log
                 record_rows=record_rows, pending=pending, out=out, null_slot=null_slot,
                 key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
                 gate=gate, norm_weight=norm_weight, norm_eps=norm_eps,
-                query_start_loc=query_start_loc)
+                query_start_loc=query_start_loc, boundaries=boundaries,
+                boundary_lens=boundary_lens)
 
 
 def fused_conv_replay_verify(*, heads, tokens, batch, x, x_row_stride, conv_weight,
@@ -345,7 +353,8 @@ def fused_conv_replay_verify(*, heads, tokens, batch, x, x_row_stride, conv_weig
                              lower_bound, state, state_slot_stride, state_indices, corr, kg,
                              record_tokens, record_rows, pending, out, conv_bias=None,
                              null_slot=0, key_dim=128, value_dim=128, items=None,
-                             threads=None, gate=None, norm_weight=None, norm_eps=1e-5):
+                             threads=None, gate=None, norm_weight=None, norm_eps=1e-5,
+                             boundaries=None, boundary_lens=None):
     """The fused step with the convolution prologue: q, k, v are the SiLU of a
     4-tap causal convolution of x (rows of ``x_row_stride``: q | k | v parts of
     H*K channels each) over each channel's window in ``conv_state`` (uint16 BF16,
@@ -365,7 +374,8 @@ def fused_conv_replay_verify(*, heads, tokens, batch, x, x_row_stride, conv_weig
                 state_indices=state_indices, corr=corr, kg=kg, record_tokens=record_tokens,
                 record_rows=record_rows, pending=pending, out=out, null_slot=null_slot,
                 key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
-                gate=gate, norm_weight=norm_weight, norm_eps=norm_eps, conv=conv)
+                gate=gate, norm_weight=norm_weight, norm_eps=norm_eps, conv=conv,
+                boundaries=boundaries, boundary_lens=boundary_lens)
 
 
 def exp_f32(x):

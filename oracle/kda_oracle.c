@@ -508,6 +508,8 @@ int kda_o_commit(int L, int H, int Q, int B, int K, int V, int state_bf16,
  *  - record row rec = record_rows[b] (or b when record_rows is NULL).
  *  - fused only: n = clamp(pending[rec], 0, RQ) when rec >= 0, else 0; the n
  *    recorded tokens are replayed onto S_0 and S_n is written back when n > 0.
+ *    With boundaries (align, as the commit's): when n > 0, bnd = bounds[b] >
+ *    null and m = blens[b] > 0, S_{min(m, n)} is also stored to slot bnd.
  *  - the stock recurrence runs over the L new tokens from S_n (verify: S_0);
  *    o -> BF16 out[tok0 + t][h*V + v].
  *  - rec >= 0: the records of tokens t < L are rewritten (u_t FP32, raw key and
@@ -533,6 +535,8 @@ struct verify_ctx {
   const float* norm_w;
   double norm_eps;
   const int32_t* qsl;     /* optional [B+1] token offsets (variable-length windows) */
+  const int32_t* bounds;  /* fused, optional: boundary slots [B] (align) */
+  const int32_t* blens;   /*   and boundary lengths m [B] */
   /* optional convolution prologue (x != NULL): q, k, v are its outputs */
   const uint16_t* x;      /* [B*T] rows of x_stride: q | k | v pre-activations */
   int64_t x_stride;
@@ -659,6 +663,13 @@ static void verify_item(void* p, long it) {
       }
       kda_o_knorm(K, kr, kn + t * K);
     }
+    if (c->bounds && c->blens && c->bounds[b] > c->null_slot && c->blens[b] > 0) {
+      const int me = c->blens[b] < n ? c->blens[b] : n;
+      kda_o_commit_seq(K, V, me, S0, u, kn, d, S);
+      const int64_t bpage = (int64_t)c->bounds[b] * c->slot_stride + (int64_t)h * (int64_t)VK;
+      for (size_t i = 0; i < VK; ++i)
+        state_put(c->state, c->state_bf16, bpage + (int64_t)i, S[i]);
+    }
     kda_o_commit_seq(K, V, n, S0, u, kn, d, S);
     for (size_t i = 0; i < VK; ++i) state_put(c->state, c->state_bf16, page + (int64_t)i, S[i]);
   } else {
@@ -739,13 +750,15 @@ int kda_o_verify(int H, int T, int B, int K, int V, const uint16_t* q, const uin
                  double norm_eps, int state_bf16, const uint16_t* x, int64_t x_stride,
                  const uint16_t* conv_w, const uint16_t* conv_b, uint16_t* conv,
                  int64_t conv_ss, int64_t conv_cs, int64_t conv_ts, double q_scale,
-                 const int32_t* query_start_loc) {
+                 const int32_t* query_start_loc, const int32_t* boundaries,
+                 const int32_t* boundary_lens) {
   struct verify_ctx c = {H,          T,          B,       K,          V,
                          RQ,         fused,      state_bf16, q,       k,          v,
                          raw_g,      raw_beta,   a_log,   dt_bias,    lower_bound,
                          state,      state_slot_stride, state_indices, null_slot, corr,
                          kg,         record_rows, pending, out,       items,
-                         gate,       norm_w,     norm_eps, query_start_loc, x, x_stride,
+                         gate,       norm_w,     norm_eps, query_start_loc, boundaries,
+                         boundary_lens, x, x_stride,
                          conv_w,     conv_b,     conv,    conv_ss,    conv_cs,
                          conv_ts,    q_scale};
   long count = items ? n_items : (long)B * H;

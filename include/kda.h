@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 #define KDA_OK 0
 #define KDA_EINVAL 1
@@ -195,6 +195,13 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
  *   record_rows          int32 [batch], required (< 0: no record row)
  *   pending              int32 [rows], indexed by record row
  *   query_start_loc      as kda_verify (an item with L = 0 does not replay)
+ *   boundaries,          int32 [batch] each, both or neither (align, as kda_commit's):
+ *   boundary_lens        for an item whose replay runs (n > 0), with bnd =
+ *                        boundaries[b] > null_slot and m = boundary_lens[b] > 0,
+ *                        S_min(m, n) is also stored to slot bnd (same page
+ *                        layout and dtype); the fold then runs in two stages,
+ *                        tokens [0, min(m, n)) and the rest. Boundary slots must
+ *                        not be any request's slot or another's boundary.
  *   gate, norm_weight, norm_eps   the optional output stage, as kda_verify
  */
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
@@ -204,7 +211,8 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             int64_t state_slot_stride, const int32_t* state_indices,
                             int null_slot, float* corr, uint16_t* kg, int record_tokens,
                             const int32_t* record_rows, const int32_t* pending,
-                            const int32_t* query_start_loc, const uint16_t* gate,
+                            const int32_t* query_start_loc, const int32_t* boundaries,
+                            const int32_t* boundary_lens, const uint16_t* gate,
                             const float* norm_weight, float norm_eps, uint16_t* out,
                             void* stream);
 
@@ -247,8 +255,8 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
  *   q_scale              finite (the pages use 128^-1/2)
  *   raw_g, raw_beta, a_log, dt_bias, lower_bound, state_dtype, state,
  *   state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
- *   record_rows, pending, gate, norm_weight, norm_eps, out
- *                        as kda_fused_replay_verify
+ *   record_rows, pending, boundaries, boundary_lens, gate, norm_weight, norm_eps,
+ *   out                  as kda_fused_replay_verify
  */
 int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_t* x,
                                  int64_t x_row_stride, const uint16_t* conv_weight,
@@ -260,7 +268,8 @@ int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_
                                  void* state, int64_t state_slot_stride,
                                  const int32_t* state_indices, int null_slot, float* corr,
                                  uint16_t* kg, int record_tokens, const int32_t* record_rows,
-                                 const int32_t* pending, const uint16_t* gate,
+                                 const int32_t* pending, const int32_t* boundaries,
+                                 const int32_t* boundary_lens, const uint16_t* gate,
                                  const float* norm_weight, float norm_eps, uint16_t* out,
                                  void* stream);
 

@@ -52,10 +52,11 @@ _SIGS = {
     "kda_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _i64, _p, _i,
                         _p, _p, _i, _p, _p, _p, _p, _f, _p, _p]),
     "kda_fused_replay_verify": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _f, _i, _p, _i64,
-                                     _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _f, _p, _p]),
+                                     _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _p, _p, _f, _p,
+                                     _p]),
     "kda_fused_conv_replay_verify": (_i, [_i, _i, _i, _p, _i64, _p, _p, _p, _i64, _i64, _i64,
                                           _f, _p, _p, _p, _p, _f, _i, _p, _i64, _p, _i, _p,
-                                          _p, _i, _p, _p, _p, _p, _f, _p, _p]),
+                                          _p, _i, _p, _p, _p, _p, _p, _p, _f, _p, _p]),
     "kda_gate_projection": (_i, [_i64, _i, _p, _i64, _p, _p, _p]),
     "kda_defer_commit": (_i, [_i, _p, _p, _p, _p, _p, _i, _p]),
     "kda_flush_plan": (_i, [_i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
@@ -215,7 +216,8 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
                             a_log, dt_bias, lower_bound: float, state, state_slot_stride: int,
                             state_indices, corr, kg, record_tokens: int, record_rows, pending,
                             out, null_slot: int = 0, gate=None, norm_weight=None,
-                            norm_eps: float = 1e-5, query_start_loc=None, stream=None):
+                            norm_eps: float = 1e-5, query_start_loc=None, boundaries=None,
+                            boundary_lens=None, stream=None):
     """Replay each request's pending tokens into its page, then verify the
     window. The pool's element type (float32 or bfloat16) is that of ``state``."""
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
@@ -226,7 +228,9 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
         _state_dtype(state), ps,
         int(state_slot_stride), psi, int(null_slot), pc, pkg, int(record_tokens), prr,
         _ptr(pending, torch.int32, "pending"),
-        _ptr(query_start_loc, torch.int32, "query_start_loc"), *_gate_args(gate, norm_weight),
+        _ptr(query_start_loc, torch.int32, "query_start_loc"),
+        _ptr(boundaries, torch.int32, "boundaries"),
+        _ptr(boundary_lens, torch.int32, "boundary_lens"), *_gate_args(gate, norm_weight),
         float(norm_eps), po, _stream(stream, state)))
     return out
 
@@ -238,7 +242,8 @@ def kda_fused_conv_replay_verify(*, heads: int, tokens: int, batch: int, x, x_ro
                                  lower_bound: float, state, state_slot_stride: int,
                                  state_indices, corr, kg, record_tokens: int, record_rows,
                                  pending, out, conv_bias=None, null_slot: int = 0, gate=None,
-                                 norm_weight=None, norm_eps: float = 1e-5, stream=None):
+                                 norm_weight=None, norm_eps: float = 1e-5, boundaries=None,
+                                 boundary_lens=None, stream=None):
     """The fused step with its convolution prologue: q, k, v from the packed
     pre-activations ``x`` (rows of ``x_row_stride`` elements) and each channel's
     window in ``conv_state`` (BF16, rewritten in place). Strides in elements."""
@@ -252,8 +257,9 @@ def kda_fused_conv_replay_verify(*, heads: int, tokens: int, batch: int, x, x_ro
         _state_dtype(state), _ptr(state, None, "state"), int(state_slot_stride),
         _ptr(state_indices, i32, "state_indices"), int(null_slot), _ptr(corr, f32, "corr"),
         _ptr(kg, bf, "kg"), int(record_tokens), _ptr(record_rows, i32, "record_rows"),
-        _ptr(pending, i32, "pending"), *_gate_args(gate, norm_weight), float(norm_eps),
-        _ptr(out, bf, "out"), _stream(stream, state)))
+        _ptr(pending, i32, "pending"), _ptr(boundaries, i32, "boundaries"),
+        _ptr(boundary_lens, i32, "boundary_lens"), *_gate_args(gate, norm_weight),
+        float(norm_eps), _ptr(out, bf, "out"), _stream(stream, state)))
     return out
 
 

@@ -165,7 +165,8 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
                          void* state, int64_t state_slot_stride, const int32_t* state_indices,
                          int null_slot, float* corr, uint16_t* kg, int record_tokens,
                          const int32_t* record_rows, const int32_t* pending,
-                         const int32_t* query_start_loc, const uint16_t* gate,
+                         const int32_t* query_start_loc, const int32_t* boundaries,
+                         const int32_t* boundary_lens, const uint16_t* gate,
                          const float* norm_weight, float norm_eps, uint16_t* out,
                          void* stream, const ConvArgs* conv = nullptr) {
   KDA_REQUIRE(heads >= 1 && heads <= 65535, "%s: heads must be in 1..65535 (got %d)", who,
@@ -182,6 +183,8 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
               "%s: state_dtype must be KDA_STATE_F32 or KDA_STATE_BF16", who);
   KDA_REQUIRE((gate == nullptr) == (norm_weight == nullptr),
               "%s: gate and norm_weight must be given together", who);
+  KDA_REQUIRE((boundaries == nullptr) == (boundary_lens == nullptr),
+              "%s: boundaries and boundary_lens must be given together", who);
   KDA_REQUIRE(gate == nullptr || (std::isfinite(norm_eps) && norm_eps >= 0.f),
               "%s: norm_eps must be finite and >= 0", who);
   if (conv != nullptr) {
@@ -225,6 +228,8 @@ static int verify_common(const char* who, bool fused, int heads, int tokens, int
   p.rows = record_rows;
   p.pending = pending;
   p.qsl = query_start_loc;
+  p.bounds = boundaries;
+  p.blens = boundary_lens;
   p.corr = corr;
   p.kg = kg;
   p.out = out;
@@ -262,8 +267,8 @@ int kda_verify(int heads, int tokens, int batch, const uint16_t* q, const uint16
   return verify_common("kda_verify", false, heads, tokens, batch, q, k, v, raw_g, raw_beta,
                        a_log, dt_bias, lower_bound, state_dtype, const_cast<void*>(state),
                        state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
-                       record_rows, nullptr, query_start_loc, gate, norm_weight, norm_eps, out,
-                       stream);
+                       record_rows, nullptr, query_start_loc, nullptr, nullptr, gate,
+                       norm_weight, norm_eps, out, stream);
 }
 
 int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
@@ -273,14 +278,15 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
                             int64_t state_slot_stride, const int32_t* state_indices,
                             int null_slot, float* corr, uint16_t* kg, int record_tokens,
                             const int32_t* record_rows, const int32_t* pending,
-                            const int32_t* query_start_loc, const uint16_t* gate,
+                            const int32_t* query_start_loc, const int32_t* boundaries,
+                            const int32_t* boundary_lens, const uint16_t* gate,
                             const float* norm_weight, float norm_eps, uint16_t* out,
                             void* stream) {
   return verify_common("kda_fused_replay_verify", true, heads, tokens, batch, q, k, v, raw_g,
                        raw_beta, a_log, dt_bias, lower_bound, state_dtype, state,
                        state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,
-                       record_rows, pending, query_start_loc, gate, norm_weight, norm_eps, out,
-                       stream);
+                       record_rows, pending, query_start_loc, boundaries, boundary_lens, gate,
+                       norm_weight, norm_eps, out, stream);
 }
 
 int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_t* x,
@@ -293,7 +299,8 @@ int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_
                                  void* state, int64_t state_slot_stride,
                                  const int32_t* state_indices, int null_slot, float* corr,
                                  uint16_t* kg, int record_tokens, const int32_t* record_rows,
-                                 const int32_t* pending, const uint16_t* gate,
+                                 const int32_t* pending, const int32_t* boundaries,
+                                 const int32_t* boundary_lens, const uint16_t* gate,
                                  const float* norm_weight, float norm_eps, uint16_t* out,
                                  void* stream) {
   const ConvArgs conv{x,          x_row_stride,     conv_weight,         conv_bias, conv_state,
@@ -301,8 +308,8 @@ int kda_fused_conv_replay_verify(int heads, int tokens, int batch, const uint16_
   return verify_common("kda_fused_conv_replay_verify", true, heads, tokens, batch, nullptr,
                        nullptr, nullptr, raw_g, raw_beta, a_log, dt_bias, lower_bound,
                        state_dtype, state, state_slot_stride, state_indices, null_slot, corr, kg,
-                       record_tokens, record_rows, pending, nullptr, gate, norm_weight, norm_eps,
-                       out, stream, &conv);
+                       record_tokens, record_rows, pending, nullptr, boundaries, boundary_lens,
+                       gate, norm_weight, norm_eps, out, stream, &conv);
 }
 
 int kda_gate_projection(int64_t tokens, int heads, const uint16_t* f_a,

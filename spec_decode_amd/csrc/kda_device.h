@@ -150,6 +150,8 @@ struct VerifyParams {
   const int32_t* rows;     // NULL (verify only): row b
   const int32_t* pending;  // fused only
   const int32_t* qsl;      // NULL: request b's rows b*T..; else [B+1] token offsets
+  const int32_t* bounds;   // fused, optional (align): boundary slots [B]
+  const int32_t* blens;    //   boundary lengths m [B]
   float* corr;
   uint16_t* kg;
   uint16_t* out;

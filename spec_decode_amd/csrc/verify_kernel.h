@@ -313,11 +313,28 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
   }
   const bool replay = FUSED && n > 0;
+  // Boundary store (align, fused only): S_me, me = min(m, n), also goes to the
+  // boundary slot when the replay runs, the slot is live and m > 0. The fold
+  // then runs in two stages, tokens [0, me) and [me, n).
+  int me = 0, bslot = 0;
+  if constexpr (FUSED) {
+    if (replay && p.bounds != nullptr) {
+      const int bs = __builtin_amdgcn_readfirstlane(p.bounds[b]);
+      const int m = __builtin_amdgcn_readfirstlane(p.blens[b]);
+      if (bs > p.null_slot && m > 0) {
+        me = m < n ? m : n;
+        bslot = bs;
+      }
+    }
+  }
+  const bool balign = me > 0;
 
   __shared__ __attribute__((aligned(16))) float x_s[16][K];    // Gamma_t kn_t | Gamma_t q_t | 0
   __shared__ __attribute__((aligned(16))) float kp_s[MAX_T][K];  // replay kn_t P_t (0 past n)
   __shared__ __attribute__((aligned(16))) float u_s[MAX_T][V];   // replay u_t (0 past n)
   __shared__ __attribute__((aligned(16))) float dn_s[K];
+  __shared__ __attribute__((aligned(16))) float kpm_s[MAX_T][K];  // align: stage one kn_t P_t
+  __shared__ __attribute__((aligned(16))) float dm_s[K];          // align: D_me
   __shared__ __attribute__((aligned(16))) float v_s[T][V];
   __shared__ __attribute__((aligned(16))) float dots_s[V][16];   // w_t | y_t per state row
   __shared__ float pair_s[PI::P2];
@@ -497,19 +514,37 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   } else {
     if constexpr (FUSED) {
       if (replay) {
+        // Suffix products over the fold's stages: stage two (tokens me..n-1,
+        // all n without align) into kp_s / dn_s, stage one (tokens 0..me-1)
+        // into kpm_s / dm_s.
+        float knr[MAX_T];
+#pragma unroll
+        for (int t = 0; t < MAX_T; ++t)
+          knr[t] = okf[t] * __builtin_amdgcn_rsqf(ssq_s[1][0][t] + ssq_s[1][1][t] + 1e-6f);
         float pp = 1.f;
 #pragma unroll
         for (int t = MAX_T - 1; t >= 0; --t) {
           float w = 0.f;
-          if (t < n) {
-            const float kn =
-                okf[t] * __builtin_amdgcn_rsqf(ssq_s[1][0][t] + ssq_s[1][1][t] + 1e-6f);
-            w = kn * pp;
+          if (t < n && t >= me) {
+            w = knr[t] * pp;
             pp *= od[t];
           }
           kp_s[t][c] = w;
         }
         dn_s[c] = pp;
+        if (balign) {
+          float pm = 1.f;
+#pragma unroll
+          for (int t = MAX_T - 1; t >= 0; --t) {
+            float w = 0.f;
+            if (t < me) {
+              w = knr[t] * pm;
+              pm *= od[t];
+            }
+            kpm_s[t][c] = w;
+          }
+          dm_s[c] = pm;
+        }
       }
     }
   }
@@ -543,6 +578,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
   floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   u32x4 sn[2];  // BF16 pages: S_n of the even tile, stored with the odd one
+  u32x4 sb[2];  // BF16 pages, align: S_me likewise
+  char* const btile0 = static_cast<char*>(p.state) +
+                       ((int64_t)bslot * p.slot_stride + (int64_t)h * PAGE +
+                        (16 * (2 * wave) + lr) * K + LDC * lq) * ES;
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
     const int c0 = chan0<SB16>(cb, lq);
@@ -568,10 +607,27 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         s = __builtin_bit_cast(floatx4, st[r][cb]);
       }
       if (replay) {
+        const int64_t toff = (16 * r * K + 4 * LDC * (SB16 ? cb >> 1 : cb)) * ES;
+        if (balign) {
+          // Stage one: S_me, stored to the boundary page.
+          const int ca = chan0<SB16>(cb, lr >> 2) + (lr & 3);
+          const floatx4 dm4 = *reinterpret_cast<const floatx4*>(&dm_s[c0]);
+          s = s * dm4;
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kpm_s[lq][ca], ub[r][0], s, 0, 0, 0);
+          if (me > 4)
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(kpm_s[4 + lq][ca], ub[r][1], s, 0, 0, 0);
+          if constexpr (SB16) {
+            sb[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
+            sb[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);
+            if (cb & 1) *reinterpret_cast<u32x4*>(btile0 + toff) = sb[r];
+          } else {
+            *reinterpret_cast<floatx4*>(btile0 + toff) = s;
+          }
+        }
         s = s * dn4;
         s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka0, ub[r][0], s, 0, 0, 0);
         if (n > 4) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka1, ub[r][1], s, 0, 0, 0);
-        char* const dst = tile0 + (16 * r * K + 4 * LDC * (SB16 ? cb >> 1 : cb)) * ES;
+        char* const dst = tile0 + toff;
         if constexpr (SB16) {
           sn[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
           sn[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);

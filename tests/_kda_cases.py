@@ -119,7 +119,7 @@ def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_lay
 def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, win,
                     rows=None, pending=None, lb=W.LOWER_BOUND, null_slot=0, label="verify",
                     stride=None, check=True, gate=None, norm_weight=None, norm_eps=1e-5,
-                    qsl=None, out_rows=None):
+                    qsl=None, out_rows=None, bounds=None, blens=None):
     """All host arrays: state flat, float32 or uint16 BF16 bits (the pool's
     type), corr float32 [rows,H,RQ,V], kg uint16
     [rows,H,RQ,2K], win a dict of uint16 arrays (q, k, v, raw_g, raw_beta).
@@ -146,7 +146,9 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
                 norm_eps=norm_eps,
                 query_start_loc=None if qsl is None else dev(np.asarray(qsl, np.int32)))
     if fused:
-        kda.kda_fused_replay_verify(pending=dev(np.asarray(pending, np.int32)), **args)
+        i32 = lambda a: None if a is None else dev(np.asarray(a, np.int32))
+        kda.kda_fused_replay_verify(pending=dev(np.asarray(pending, np.int32)),
+                                    boundaries=i32(bounds), boundary_lens=i32(blens), **args)
     else:
         kda.kda_verify(**args)
     torch.cuda.synchronize()
@@ -160,14 +162,16 @@ def run_verify_case(*, fused, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bia
                  out=ref["out"], record_rows=rows, null_slot=null_slot, gate=gate,
                  norm_weight=norm_weight, norm_eps=norm_eps, query_start_loc=qsl)
     if fused:
-        oracle.fused_replay_verify(pending=pending, **oargs)
+        oracle.fused_replay_verify(pending=pending, boundaries=bounds, boundary_lens=blens,
+                                   **oargs)
     else:
         oracle.verify(**oargs)
     if check:
         compare_verify(gpu, ref, dict(state=state, corr=corr, kg=kg), fused=fused, H=H, B=B,
                        T=T, RQ=RQ, slots=slots, rows=rows, pending=pending, stride=stride,
                        null_slot=null_slot, label=label,
-                       out_ulps=GATED_OUT_ULPS if gate is not None else 1, qsl=qsl)
+                       out_ulps=GATED_OUT_ULPS if gate is not None else 1, qsl=qsl,
+                       bounds=bounds, blens=blens)
     return gpu, ref
 
 
@@ -179,7 +183,7 @@ def window_lengths(B, T, qsl):
 
 
 def verify_written(*, fused, H, B, T, RQ, slots, rows, pending, stride, null_slot, n_state,
-                   corr_shape, qsl=None):
+                   corr_shape, qsl=None, bounds=None, blens=None):
     smask = np.zeros(n_state, dtype=bool)
     cmask = np.zeros(corr_shape, dtype=bool)
     lens = window_lengths(B, T, qsl)
@@ -192,18 +196,22 @@ def verify_written(*, fused, H, B, T, RQ, slots, rows, pending, stride, null_slo
             if fused:
                 n = min(max(int(pending[r]), 0), RQ)
                 if n > 0:
-                    for h in range(H):
-                        o = int(slots[b]) * stride + h * V * K
-                        smask[o:o + V * K] = True
+                    pages = [int(slots[b])]
+                    if bounds is not None and bounds[b] > null_slot and blens[b] > 0:
+                        pages.append(int(bounds[b]))
+                    for sl in pages:
+                        for h in range(H):
+                            o = sl * stride + h * V * K
+                            smask[o:o + V * K] = True
     return smask, cmask
 
 
 def compare_verify(gpu, ref, orig, *, fused, H, B, T, RQ, slots, rows, pending, stride,
-                   null_slot, label, out_ulps=1, qsl=None):
+                   null_slot, label, out_ulps=1, qsl=None, bounds=None, blens=None):
     smask, cmask = verify_written(fused=fused, H=H, B=B, T=T, RQ=RQ, slots=slots, rows=rows,
                                   pending=pending, stride=stride, null_slot=null_slot,
                                   n_state=orig["state"].size, corr_shape=orig["corr"].shape,
-                                  qsl=qsl)
+                                  qsl=qsl, bounds=bounds, blens=blens)
     assert_bf16_close(f"{label} out", gpu["out"], ref["out"], out_ulps)
     assert_exact(f"{label} key/gate records", gpu["kg"], ref["kg"])
     assert_f32_close(f"{label} corrections (written)", gpu["corr"][cmask], ref["corr"][cmask])

@@ -61,6 +61,8 @@ def _verify_args(tokens, *, state=None, dtype=0, stride=4 * 128 * 128, rq=8, row
     if fused:
         args.append(P(pending))
     args.append(P(None))  # query_start_loc
+    if fused:
+        args += [P(None), P(None)]  # boundaries, boundary_lens
     return args + [P(gate), P(norm_weight), ctypes.c_float(1e-5), fake, P(None)]
 
 
@@ -115,8 +117,8 @@ def test_conv_entry_rejects_bad_arguments(lib):
                  fake, P(None), fake, I64(strides[0]), I64(strides[1]), I64(strides[2]),
                  ctypes.c_float(q_scale), fake, fake, fake, fake, ctypes.c_float(-5.0),
                  ctypes.c_int(0), fake, I64(4 * 128 * 128), fake, ctypes.c_int(0), fake, fake,
-                 ctypes.c_int(4), fake, fake, P(None), P(None), ctypes.c_float(1e-5), fake,
-                 P(None))
+                 ctypes.c_int(4), fake, fake, P(None), P(None), P(None), P(None),
+                 ctypes.c_float(1e-5), fake, P(None))
 
     assert call(x_stride=3 * 4 * 128 - 1) == 1 and "x_row_stride" in _err(lib)
     assert call(q_scale=float("inf")) == 1 and "q_scale" in _err(lib)

@@ -397,3 +397,28 @@ def test_variable_length_windows(T, fused, bf16, gated):
                     corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
                     win=win, rows=c["rows"], pending=pending if fused else None, qsl=qsl,
                     out_rows=rows_total, label=f"varlen T={T} fused={fused}", **kw)
+
+
+# ---------------------------------------------------------------- align inside the fused replay
+
+@pytest.mark.parametrize("T,bf16", [(2, False), (4, False), (8, False), (3, True), (8, True)])
+def test_fused_boundary_stores(T, bf16):
+    """Boundary slots with m = 1, n - 1, n, above n, 0, and a null boundary;
+    pending counts across both MFMA stages (m and n on each side of 4)."""
+    H, B, RQ, S = 3, 8, 8, 20
+    c = _vf_case(1300 + T, H, B, T, RQ, S, null_rows=(7,), norec_rows=(6,), bf16=bf16)
+    slots, rows = c["slots"], c["rows"]
+    n_req = [8, 6, 5, 3, 7, 4, 2, 5]
+    m_req = [5, 5, 5, 9, 0, 1, 2, 3]
+    pending = np.zeros(B, np.int32)
+    for b in range(B):
+        if rows[b] >= 0:
+            pending[rows[b]] = n_req[b]
+    free = [sl for sl in range(1, S) if sl not in set(slots.tolist())]
+    bounds = np.array(free[:B], np.int32)
+    bounds[2] = 0  # a null boundary
+    blens = np.array(m_req, np.int32)
+    run_verify_case(fused=True, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=slots,
+                    corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                    win=c["win"], rows=rows, pending=pending, bounds=bounds, blens=blens,
+                    label=f"fused align T={T} bf16={bf16}")

@@ -57,6 +57,7 @@
 // that the in-order return of loads lets the prologue start early.
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "kda_device.h"
@@ -329,14 +330,20 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
   const bool balign = me > 0;
 
-  __shared__ __attribute__((aligned(16))) float x_s[16][K];    // Gamma_t kn_t | Gamma_t q_t | 0
+  // BF16 pages without the convolution: LDS bounds the occupancy, so x_s (read
+  // only in the state pass) and dots_s (written after it, behind a barrier)
+  // share their 8 KiB. Elsewhere the registers bound it and they stay apart.
+  constexpr bool kShareXD = SB16 && !CONV;
+  __shared__ __attribute__((aligned(16))) float x_s[16][K];  // Gamma_t kn_t | Gamma_t q_t | 0
+  __shared__ __attribute__((aligned(16))) float dots_own[kShareXD ? 1 : V][16];
+  float (*const dots_s)[16] =
+      kShareXD ? reinterpret_cast<float (*)[16]>(&x_s[0][0]) : dots_own;  // w_t | y_t per row
   __shared__ __attribute__((aligned(16))) float kp_s[MAX_T][K];  // replay kn_t P_t (0 past n)
   __shared__ __attribute__((aligned(16))) float u_s[MAX_T][V];   // replay u_t (0 past n)
   __shared__ __attribute__((aligned(16))) float dn_s[K];
   __shared__ __attribute__((aligned(16))) float kpm_s[MAX_T][K];  // align: stage one kn_t P_t
   __shared__ __attribute__((aligned(16))) float dm_s[K];          // align: D_me
   __shared__ __attribute__((aligned(16))) float v_s[T][V];
-  __shared__ __attribute__((aligned(16))) float dots_s[V][16];   // w_t | y_t per state row
   __shared__ float pair_s[PI::P2];
   __shared__ __attribute__((aligned(16))) float part_s[PI::P2][PairStage<T>::PARTS];
   __shared__ float ssq_s[2][2][MAX_T];  // [new | old keys][wave of the half][token]
@@ -582,67 +589,80 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   char* const btile0 = static_cast<char*>(p.state) +
                        ((int64_t)bslot * p.slot_stride + (int64_t)h * PAGE +
                         (16 * (2 * wave) + lr) * K + LDC * lq) * ES;
+  // The pass over the 16 tiles, compiled with and without the boundary stage
+  // so that the common case carries no branch inside the unrolled loop.
+  auto state_pass = [&](auto align_tag) {
+    constexpr bool ALIGN = decltype(align_tag)::value;
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-    const int c0 = chan0<SB16>(cb, lq);
-    const floatx4 xa = *reinterpret_cast<const floatx4*>(&x_s[lr][c0]);
-    floatx4 dn4 = {1.f, 1.f, 1.f, 1.f};
-    float ka0 = 0.f, ka1 = 0.f;
-    if (replay) {
+    for (int cb = 0; cb < 8; ++cb) {
+      const int c0 = chan0<SB16>(cb, lq);
+      const floatx4 xa = *reinterpret_cast<const floatx4*>(&x_s[lr][c0]);
+      floatx4 dn4 = {1.f, 1.f, 1.f, 1.f};
+      float ka0 = 0.f, ka1 = 0.f;
       // A operand row lr of the replay MFMA is the channel of accumulator row lr.
       const int ca = chan0<SB16>(cb, lr >> 2) + (lr & 3);
-      dn4 = *reinterpret_cast<const floatx4*>(&dn_s[c0]);
-      ka0 = kp_s[lq][ca];
-      ka1 = kp_s[4 + lq][ca];
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      floatx4 s;
-      if constexpr (SB16) {
-        const u32x4 w = st[r][cb >> 1];
-        const uint32_t w0 = (cb & 1) ? w[2] : w[0];
-        const uint32_t w1 = (cb & 1) ? w[3] : w[1];
-        s = floatx4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
-      } else {
-        s = __builtin_bit_cast(floatx4, st[r][cb]);
-      }
       if (replay) {
-        const int64_t toff = (16 * r * K + 4 * LDC * (SB16 ? cb >> 1 : cb)) * ES;
-        if (balign) {
-          // Stage one: S_me, stored to the boundary page.
-          const int ca = chan0<SB16>(cb, lr >> 2) + (lr & 3);
-          const floatx4 dm4 = *reinterpret_cast<const floatx4*>(&dm_s[c0]);
-          s = s * dm4;
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(kpm_s[lq][ca], ub[r][0], s, 0, 0, 0);
-          if (me > 4)
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(kpm_s[4 + lq][ca], ub[r][1], s, 0, 0, 0);
+        dn4 = *reinterpret_cast<const floatx4*>(&dn_s[c0]);
+        ka0 = kp_s[lq][ca];
+        ka1 = kp_s[4 + lq][ca];
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        floatx4 s;
+        if constexpr (SB16) {
+          const u32x4 w = st[r][cb >> 1];
+          const uint32_t w0 = (cb & 1) ? w[2] : w[0];
+          const uint32_t w1 = (cb & 1) ? w[3] : w[1];
+          s = floatx4{bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+        } else {
+          s = __builtin_bit_cast(floatx4, st[r][cb]);
+        }
+        if (replay) {
+          const int64_t toff = (16 * r * K + 4 * LDC * (SB16 ? cb >> 1 : cb)) * ES;
+          if constexpr (ALIGN) {
+            // Stage one: S_me, stored to the boundary page.
+            const floatx4 dm4 = *reinterpret_cast<const floatx4*>(&dm_s[c0]);
+            s = s * dm4;
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(kpm_s[lq][ca], ub[r][0], s, 0, 0, 0);
+            if (me > 4)
+              s = __builtin_amdgcn_mfma_f32_16x16x4f32(kpm_s[4 + lq][ca], ub[r][1], s, 0, 0, 0);
+            if constexpr (SB16) {
+              sb[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
+              sb[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);
+              if (cb & 1) *reinterpret_cast<u32x4*>(btile0 + toff) = sb[r];
+            } else {
+              *reinterpret_cast<floatx4*>(btile0 + toff) = s;
+            }
+          }
+          s = s * dn4;
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka0, ub[r][0], s, 0, 0, 0);
+          if (n > 4) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka1, ub[r][1], s, 0, 0, 0);
+          char* const dst = tile0 + toff;
           if constexpr (SB16) {
-            sb[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
-            sb[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);
-            if (cb & 1) *reinterpret_cast<u32x4*>(btile0 + toff) = sb[r];
+            sn[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
+            sn[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);
+            if (cb & 1) *reinterpret_cast<u32x4*>(dst) = sn[r];
           } else {
-            *reinterpret_cast<floatx4*>(btile0 + toff) = s;
+            *reinterpret_cast<floatx4*>(dst) = s;
           }
         }
-        s = s * dn4;
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka0, ub[r][0], s, 0, 0, 0);
-        if (n > 4) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka1, ub[r][1], s, 0, 0, 0);
-        char* const dst = tile0 + toff;
-        if constexpr (SB16) {
-          sn[r][(cb & 1) * 2] = pack_bf16x2(s[0], s[1]);
-          sn[r][(cb & 1) * 2 + 1] = pack_bf16x2(s[2], s[3]);
-          if (cb & 1) *reinterpret_cast<u32x4*>(dst) = sn[r];
-        } else {
-          *reinterpret_cast<floatx4*>(dst) = s;
-        }
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[0], s[0], acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[1], s[1], acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[2], s[2], acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[3], s[3], acc[r], 0, 0, 0);
       }
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[0], s[0], acc[r], 0, 0, 0);
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[1], s[1], acc[r], 0, 0, 0);
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[2], s[2], acc[r], 0, 0, 0);
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[3], s[3], acc[r], 0, 0, 0);
     }
+  };
+  if constexpr (FUSED) {
+    if (balign)
+      state_pass(std::true_type{});
+    else
+      state_pass(std::false_type{});
+  } else {
+    state_pass(std::false_type{});
   }
   // acc[r], lane l, value i: column j = 4(l/16) + i of state row 16(2w+r) + l%16.
+  if constexpr (kShareXD) __syncthreads();  // every wave has read x_s: it now holds the dots
 #pragma unroll
   for (int r = 0; r < 2; ++r)
     *reinterpret_cast<floatx4*>(&dots_s[16 * (2 * wave + r) + lr][4 * lq]) = acc[r];

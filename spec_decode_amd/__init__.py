@@ -104,6 +104,13 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
     return t.data_ptr()
 
 
+def _need(t: Optional[torch.Tensor], count: int, name: str) -> None:
+    """Per-request device arrays are read at indices below ``count``: a shorter
+    tensor would be read past its end, so reject it on the host."""
+    if t is not None and isinstance(t, torch.Tensor) and t.numel() < count:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {count}")
+
+
 def _ptr_rows(t: torch.Tensor, dtype, row_stride: int, name: str):
     """Device address of a row-major 2-D view whose rows are ``row_stride``
     elements apart (e.g. a column slice of a wider tensor)."""
@@ -160,6 +167,10 @@ def kda_commit(*, heads: int, window: int, batch: int, state_dtype: int,
     ca, cst = _table(corr_addrs, ctypes.c_uint64), _table(corr_row_strides, ctypes.c_int64)
     ka, kst = _table(kg_addrs, ctypes.c_uint64), _table(kg_row_strides, ctypes.c_int64)
     i32 = torch.int32
+    for t, name in ((sources, "sources"), (commit_lens, "commit_lens"),
+                    (destinations, "destinations"), (boundaries, "boundaries"),
+                    (boundary_lens, "boundary_lens"), (record_rows, "record_rows")):
+        _need(t, batch, name)
     _check(_lib.kda_commit(
         L, heads, window, batch, state_dtype, st, sst, ca, cst, ka, kst,
         _ptr(a_log, torch.float32, "a_log"), _ptr(dt_bias, torch.float32, "dt_bias"),
@@ -200,6 +211,9 @@ def kda_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw_g, raw_beta,
     """Stock verify: writes out (o, or its gated RMSNorm with gate and
     norm_weight) and the records, never the state. The pool's element type
     (float32 or bfloat16) is that of ``state``."""
+    _need(state_indices, batch, "state_indices")
+    _need(record_rows, batch, "record_rows")
+    _need(query_start_loc, batch + 1 if batch else 0, "query_start_loc")
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
         q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
         record_rows, out)
@@ -220,6 +234,10 @@ def kda_fused_replay_verify(*, heads: int, tokens: int, batch: int, q, k, v, raw
                             boundary_lens=None, stream=None):
     """Replay each request's pending tokens into its page, then verify the
     window. The pool's element type (float32 or bfloat16) is that of ``state``."""
+    for t, name in ((state_indices, "state_indices"), (record_rows, "record_rows"),
+                    (boundaries, "boundaries"), (boundary_lens, "boundary_lens")):
+        _need(t, batch, name)
+    _need(query_start_loc, batch + 1 if batch else 0, "query_start_loc")
     (pq, pk, pv, pg, pb, pa, pd, ps, psi, pc, pkg, prr, po) = _verify_args(
         q, k, v, raw_g, raw_beta, a_log, dt_bias, state, state_indices, corr, kg,
         record_rows, out)
@@ -248,6 +266,9 @@ def kda_fused_conv_replay_verify(*, heads: int, tokens: int, batch: int, x, x_ro
     pre-activations ``x`` (rows of ``x_row_stride`` elements) and each channel's
     window in ``conv_state`` (BF16, rewritten in place). Strides in elements."""
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    for t, name in ((state_indices, "state_indices"), (record_rows, "record_rows"),
+                    (boundaries, "boundaries"), (boundary_lens, "boundary_lens")):
+        _need(t, batch, name)
     _check(_lib.kda_fused_conv_replay_verify(
         heads, tokens, batch, _ptr_rows(x, bf, int(x_row_stride), "x"), int(x_row_stride), _ptr(conv_weight, bf, "conv_weight"),
         _ptr(conv_bias, bf, "conv_bias"), _ptr(conv_state, bf, "conv_state"),
@@ -278,6 +299,9 @@ def kda_gate_projection(*, tokens: int, heads: int, f_a, f_a_row_stride: int, f_
 def kda_defer_commit(*, batch: int, state_indices, commit_lens, record_rows, pending,
                      eager=None, null_slot: int = 0, stream=None):
     i32 = torch.int32
+    for t, name in ((state_indices, "state_indices"), (commit_lens, "commit_lens"),
+                    (record_rows, "record_rows"), (eager, "eager")):
+        _need(t, batch, name)
     _check(_lib.kda_defer_commit(batch, _ptr(state_indices, i32, "state_indices"),
                                  _ptr(commit_lens, i32, "commit_lens"),
                                  _ptr(record_rows, i32, "record_rows"),
@@ -289,6 +313,10 @@ def kda_flush_plan(*, batch: int, spec_query_len: int, state_indices, record_row
                    commit_lens, final_indices, boundaries, boundary_lens, null_slot: int = 0,
                    stream=None):
     i32 = torch.int32
+    for t, name in ((state_indices, "state_indices"), (record_rows, "record_rows"),
+                    (commit_lens, "commit_lens"), (final_indices, "final_indices"),
+                    (boundaries, "boundaries"), (boundary_lens, "boundary_lens")):
+        _need(t, batch, name)
     _check(_lib.kda_flush_plan(batch, int(spec_query_len),
                                _ptr(state_indices, i32, "state_indices"),
                                _ptr(record_rows, i32, "record_rows"),

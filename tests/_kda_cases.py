@@ -297,3 +297,54 @@ def run_conv_case(*, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, raw_g,
     assert_exact(f"{label} windows (written)", gpu["pool"][cm], ref["pool"][cm])
     assert_exact(f"{label} windows (untouched)", gpu["pool"][~cm], pool[~cm])
     return gpu, ref
+
+
+# ---------------------------------------------------------------- sampled full-size checks
+
+def sampled_fused_oracle(*, R, H, T, RQ, state_pages, slots, rows, pending_row, corr, kg,
+                         win, a_log, dt_bias, lb, qsl=None, bounds=None, blens=None,
+                         state_dtype=np.float32):
+    """The oracle on a compact copy of requests R of a large fused call: request j
+    of the copy owns slot j + 1 (and, with boundaries, slot nR + 1 + j) and
+    record row j. state_pages(slot) returns a slot's host page set; win holds
+    the full call's activation rows (indexed through qsl when given).
+    Returns the copy's (state, corr, kg, out, token rows per request)."""
+    nR = len(R)
+    page = H * V * K
+    n_slots = nR + 1 + (nR if bounds is not None else 0)
+    m_state = np.zeros(n_slots * page, state_dtype)
+    m_slots = np.array([j + 1 if slots[b] > 0 else 0 for j, b in enumerate(R)], np.int32)
+    m_rows = np.array([j if rows[b] >= 0 else -1 for j, b in enumerate(R)], np.int32)
+    m_corr = np.zeros((nR, H, RQ, V), np.float32)
+    m_kg = np.zeros((nR, H, RQ, 2 * K), np.uint16)
+    m_pend = np.zeros(nR, np.int32)
+    m_bnd = m_blen = None
+    if bounds is not None:
+        m_bnd = np.array([nR + 1 + j if bounds[b] > 0 else 0 for j, b in enumerate(R)], np.int32)
+        m_blen = np.array([blens[b] for b in R], np.int32)
+    for j, b in enumerate(R):
+        if slots[b] > 0:
+            m_state[(j + 1) * page:(j + 2) * page] = state_pages(int(slots[b]))
+        if bounds is not None and bounds[b] > 0:
+            m_state[(nR + 1 + j) * page:(nR + 2 + j) * page] = state_pages(int(bounds[b]))
+        if rows[b] >= 0:
+            m_corr[j], m_kg[j], m_pend[j] = corr[rows[b]], kg[rows[b]], pending_row[rows[b]]
+    lens = window_lengths(len(slots), T, qsl)
+    toks = [np.arange(b * T, b * T + T) if qsl is None else
+            np.arange(int(qsl[b]), int(qsl[b]) + lens[b]) for b in R]
+    m_qsl = None
+    if qsl is not None:
+        m_qsl = np.zeros(nR + 1, np.int32)
+        m_qsl[1:] = np.cumsum([lens[b] for b in R])
+    tok = np.concatenate(toks) if toks else np.zeros(0, np.int64)
+    m_win = {k: np.ascontiguousarray(v[tok]) for k, v in win.items()}
+    m_out = np.zeros((max(len(tok), 1), H * V), np.uint16)
+    oracle.fused_replay_verify(heads=H, tokens=T, batch=nR, q=m_win["q"], k=m_win["k"],
+                               v=m_win["v"], raw_g=m_win["raw_g"], raw_beta=m_win["raw_beta"],
+                               a_log=a_log, dt_bias=dt_bias, lower_bound=lb, state=m_state,
+                               state_slot_stride=page, state_indices=m_slots, corr=m_corr,
+                               kg=m_kg, record_tokens=RQ, record_rows=m_rows, pending=m_pend,
+                               out=m_out, query_start_loc=m_qsl, boundaries=m_bnd,
+                               boundary_lens=m_blen)
+    return dict(state=m_state, corr=m_corr, kg=m_kg, out=m_out, toks=toks, slots=m_slots,
+                bounds=m_bnd)

@@ -177,3 +177,23 @@ def test_zero_batch_is_a_no_op(lib):
     lib.kda_flush_plan.restype = ctypes.c_int
     assert lib.kda_flush_plan(ctypes.c_int(0), ctypes.c_int(4), *([P(None)] * 7),
                               ctypes.c_int(0), P(None)) == 0
+
+
+def test_binding_rejects_short_per_request_arrays(lib):
+    """The binding checks per-request array lengths on the host: a tensor
+    shorter than the batch would be read past its end by the kernels."""
+    import torch
+    import spec_decode_amd as kda
+    B = 4
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)
+    base = dict(heads=1, tokens=2, batch=B, q=None, k=None, v=None, raw_g=None, raw_beta=None,
+                a_log=None, dt_bias=None, lower_bound=-5.0, state=None, state_slot_stride=0,
+                corr=None, kg=None, record_tokens=2, out=None)
+    with pytest.raises(ValueError, match="boundaries"):
+        kda.kda_fused_replay_verify(state_indices=i32(B), record_rows=i32(B), pending=i32(B),
+                                    boundaries=i32(B - 1), boundary_lens=i32(B), **base)
+    with pytest.raises(ValueError, match="query_start_loc"):
+        kda.kda_verify(state_indices=i32(B), query_start_loc=i32(B), **base)
+    with pytest.raises(ValueError, match="state_indices"):
+        kda.kda_defer_commit(batch=B, state_indices=i32(B - 2), commit_lens=i32(B),
+                             record_rows=i32(B), pending=i32(B))

@@ -22,6 +22,7 @@ import oracle
 import workloads as W
 from _compare import assert_bf16_close, assert_exact, assert_f32_close
 from _kda_cases import (DEV, announce, dev, dev_bf16, np_of, run_commit_case, run_verify_case,
+                        sampled_fused_oracle,
                         window_np)
 
 pytestmark = pytest.mark.gpu
@@ -420,4 +421,152 @@ def test_config4_large_decode_full_size_sampled():
                              g_final[sl * page:(sl + 1) * page],
                              m_state[(j + 1) * page:(j + 2) * page])
     del d_state, before, fused_state
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- limits and variants at size
+
+def _check_sampled(label, R, m, g_out, g_state_pages, g_corr, g_kg, slots, rows, bounds, T,
+                   bf16, page):
+    close = assert_bf16_close if bf16 else assert_f32_close
+    nR = len(R)
+    row0 = 0
+    for j, b in enumerate(R):
+        toks = m["toks"][j]
+        n_t = len(toks)
+        assert_bf16_close(f"{label} out request {b}", g_out[toks], m["out"][row0:row0 + n_t])
+        row0 += n_t
+        if slots[b] > 0:
+            close(f"{label} page request {b}", g_state_pages(int(slots[b])),
+                  m["state"][(j + 1) * page:(j + 2) * page])
+            if bounds is not None and bounds[b] > 0:
+                close(f"{label} boundary page request {b}", g_state_pages(int(bounds[b])),
+                      m["state"][(nR + 1 + j) * page:(nR + 2 + j) * page])
+        if rows[b] >= 0 and slots[b] > 0 and n_t > 0:
+            assert_f32_close(f"{label} corrections request {b}", g_corr[rows[b]], m["corr"][j])
+            assert_exact(f"{label} key/gate request {b}", g_kg[rows[b]], m["kg"][j])
+
+
+def test_maximum_batch_grid_fused_sampled():
+    """65535 requests (the largest grid the kernels take), one head, FP32 pool
+    of 65536 slots (4 GiB), ragged null slots and missing record rows; 24
+    sampled requests against the oracle, and every page the call must not
+    write compared bit for bit."""
+    import spec_decode_amd as kda
+    H, B, T, RQ, S = 1, 65535, 2, 2, 65536
+    page = H * V * K
+    g = W._gen(900)
+    slots = (W.permutation(g, S - 1) + 1).numpy()
+    slots[::997] = 0
+    rows = W.permutation(g, B).numpy()
+    rows[5::1009] = -1
+    pending_row = W.uniform_int(g, -1, RQ + 1, B).numpy()
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    corr, kg = W.draw_records(g, B, H, RQ)
+    corr, kg = corr.numpy(), W.bits(kg)
+    win = window_np(W.draw_window(g, B, T, H))
+    d_state = W.draw_state(901, S * page, torch.float32, DEV)
+    before = d_state.clone()
+    d_corr, d_kg = dev(corr), dev_bf16(kg)
+    out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=DEV)
+    announce("max batch: fused H=1 B=65535 T=2")
+    kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]),
+                                k=dev_bf16(win["k"]), v=dev_bf16(win["v"]),
+                                raw_g=dev_bf16(win["raw_g"]), raw_beta=dev_bf16(win["raw_beta"]),
+                                a_log=dev(a_log[0].numpy()), dt_bias=dev(dtb[0].numpy()),
+                                lower_bound=W.LOWER_BOUND, state=d_state, state_slot_stride=page,
+                                state_indices=dev(slots), corr=d_corr, kg=d_kg, record_tokens=RQ,
+                                record_rows=dev(rows), pending=dev(pending_row), out=out)
+    torch.cuda.synchronize()
+    n_of = lambda b: min(max(int(pending_row[rows[b]]), 0), RQ) if rows[b] >= 0 else 0
+    touched = torch.zeros(S, dtype=torch.bool)
+    for b in range(B):
+        if slots[b] > 0 and n_of(b) > 0:
+            touched[int(slots[b])] = True
+    keep = (~touched).nonzero().flatten().to(DEV)
+    assert torch.equal(d_state.view(S, page).index_select(0, keep).view(torch.int32),
+                       before.view(S, page).index_select(0, keep).view(torch.int32))
+    rng = np.random.default_rng(902)
+    R = [0, 1, B - 1, 997, 5] + [int(x) for x in rng.choice(B, 19, replace=False)]
+    R = list(dict.fromkeys(R))
+    s_host = lambda sl: before[sl * page:(sl + 1) * page].cpu().numpy()
+    m = sampled_fused_oracle(R=R, H=H, T=T, RQ=RQ, state_pages=s_host, slots=slots, rows=rows,
+                             pending_row=pending_row, corr=corr, kg=kg, win=win,
+                             a_log=a_log[0].numpy(), dt_bias=dtb[0].numpy(), lb=W.LOWER_BOUND)
+    g_pages = lambda sl: d_state[sl * page:(sl + 1) * page].cpu().numpy()
+    _check_sampled("max batch", R, m, np_of(out), g_pages, np_of(d_corr), np_of(d_kg), slots,
+                   rows, None, T, False, page)
+    del d_state, before
+    torch.cuda.empty_cache()
+
+
+def test_large_decode_ragged_windows_and_boundaries_bf16_sampled():
+    """The large decode shape (H=64, B=512, q=8) on a BF16 pool of 1040 slots
+    (2 GiB): window lengths 0..8 through query_start_loc and boundary stores
+    for half the requests (m in 1..9); 30 sampled requests against the oracle
+    and the pages nobody writes compared bit for bit."""
+    import spec_decode_amd as kda
+    H, B, T, RQ, S = 64, 512, 8, 8, 1040
+    page = H * V * K
+    g = W._gen(910)
+    perm = (W.permutation(g, S - 1) + 1).numpy()
+    slots = perm[:B].copy()
+    slots[::41] = 0
+    bounds = perm[B:2 * B].copy()
+    bounds[1::2] = 0
+    assert slots.size == B and bounds.size == B
+    blens = W.uniform_int(g, 1, RQ + 1, B).numpy()
+    rows = W.permutation(g, B).numpy()
+    rows[3::37] = -1
+    pending_row = W.uniform_int(g, 0, RQ, B).numpy()
+    lens = W.uniform_int(g, 0, T, B).numpy()
+    qsl = np.zeros(B + 1, np.int32)
+    qsl[1:] = np.cumsum(lens)
+    total = int(qsl[-1])
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    corr, kg = W.draw_records(g, B, H, RQ)
+    corr, kg = corr.numpy(), W.bits(kg)
+    win = {k: np.ascontiguousarray(v[:total]) for k, v in window_np(W.draw_window(g, B, T, H)).items()}
+    d_state = W.draw_state(911, S * page, torch.bfloat16, DEV)
+    before = d_state.clone()
+    d_corr, d_kg = dev(corr), dev_bf16(kg)
+    out = torch.zeros((total, H * V), dtype=torch.bfloat16, device=DEV)
+    announce("large decode ragged + boundaries, BF16 pool")
+    kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]),
+                                k=dev_bf16(win["k"]), v=dev_bf16(win["v"]),
+                                raw_g=dev_bf16(win["raw_g"]), raw_beta=dev_bf16(win["raw_beta"]),
+                                a_log=dev(a_log[0].numpy()), dt_bias=dev(dtb[0].numpy()),
+                                lower_bound=W.LOWER_BOUND, state=d_state, state_slot_stride=page,
+                                state_indices=dev(slots), corr=d_corr, kg=d_kg, record_tokens=RQ,
+                                record_rows=dev(rows), pending=dev(pending_row),
+                                query_start_loc=dev(qsl), boundaries=dev(bounds),
+                                boundary_lens=dev(blens), out=out)
+    torch.cuda.synchronize()
+    touched = torch.zeros(S, dtype=torch.bool)
+    for b in range(B):
+        n = min(pending_row[rows[b]], RQ) if rows[b] >= 0 else 0
+        if slots[b] > 0 and lens[b] > 0 and n > 0:
+            touched[int(slots[b])] = True
+            if bounds[b] > 0:
+                touched[int(bounds[b])] = True
+    keep = (~touched).nonzero().flatten().to(DEV)
+    assert torch.equal(d_state.view(S, page).index_select(0, keep).view(torch.int16),
+                       before.view(S, page).index_select(0, keep).view(torch.int16))
+    rng = np.random.default_rng(912)
+    live = [b for b in range(B) if slots[b] > 0 and rows[b] >= 0]
+    by_len = {}
+    for b in live:
+        by_len.setdefault(int(lens[b]), []).append(b)
+    R = [0, 41, 3] + [int(rng.choice(by_len[l])) for l in sorted(by_len)]
+    R += [int(x) for x in rng.choice(live, 16, replace=False)]
+    R = list(dict.fromkeys(R))
+    s_host = lambda sl: np_of(before[sl * page:(sl + 1) * page])
+    m = sampled_fused_oracle(R=R, H=H, T=T, RQ=RQ, state_pages=s_host, slots=slots, rows=rows,
+                             pending_row=pending_row, corr=corr, kg=kg, win=win,
+                             a_log=a_log[0].numpy(), dt_bias=dtb[0].numpy(), lb=W.LOWER_BOUND,
+                             qsl=qsl, bounds=bounds, blens=blens, state_dtype=np.uint16)
+    g_pages = lambda sl: np_of(d_state[sl * page:(sl + 1) * page])
+    _check_sampled("ragged+bnd", R, m, np_of(out), g_pages, np_of(d_corr), np_of(d_kg), slots,
+                   rows, bounds, T, True, page)
+    del d_state, before
     torch.cuda.empty_cache()

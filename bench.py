@@ -40,6 +40,11 @@ K = V = 128
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=("large_decode", "commit", "fused", "align"),
+                    default="large_decode",
+                    help="large_decode (default): the whole step on the large decode batch; "
+                         "commit / fused / align: that kernel alone on the BF16 commit, "
+                         "fused replay+verify and 8-layer align commit workloads")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -215,6 +220,122 @@ def cpu_baseline(host, H, T, RQ, n_req, lb, bf16=False):
     }
 
 
+# ----------------------------------------------------------------- single-kernel workloads
+
+def bench_kernel_workload(args):
+    """Times one kernel on its own workload (W warm-up launches, K timed) and
+    prints the same JSON contract: value = algorithmic state bytes per second."""
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import spec_decode_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    i32 = lambda t: t.to(dev)
+    if args.workload in ("commit", "align"):
+        w = W.config1(device=dev) if args.workload == "commit" else W.config3(device=dev)
+        a = w.arrays
+        L, H, B, Q = w.layers, w.heads, w.batch, w.tokens
+        states = [a["state"]] if L == 1 else [a[f"state{l}"] for l in range(L)]
+        corrs = [a["corr"].to(dev)] if L == 1 else [a[f"corr{l}"].to(dev) for l in range(L)]
+        kgs = [a["kg"].to(dev)] if L == 1 else [a[f"kg{l}"].to(dev) for l in range(L)]
+        bnd = a.get("boundaries")
+        blen = a.get("boundary_lens")
+        call = dict(heads=H, window=Q, batch=B, state_dtype=kda.KDA_STATE_BF16,
+                    state_addrs=[t.data_ptr() for t in states], state_slot_strides=w.slot_strides,
+                    corr_addrs=[t.data_ptr() for t in corrs], corr_row_strides=[H * Q * V] * L,
+                    kg_addrs=[t.data_ptr() for t in kgs], kg_row_strides=[H * Q * 2 * K] * L,
+                    a_log=a["a_log"].to(dev), dt_bias=a["dt_bias"].to(dev),
+                    sources=i32(a["sources"]), commit_lens=i32(a["commit_lens"]),
+                    destinations=i32(a["destinations"]),
+                    boundaries=None if bnd is None else i32(bnd),
+                    boundary_lens=None if blen is None else i32(blen), lower_bound=w.lower_bound)
+        launch = lambda: kda.kda_commit(**call)
+        src, dst = a["sources"].numpy(), a["destinations"].numpy()
+        lens = a["commit_lens"].numpy()
+        bn = None if bnd is None else bnd.numpy()
+        bl = None if blen is None else blen.numpy()
+        page = V * K * 2
+        st = tot = 0
+        for b in range(B):
+            n = min(int(lens[b]), Q)
+            if not (n > 0 and src[b] > 0 and dst[b] > 0):
+                continue
+            s_b = 2 * page + (page if bn is not None and bn[b] > 0 and bl[b] > 0 else 0)
+            st += L * H * s_b
+            tot += L * H * (s_b + n * (V * 4 + 2 * K * 2))
+        items = L * B * H
+        name = "kda_commit (BF16)" if L == 1 else "kda_commit (BF16, align, 8 layers)"
+        workload = ("commit: L=1 H=32 B=64 window 4, BF16 pool of 256 slots, src -> dst"
+                    if L == 1 else
+                    "align_commit: L=8 H=32 B=256 window 8, BF16 pools of 641 slots, "
+                    "128 boundary stores")
+        dtype = "f32"
+    else:  # fused
+        w = W.config2(device=dev)
+        a = w.arrays
+        H, B, T, RQ = w.heads, w.batch, w.tokens, w.record_tokens
+        state = a["state"]
+        slots, rows = i32(a["state_indices"]), i32(a["record_rows"])
+        corr, kg = a["corr"].to(dev), a["kg"].to(dev)
+        pend_row = torch.zeros(B, dtype=torch.int32)
+        pend_row[a["record_rows"].long()] = a["pending"]
+        pending = i32(pend_row)
+        a_log, dt_bias = a["a_log"][0].contiguous().to(dev), a["dt_bias"][0].contiguous().to(dev)
+        new, prior = w.windows["new"].to(dev), w.windows["prior"].to(dev)
+        out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=dev)
+        kda.kda_verify(heads=H, tokens=T, batch=B, q=prior.q, k=prior.k, v=prior.v,
+                       raw_g=prior.raw_g, raw_beta=prior.raw_beta, a_log=a_log, dt_bias=dt_bias,
+                       lower_bound=w.lower_bound, state=state, state_slot_stride=H * V * K,
+                       state_indices=slots, corr=corr, kg=kg, record_tokens=RQ,
+                       record_rows=rows, out=out)
+        launch = lambda: kda.kda_fused_replay_verify(
+            heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v, raw_g=new.raw_g,
+            raw_beta=new.raw_beta, a_log=a_log, dt_bias=dt_bias, lower_bound=w.lower_bound,
+            state=state, state_slot_stride=H * V * K, state_indices=slots, corr=corr, kg=kg,
+            record_tokens=RQ, record_rows=rows, pending=pending, out=out)
+        st, tot = fused_bytes(a["state_indices"].numpy(), a["record_rows"].numpy(),
+                              pend_row.numpy(), T, RQ, H)
+        items = B * H
+        name = "kda_fused_replay_verify (FP32)"
+        workload = "fused: L=1 H=32 B=128 q=4, FP32 pool of 256 slots, pending 0..4"
+        dtype = "f32"
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        launch()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[2 * i].record()
+        launch()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
+    mean_ms = sum(ms) / len(ms)
+    achieved = tot / (mean_ms * 1e-3) / 1e9
+    value = st * args.steps / wall / 1e9
+    print(json.dumps({
+        "metric": "state GB/s (% of HBM peak) + (req,head) items/s, KDA commit & fused verify",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic", "config": {"workload": workload, "kernel": name},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "items_per_s": round(items / (mean_ms * 1e-3), 1),
+        "kernels": {name: {"mean_ms": round(mean_ms, 4), "min_ms": round(min(ms), 4),
+                           "state_gbs": round(st / (mean_ms * 1e-3) / 1e9, 1),
+                           "total_gbs": round(achieved, 1)}},
+        "roofline": {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": int(tot)},
+    }), flush=True)
+
+
 # ----------------------------------------------------------------- main
 
 def main():
@@ -226,6 +347,9 @@ def main():
         sys.exit(2)
     if args.steps < 1:
         sys.exit("--steps must be >= 1")
+    if args.workload != "large_decode":
+        bench_kernel_workload(args)
+        return
     import numpy as np
     import torch
 

@@ -83,7 +83,7 @@ def _load():
 
 
 def default_threads() -> int:
-    """Every core this process may run on (capped at 16, the GPU machine's share)."""
+    """Every core this process may run on, capped at 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover

@@ -252,7 +252,7 @@ def conv_written(slots, H, RQ, T, strides, null_slot, n_elems):
 def run_conv_case(*, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, raw_g, raw_beta,
                   x, pitch, conv_w, conv_b, pool, strides, rows, pending,
                   lb=W.LOWER_BOUND, null_slot=0, label="fused conv", gate=None,
-                  norm_weight=None, norm_eps=1e-5, q_scale=K ** -0.5):
+                  norm_weight=None, norm_eps=1e-5, q_scale=K ** -0.5, bounds=None, blens=None):
     """kda_fused_conv_replay_verify on the GPU and the oracle on host copies.
     Host arrays: x uint16 [B*T, pitch], conv_w uint16 [3, 4, HK], conv_b uint16
     [3HK] or None, pool uint16 flat window pool with the given strides; the
@@ -276,7 +276,9 @@ def run_conv_case(*, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, raw_g,
         pending=dev(np.asarray(pending, np.int32)), out=d["out"], null_slot=null_slot,
         gate=None if gate is None else dev_bf16(gate),
         norm_weight=None if norm_weight is None else dev(np.asarray(norm_weight, np.float32)),
-        norm_eps=norm_eps)
+        norm_eps=norm_eps,
+        boundaries=None if bounds is None else dev(np.asarray(bounds, np.int32)),
+        boundary_lens=None if blens is None else dev(np.asarray(blens, np.int32)))
     torch.cuda.synchronize()
     gpu = {k: np_of(v) for k, v in d.items()}
     ref = dict(state=state.copy(), corr=corr.copy(), kg=kg.copy(), pool=pool.copy(),
@@ -288,11 +290,13 @@ def run_conv_case(*, H, B, T, RQ, state, slots, corr, kg, a_log, dt_bias, raw_g,
         raw_g=raw_g, raw_beta=raw_beta, a_log=a_log, dt_bias=dt_bias, lower_bound=lb,
         state=ref["state"], state_slot_stride=stride, state_indices=slots, corr=ref["corr"],
         kg=ref["kg"], record_tokens=RQ, record_rows=rows, pending=pending, out=ref["out"],
-        null_slot=null_slot, gate=gate, norm_weight=norm_weight, norm_eps=norm_eps)
+        null_slot=null_slot, gate=gate, norm_weight=norm_weight, norm_eps=norm_eps,
+        boundaries=bounds, boundary_lens=blens)
     compare_verify(gpu, ref, dict(state=state, corr=corr, kg=kg), fused=True, H=H, B=B, T=T,
                    RQ=RQ, slots=slots, rows=rows, pending=pending, stride=stride,
                    null_slot=null_slot, label=label,
-                   out_ulps=GATED_OUT_ULPS if gate is not None else 1)
+                   out_ulps=GATED_OUT_ULPS if gate is not None else 1, bounds=bounds,
+                   blens=blens)
     cm = conv_written(slots, H, RQ, T, strides, null_slot, pool.size)
     assert_exact(f"{label} windows (written)", gpu["pool"][cm], ref["pool"][cm])
     assert_exact(f"{label} windows (untouched)", gpu["pool"][~cm], pool[~cm])

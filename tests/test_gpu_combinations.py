@@ -1,0 +1,130 @@
+"""GPU parity over seeded random combinations of the verify and fused options
+(window, record capacity, heads, batch, FP32/BF16 pool, gated output stage,
+variable-length windows, boundary stores, padded slot strides, null slots,
+missing record rows, edge pending counts), each against the FP64 oracle
+element by element. The single-option tests cover each option alone; these
+cover them together."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _kda_cases import conv_pool_layout, run_conv_case, run_verify_case, window_np
+
+pytestmark = pytest.mark.gpu
+
+K = V = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import spec_decode_amd  # noqa: F401  (fails loudly without libkda.so)
+
+    torch.cuda.init()
+    yield
+
+
+def _draw(seed):
+    r = np.random.default_rng(seed)
+    T = int(r.integers(1, 9))
+    RQ = int(r.integers(T, 9))
+    H = int(r.integers(1, 5))
+    B = int(r.integers(1, 10))
+    return r, dict(T=T, RQ=RQ, H=H, B=B, bf16=bool(r.integers(2)), gated=bool(r.integers(2)),
+                   fused=bool(r.integers(3) > 0), varlen=bool(r.integers(2)),
+                   align=bool(r.integers(2)), pad=int(r.integers(2)))
+
+
+@pytest.mark.parametrize("seed", list(range(48)))
+def test_random_combination(seed):
+    r, c = _draw(2000 + seed)
+    T, RQ, H, B, bf16 = c["T"], c["RQ"], c["H"], c["B"], c["bf16"]
+    fused, align = c["fused"], c["fused"] and c["align"]
+    S = 2 * B + 3
+    page = H * V * K
+    stride = page + (8 * int(r.integers(1, 40)) if c["pad"] else 0)
+    g = W._gen(3000 + seed)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    corr, kg = W.draw_records(g, B, H, RQ)
+    state = W.draw_state(4000 + seed, S * stride, torch.float32)
+    state = W.bits(state.to(torch.bfloat16)) if bf16 else state.numpy().copy()
+    perm = r.permutation(np.arange(1, S)).astype(np.int32)
+    slots = perm[:B].copy()
+    bounds = perm[B:2 * B].copy()
+    for b in range(B):
+        if r.random() < 0.15:
+            slots[b] = 0
+        if r.random() < 0.3:
+            bounds[b] = 0
+    rows = r.permutation(B).astype(np.int32)
+    for b in range(B):
+        if r.random() < 0.15:
+            rows[b] = -1
+    pending = r.integers(-1, RQ + 2, B).astype(np.int32)
+    blens = r.integers(0, RQ + 2, B).astype(np.int32)
+    qsl = None
+    out_rows = B * T
+    win = window_np(W.draw_window(g, B, T, H))
+    if c["varlen"]:
+        lens = r.integers(0, T + 2, B)
+        qsl = np.zeros(B + 1, np.int32)
+        qsl[1:] = np.cumsum(lens)
+        out_rows = int(qsl[-1]) + 1
+        big = window_np(W.draw_window(g, max(out_rows // T + 1, B), T, H))
+        win = {k: np.ascontiguousarray(v[:out_rows]) for k, v in big.items()}
+    kw = {}
+    if c["gated"]:
+        gate, weight, eps = W.draw_output_stage(W._gen(5000 + seed), max(out_rows // T + 1, B),
+                                                T, H)
+        kw = dict(gate=np.ascontiguousarray(W.bits(gate)[:out_rows]),
+                  norm_weight=weight.numpy(), norm_eps=eps)
+    if align:
+        kw.update(bounds=bounds, blens=blens)
+    run_verify_case(fused=fused, H=H, B=B, T=T, RQ=RQ, state=state, slots=slots,
+                    corr=corr.numpy().copy(), kg=W.bits(kg), a_log=a_log[0].numpy(),
+                    dt_bias=dtb[0].numpy(), win=win, rows=rows,
+                    pending=pending if fused else None, stride=stride, qsl=qsl,
+                    out_rows=out_rows, label=f"combination {seed}: {c}", **kw)
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_random_conv_combination(seed):
+    r, c = _draw(6000 + seed)
+    T, RQ, H, B, bf16 = c["T"], c["RQ"], c["H"], c["B"], c["bf16"]
+    S = 2 * B + 3
+    page = H * V * K
+    g = W._gen(7000 + seed)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    corr, kg = W.draw_records(g, B, H, RQ)
+    state = W.draw_state(8000 + seed, S * page, torch.float32)
+    state = W.bits(state.to(torch.bfloat16)) if bf16 else state.numpy().copy()
+    perm = r.permutation(np.arange(1, S)).astype(np.int32)
+    slots = perm[:B].copy()
+    bounds = perm[B:2 * B].copy()
+    for b in range(B):
+        if r.random() < 0.15:
+            slots[b] = 0
+    rows = r.permutation(B).astype(np.int32)
+    for b in range(B):
+        if r.random() < 0.15:
+            rows[b] = -1
+    pending = r.integers(-1, RQ + 2, B).astype(np.int32)
+    blens = r.integers(0, RQ + 2, B).astype(np.int32)
+    win = window_np(W.draw_window(g, B, T, H))
+    cv = W.draw_conv_inputs(W._gen(9000 + seed), B, T, H, RQ, S)
+    dim_first = bool(r.integers(2))
+    pool = W.bits(cv.window)
+    pool = (pool if dim_first else pool.transpose(0, 2, 1)).reshape(-1).copy()
+    kw = {}
+    if c["gated"]:
+        gate, weight, eps = W.draw_output_stage(W._gen(9500 + seed), B, T, H)
+        kw = dict(gate=W.bits(gate), norm_weight=weight.numpy(), norm_eps=eps)
+    if c["align"]:
+        kw.update(bounds=bounds, blens=blens)
+    run_conv_case(H=H, B=B, T=T, RQ=RQ, state=state, slots=slots, corr=corr.numpy().copy(),
+                  kg=W.bits(kg), a_log=a_log[0].numpy(), dt_bias=dtb[0].numpy(),
+                  raw_g=win["raw_g"], raw_beta=win["raw_beta"], x=W.bits(cv.x), pitch=cv.pitch,
+                  conv_w=W.bits(cv.weight),
+                  conv_b=W.bits(cv.bias) if r.integers(2) else None, pool=pool,
+                  strides=conv_pool_layout(S, H, RQ + 2, dim_first), rows=rows, pending=pending,
+                  label=f"conv combination {seed}: {c}", **kw)

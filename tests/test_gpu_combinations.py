@@ -128,3 +128,55 @@ def test_random_conv_combination(seed):
                   conv_b=W.bits(cv.bias) if r.integers(2) else None, pool=pool,
                   strides=conv_pool_layout(S, H, RQ + 2, dim_first), rows=rows, pending=pending,
                   label=f"conv combination {seed}: {c}", **kw)
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_commit_combination(seed):
+    """kda_commit over random layer counts (up to 18, more than one launch),
+    windows, pool types, padded per-layer strides, in-place or src -> dst,
+    boundaries, record rows and lengths (0, negative, above the window)."""
+    from _kda_cases import run_commit_case
+    r = np.random.default_rng(10000 + seed)
+    L = int(r.choice([1, 1, 2, 3, 5, 17, 18]))
+    H = int(r.integers(1, 4))
+    B = int(r.integers(1, 8))
+    Q = int(r.integers(1, 9))
+    bf16 = bool(r.integers(2))
+    inplace = bool(r.integers(2))
+    align = bool(r.integers(2))
+    S = 3 * B + 2
+    page = H * V * K
+    g = W._gen(11000 + seed)
+    strides = [page + 8 * int(r.integers(0, 20)) for _ in range(L)]
+    dt = torch.bfloat16 if bf16 else torch.float32
+    states, corrs, kgs = [], [], []
+    for l in range(L):
+        st = W.draw_state(12000 + seed * 32 + l, S * strides[l], dt)
+        states.append(W.bits(st) if bf16 else st.numpy().copy())
+        c, k = W.draw_records(g, B, H, Q)
+        corrs.append(c.numpy().copy())
+        kgs.append(W.bits(k))
+    a_log, dtb = W.draw_gate_params(g, L, H)
+    perm = r.permutation(np.arange(1, S)).astype(np.int32)
+    src = perm[:B].copy()
+    dst = src.copy() if inplace else perm[B:2 * B].copy()
+    bnd = perm[2 * B:3 * B].copy()
+    for b in range(B):
+        if r.random() < 0.15:
+            src[b] = 0
+        if r.random() < 0.25:
+            bnd[b] = 0
+    lens = r.integers(-1, Q + 3, B).astype(np.int32)
+    blen = r.integers(-1, Q + 3, B).astype(np.int32)
+    rows = None
+    if r.integers(2):
+        rows = r.permutation(B).astype(np.int32)
+        for b in range(B):
+            if r.random() < 0.15:
+                rows[b] = -1
+    run_commit_case(H=H, B=B, Q=Q, bf16=bf16, layers_state=states, strides=strides,
+                    corr_layers=corrs, kg_layers=kgs, a_log=a_log.numpy(), dt_bias=dtb.numpy(),
+                    src=src, lens=lens, dst=dst, bnd=bnd if align else None,
+                    blen=blen if align else None, rows=rows,
+                    label=f"commit combination {seed}: L={L} H={H} B={B} Q={Q} bf16={bf16} "
+                          f"inplace={inplace} align={align}")

@@ -61,6 +61,10 @@ def parse_args():
     ap.add_argument("--conv", action="store_true",
                     help="run the fused step with its convolution prologue (q, k, v from "
                          "packed pre-activations and a window pool)")
+    ap.add_argument("--conv-layout", choices=("dim_first", "window_major"), default="dim_first",
+                    help="window pool layout with --conv: [slot][3HK][RQ+2] (each channel's "
+                         "window contiguous) or [slot][RQ+2][3HK] (each window entry a "
+                         "contiguous row of channels)")
     ap.add_argument("--gate-proj", action="store_true",
                     help="compute raw_g in the step with kda_gate_projection (F_A a column "
                          "slice of packed projection rows, F_B [H*128, 128])")
@@ -103,7 +107,7 @@ def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False, es=4, 
     gated output stage reads q*256 B of gates per live item; es is the state
     element size. With the convolution prologue, q, k, v are read as the same
     bytes of pre-activations, plus each live item's windows (3*128 channels,
-    RQ + 2 values read, q + 2 written, BF16) and the weights once."""
+    the 3 taps read, q + 2 values written, BF16) and the weights once."""
     page = V * K * es
     state = total = 0
     for b in range(len(slots)):
@@ -118,7 +122,7 @@ def fused_bytes(slots, rows, pending, T, RQ, H, null_slot=0, gated=False, es=4, 
         t += T * (3 * K * 2 + V * 2) + T * 2        # q, k, raw_g, v, raw_beta
         t += T * V * 2                              # o
         t += T * V * 2 if gated else 0              # gate
-        t += (3 * K * (RQ + 2) * 2 + 3 * K * (T + 2) * 2) if conv else 0  # windows
+        t += (3 * K * 3 * 2 + 3 * K * (T + 2) * 2) if conv else 0  # windows
         state += H * s
         total += H * t
     if conv:
@@ -403,10 +407,15 @@ def main():
     conv = None
     if args.conv:
         cv = W.draw_conv_inputs(W._gen(4 + 300), B, T, H, RQ, w.slots)
-        conv = dict(x=cv.x.to(dev), pitch=cv.pitch, weight=cv.weight.to(dev),
-                    bias=cv.bias.to(dev), pool=cv.window.to(dev).reshape(-1))
         hk3 = 3 * H * K
-        conv["strides"] = (hk3 * (RQ + 2), RQ + 2, 1)
+        window = cv.window  # [slots, 3HK, RQ + 2]
+        if args.conv_layout == "window_major":
+            window = window.transpose(1, 2).contiguous()
+            strides = (hk3 * (RQ + 2), 1, hk3)
+        else:
+            strides = (hk3 * (RQ + 2), RQ + 2, 1)
+        conv = dict(x=cv.x.to(dev), pitch=cv.pitch, weight=cv.weight.to(dev),
+                    bias=cv.bias.to(dev), pool=window.to(dev).reshape(-1), strides=strides)
     gp = None
     if args.gate_proj:
         hk = H * K
@@ -556,6 +565,7 @@ def main():
             "gated_output": bool(args.gated_output),
             "state_dtype": args.state_dtype,
             "conv_prologue": bool(args.conv),
+            "conv_layout": args.conv_layout if args.conv else None,
             "gate_projection": bool(args.gate_proj),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),

@@ -10,7 +10,7 @@ static hipError_t launch_t(const VerifyParams& p, int tokens, dim3 grid, hipStre
   switch (tokens) {
 #define KDA_VERIFY_CASE(TT)                                                                   \
   case TT:                                                                                   \
-    hipLaunchKernelGGL((verify_kernel<TT, FUSED, GATED, SB16, false>), grid, dim3(256), 0,   \
+    hipLaunchKernelGGL((verify_kernel<TT, FUSED, GATED, SB16, CONV_NONE>), grid, dim3(256), 0, \
                        stream, p);                                                           \
     break;
     KDA_VERIFY_CASE(1)

@@ -182,82 +182,117 @@ __device__ __forceinline__ void conv_silu(const float (&seq)[3 + T], const float
   }
 }
 
-// c ? a : b for a wave-uniform c, as one opaque v_cndmask: a plain select
-// between two array elements would be folded into an indexed access, which
-// forces the array out of registers.
-__device__ __forceinline__ uint32_t uniform_pick(uint64_t mask, uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(mask));
-  return r;
-}
+// Window pool layouts of the convolution prologue: any strides, or packed
+// dim-first windows (tap stride 1, channel stride W = RQ + 2, slot stride a
+// multiple of 8 elements, 16-byte aligned base). In the packed layout the
+// windows of a wave's 64 channels are one contiguous block of 128 W bytes,
+// which the wave moves with 16-byte accesses through LDS.
+constexpr int CONV_NONE = 0, CONV_STRIDED = 1, CONV_PACKED = 2;
+constexpr int CONV_BLOCK = 64 * (MAX_T + 2) * 2;  // LDS bytes of one wave's block, W <= MAX_T + 2
 
-// The window's 3 taps at a wave-uniform offset off in 0..MAX_T-1 (entries
-// loaded as raw bits, index i at position i): a barrel shift by the bits of
-// off, each stage a choice between two constant positions.
-__device__ __forceinline__ void window_taps(const uint32_t (&wn)[MAX_T + 2], int off,
-                                            uint32_t (&taps)[3]) {
-  static_assert(MAX_T == 8, "three shift stages cover offsets 0..7");
-  const int o = __builtin_amdgcn_readfirstlane(off);
-  const uint64_t m4 = (o & 4) ? ~0ull : 0ull, m2 = (o & 2) ? ~0ull : 0ull,
-                 m1 = (o & 1) ? ~0ull : 0ull;
-  uint32_t s1[6], s2[4];
-#pragma unroll
-  for (int j = 0; j < 6; ++j) s1[j] = uniform_pick(m4, wn[j + 4], wn[j]);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) s2[j] = uniform_pick(m2, s1[j + 2], s1[j]);
-#pragma unroll
-  for (int j = 0; j < 3; ++j) taps[j] = uniform_pick(m1, s2[j + 1], s2[j]);
-}
-
-// One channel's convolution operands as raw BF16 bits: the window entries
-// (index i at position i, clamped to the window so every load is in bounds),
-// the T inputs, the 4 weights and the bias.
+// One channel's convolution operands as raw BF16 bits: the T inputs, the 4
+// weights and the bias; strided layout: the 3 window taps at the item's
+// offset; packed layout: the wave's window block, 16-byte chunks lane and
+// lane + 64 (clamped to the last chunk).
 template <int T>
 struct ConvIn {
-  uint32_t win[MAX_T + 2];
+  uint32_t tap[3];
+  u32x4 blk[2];
   uint32_t x[T];
   uint32_t w[4];
   uint32_t bias;
 };
 
-// Loads of channel col (= part * H*K + head channel) of the conv operands.
-template <int T>
+// Loads of channel col (= part * H*K + head channel) of the conv operands. The
+// taps start at the wave-uniform offset off = max(n - 1, 0) <= RQ - 1, so the
+// last one, off + 2 <= RQ + 1, lies inside the window of RQ + 2 entries. The
+// inputs, weights and bias do not depend on n and are issued first.
+template <int T, int MODE>
 __device__ __forceinline__ void conv_load(const VerifyParams& p, ConvIn<T>& ci, int slot,
                                           int64_t col, int64_t head_row, int part,
-                                          int64_t dim, int64_t tok0) {
-  const uint16_t* wp = p.conv + (int64_t)slot * p.conv_ss + col * p.conv_cs;
-#pragma unroll
-  for (int i = 0; i < MAX_T + 2; ++i)
-    ci.win[i] = wp[(int64_t)(i < p.rq + 2 ? i : p.rq + 1) * p.conv_ts];
+                                          int64_t dim, int64_t tok0, int off) {
 #pragma unroll
   for (int t = 0; t < T; ++t) ci.x[t] = p.x[(tok0 + t) * p.x_stride + col];
 #pragma unroll
   for (int i = 0; i < 4; ++i) ci.w[i] = p.conv_w[(part * 4 + i) * dim + head_row];
-  ci.bias = p.conv_b != nullptr ? p.conv_b[col] : 0u;
+  // Unconditional (without a bias, from the weights, col < 3HK <= 12HK, then
+  // dropped): a load under a branch ends in a wait for every load before it.
+  const bool has_bias = p.conv_b != nullptr;
+  const uint32_t braw = (has_bias ? p.conv_b : p.conv_w)[col];
+  ci.bias = has_bias ? braw : 0u;
+  if constexpr (MODE == CONV_PACKED) {
+    // The block of channels col0 .. col0 + 63 (col0 = col rounded down to 64:
+    // a wave's channels), 8 W chunks of 16 bytes.
+    const int W = p.rq + 2;
+    const int nchunk = 8 * W;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const u32x4* bp = reinterpret_cast<const u32x4*>(
+        p.conv + (int64_t)slot * p.conv_ss + (col & ~(int64_t)63) * W);
+    ci.blk[0] = bp[lane < nchunk ? lane : nchunk - 1];
+    ci.blk[1] = bp[lane + WAVE < nchunk ? lane + WAVE : nchunk - 1];
+  } else {
+    const uint16_t* wp = p.conv + (int64_t)slot * p.conv_ss + col * p.conv_cs;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) ci.tap[i] = wp[(int64_t)(off + i) * p.conv_ts];
+  }
 }
 
-// The channel's taps at the offset, its convolution + SiLU (BF16 bits into y),
-// then the window write-back [tap 1, tap 2, x_0 .. x_{T-1}]: the thread
-// rewrites only entries of its own channel, which it has read.
-template <int T>
+// Orders one wave's LDS accesses across its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The window write-back [tap 1, tap 2, x_0 .. x_{T-1}] (entries past T + 1 keep
+// their values; the thread rewrites only entries of its own channel), then the
+// channel's convolution + SiLU (BF16 bits into y). Storing first lets the raw
+// bits die as they are converted. Packed layout: the block goes to the wave's
+// LDS area blk_s (CONV_BLOCK bytes), each lane reads its taps there and writes
+// its new entries back, and the wave stores the whole block.
+template <int T, int MODE>
 __device__ __forceinline__ void conv_part(const VerifyParams& p, const ConvIn<T>& ci, int slot,
-                                          int64_t col, int off, uint32_t (&y)[T]) {
-  uint32_t taps[3];
-  window_taps(ci.win, off, taps);
+                                          int64_t col, int off, uint8_t* blk_s,
+                                          uint32_t (&y)[T]) {
+  uint32_t tap[3];
+  if constexpr (MODE == CONV_PACKED) {
+    const int W = p.rq + 2;
+    const int nchunk = 8 * W;
+    const int lane = threadIdx.x & (WAVE - 1);
+    u32x4* const bs = reinterpret_cast<u32x4*>(blk_s);
+    if (lane < nchunk) bs[lane] = ci.blk[0];
+    if (lane + WAVE < nchunk) bs[lane + WAVE] = ci.blk[1];
+    wave_lds_sync();
+    uint16_t* const mine = reinterpret_cast<uint16_t*>(blk_s) + (col & 63) * W;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) tap[i] = mine[off + i];
+    mine[0] = (uint16_t)tap[1];
+    mine[1] = (uint16_t)tap[2];
+#pragma unroll
+    for (int t = 0; t < T; ++t) mine[2 + t] = (uint16_t)ci.x[t];
+    wave_lds_sync();
+    u32x4* const bp = reinterpret_cast<u32x4*>(
+        p.conv + (int64_t)slot * p.conv_ss + (col & ~(int64_t)63) * W);
+    if (lane < nchunk) bp[lane] = bs[lane];
+    if (lane + WAVE < nchunk) bp[lane + WAVE] = bs[lane + WAVE];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) tap[i] = ci.tap[i];
+    uint16_t* wp = p.conv + (int64_t)slot * p.conv_ss + col * p.conv_cs;
+    wp[0] = (uint16_t)tap[1];
+    wp[p.conv_ts] = (uint16_t)tap[2];
+#pragma unroll
+    for (int t = 0; t < T; ++t) wp[(int64_t)(2 + t) * p.conv_ts] = (uint16_t)ci.x[t];
+  }
   float seq[3 + T];
   float w[4];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) seq[i] = bf16_bits_to_f32(taps[i]);
+  for (int i = 0; i < 3; ++i) seq[i] = bf16_bits_to_f32(tap[i]);
 #pragma unroll
   for (int t = 0; t < T; ++t) seq[3 + t] = bf16_bits_to_f32(ci.x[t]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = bf16_bits_to_f32(ci.w[i]);
   conv_silu<T>(seq, w, bf16_bits_to_f32(ci.bias), y);
-  uint16_t* wp = p.conv + (int64_t)slot * p.conv_ss + col * p.conv_cs;
-  wp[0] = (uint16_t)taps[1];
-  wp[p.conv_ts] = (uint16_t)taps[2];
-#pragma unroll
-  for (int t = 0; t < T; ++t) wp[(int64_t)(2 + t) * p.conv_ts] = (uint16_t)ci.x[t];
 }
 
 // First key channel of lane group g (= lane / 16) in tile cb: values i = 0..3
@@ -267,7 +302,7 @@ __device__ __forceinline__ constexpr int chan0(int cb, int g) {
   return SB16 ? 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) : 16 * cb + 4 * g;
 }
 
-template <int T, bool FUSED, bool GATED, bool SB16, bool CONV>
+template <int T, bool FUSED, bool GATED, bool SB16, int CONV>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   static_assert(FUSED || !CONV, "the convolution prologue is a fused-step prologue");
   using PI = Pairs<T>;
@@ -330,10 +365,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
   const bool balign = me > 0;
 
-  // BF16 pages without the convolution: LDS bounds the occupancy, so x_s (read
-  // only in the state pass) and dots_s (written after it, behind a barrier)
-  // share their 8 KiB. Elsewhere the registers bound it and they stay apart.
-  constexpr bool kShareXD = SB16 && !CONV;
+  // BF16 pages: LDS bounds the occupancy, so x_s (read only in the state pass)
+  // and dots_s (written after it, behind a barrier) share their 8 KiB. With
+  // FP32 pages the registers bound it and they stay apart.
+  constexpr bool kShareXD = SB16;
   __shared__ __attribute__((aligned(16))) float x_s[16][K];  // Gamma_t kn_t | Gamma_t q_t | 0
   __shared__ __attribute__((aligned(16))) float dots_own[kShareXD ? 1 : V][16];
   float (*const dots_s)[16] =
@@ -376,10 +411,17 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   uint32_t kb[T], gb[T], qb[T];  // lower: new raw key, gate, q bits
   uint32_t vb[T];                // upper: new v bits
   // Convolution prologue: per part this thread convolves (lower: q, k; upper:
-  // v), the window entries (clamped to the window, so every load is in bounds),
-  // the T inputs, the 4 weights and the bias, all as raw BF16 bits.
+  // v), the 3 taps at the replay-aware offset (after n accepted tokens they
+  // start at n - 1; n = 0 reads from 0), the T inputs, the 4 weights and the
+  // bias, all as raw BF16 bits.
   ConvIn<T> cin0, cin1;  // lower: q part, k part; upper: v part in cin0
   const int64_t dim = (int64_t)H * K;
+  const int conv_off = n > 0 ? n - 1 : 0;
+  // Packed window blocks stage through x_s, which is first written after the
+  // prologue's part one: areas 2w, 2w + 1 (q, k) of lower wave w, w + 2 (v) of
+  // upper wave w, 6 * CONV_BLOCK <= sizeof x_s.
+  uint8_t* const blk_s = reinterpret_cast<uint8_t*>(&x_s[0][0]);
+  static_assert(6 * CONV_BLOCK <= 16 * K * sizeof(float), "window blocks fit in x_s");
   uint32_t okb[MAX_T], ogb[MAX_T];
   float ou[MAX_T];
   uint32_t rbb = 0;
@@ -394,10 +436,17 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
                      ((int64_t)slot * p.slot_stride + (int64_t)h * PAGE) * ES;
   char* const tile0 = page + ((16 * (2 * wave) + lr) * K + LDC * lq) * ES;
   u32x4 st[2][NLD];
+  float kf[T], qf[T], dnew[T];
+  float okf[MAX_T], od[MAX_T];
+  // ---- 3. Prologue, part one: decays, key sums of squares, staging; with the
+  // convolution, first the window write-back and the convolution + SiLU (each
+  // thread touches only the window entries of its own channels). Each half's
+  // loads and part one form one branch, so no merge point holds both halves'
+  // loaded values at once.
   if (lower) {
     if constexpr (CONV) {
-      conv_load<T>(p, cin0, slot, 0 * dim + head_row, head_row, 0, dim, tok0);
-      conv_load<T>(p, cin1, slot, 1 * dim + head_row, head_row, 1, dim, tok0);
+      conv_load<T, CONV>(p, cin0, slot, 0 * dim + head_row, head_row, 0, dim, tok0, conv_off);
+      conv_load<T, CONV>(p, cin1, slot, 1 * dim + head_row, head_row, 1, dim, tok0, conv_off);
 #pragma unroll
       for (int t = 0; t < T; ++t) gb[t] = p.g[(tok0 + (t < L ? t : last)) * H * K + head_row];
     } else {
@@ -415,49 +464,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j)
         st[r][j] = *reinterpret_cast<const u32x4*>(tile0 + (16 * r * K + 4 * LDC * j) * ES);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int j = 0; j < NLD; ++j)
-        st[r][j] = *reinterpret_cast<const u32x4*>(tile0 + (16 * r * K + 4 * LDC * j) * ES);
     __builtin_amdgcn_sched_barrier(0);
+    const float ea = __expf(a_log_h);
     if constexpr (CONV) {
-      conv_load<T>(p, cin0, slot, 2 * dim + head_row, head_row, 2, dim, tok0);
-    } else {
-#pragma unroll
-      for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + (t < L ? t : last)) * H * V + head_row];
-    }
-    rbb = p.rb[(tok0 + (c < L ? c : last)) * H + h];  // unconditional: no divergent load
-    if constexpr (FUSED) {
-      const int64_t rbase = ((int64_t)(rec < 0 ? 0 : rec) * H + h) * p.rq;
-#pragma unroll
-      for (int t = 0; t < MAX_T; ++t) {
-        okb[t] = 0;
-        ogb[t] = 0;
-        ou[t] = 0.f;
-        if (t < n) {
-          okb[t] = p.kg[(rbase + t) * 2 * K + c];
-          ogb[t] = p.kg[(rbase + t) * 2 * K + K + c];
-          ou[t] = p.corr[(rbase + t) * V + c];
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 3. Prologue, part one: decays, key sums of squares, staging.
-  const float ea = __expf(a_log_h);
-  float kf[T], qf[T], dnew[T];
-  float okf[MAX_T], od[MAX_T];
-  // Convolution prologue: taps at the replay-aware offset, convolution + SiLU,
-  // then the window write-back (each thread rewrites only the entries of its
-  // own channels, which it has read).
-  const int conv_off = n > 0 ? n - 1 : 0;
-  if (lower) {
-    if constexpr (CONV) {
-      conv_part<T>(p, cin0, slot, 0 * dim + head_row, conv_off, qb);
-      conv_part<T>(p, cin1, slot, 1 * dim + head_row, conv_off, kb);
+      conv_part<T, CONV>(p, cin0, slot, 0 * dim + head_row, conv_off, blk_s + 2 * wave * CONV_BLOCK, qb);
+      conv_part<T, CONV>(p, cin1, slot, 1 * dim + head_row, conv_off,
+                         blk_s + (2 * wave + 1) * CONV_BLOCK, kb);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -473,7 +485,47 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       if (lane == 0) ssq_s[0][wave][t] = s;
     }
   } else {
-    if constexpr (CONV) conv_part<T>(p, cin0, slot, 2 * dim + head_row, conv_off, vb);
+    // The v part's convolution operands go before the page, so that its
+    // convolution runs while the page streams in.
+    if constexpr (CONV) {
+      conv_load<T, CONV>(p, cin0, slot, 2 * dim + head_row, head_row, 2, dim, tok0, conv_off);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        st[r][j] = *reinterpret_cast<const u32x4*>(tile0 + (16 * r * K + 4 * LDC * j) * ES);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!CONV) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + (t < L ? t : last)) * H * V + head_row];
+    }
+    rbb = p.rb[(tok0 + (c < L ? c : last)) * H + h];  // unconditional: no divergent load
+    if constexpr (CONV) {
+      // Before the record loads: their count depends on n, so a wait placed
+      // after them could not tell the convolution's operands from the page.
+      __builtin_amdgcn_sched_barrier(0);
+      conv_part<T, CONV>(p, cin0, slot, 2 * dim + head_row, conv_off, blk_s + (wave + 2) * CONV_BLOCK,
+                         vb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (FUSED) {
+      const int64_t rbase = ((int64_t)(rec < 0 ? 0 : rec) * H + h) * p.rq;
+#pragma unroll
+      for (int t = 0; t < MAX_T; ++t) {
+        okb[t] = 0;
+        ogb[t] = 0;
+        ou[t] = 0.f;
+        if (t < n) {
+          okb[t] = p.kg[(rbase + t) * 2 * K + c];
+          ogb[t] = p.kg[(rbase + t) * 2 * K + K + c];
+          ou[t] = p.corr[(rbase + t) * V + c];
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float ea = __expf(a_log_h);
 #pragma unroll
     for (int t = 0; t < T; ++t) v_s[t][c] = t < L ? bf16_bits_to_f32(vb[t]) : 0.f;
     if (c < T) beta_s[c] = c < L ? sigmoidf_fast(bf16_bits_to_f32(rbb)) : 0.f;
@@ -725,6 +777,45 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       }
     }
   }
+}
+
+// Launch of the fused replay+verify with the convolution prologue over window
+// layout MODE, for T = tokens, FP32 or BF16 pages, with or without the gated
+// output stage.
+template <int MODE>
+hipError_t launch_conv_mode(const VerifyParams& p, int tokens, bool bf16, int batch,
+                            hipStream_t stream) {
+  const dim3 grid(p.heads, batch);
+  const bool gated = p.gate != nullptr;
+  hipError_t err = hipSuccess;
+  auto launch = [&](auto t_tag, auto gated_tag, auto bf16_tag) {
+    constexpr int TT = decltype(t_tag)::value;
+    constexpr bool G = decltype(gated_tag)::value;
+    constexpr bool B = decltype(bf16_tag)::value;
+    hipLaunchKernelGGL((verify_kernel<TT, true, G, B, MODE>), grid, dim3(256), 0, stream, p);
+    err = hipGetLastError();
+  };
+  auto by_page = [&](auto t_tag) {
+    if (gated) {
+      if (bf16) launch(t_tag, std::true_type{}, std::true_type{});
+      else launch(t_tag, std::true_type{}, std::false_type{});
+    } else {
+      if (bf16) launch(t_tag, std::false_type{}, std::true_type{});
+      else launch(t_tag, std::false_type{}, std::false_type{});
+    }
+  };
+  switch (tokens) {
+    case 1: by_page(std::integral_constant<int, 1>{}); break;
+    case 2: by_page(std::integral_constant<int, 2>{}); break;
+    case 3: by_page(std::integral_constant<int, 3>{}); break;
+    case 4: by_page(std::integral_constant<int, 4>{}); break;
+    case 5: by_page(std::integral_constant<int, 5>{}); break;
+    case 6: by_page(std::integral_constant<int, 6>{}); break;
+    case 7: by_page(std::integral_constant<int, 7>{}); break;
+    case 8: by_page(std::integral_constant<int, 8>{}); break;
+    default: return hipErrorInvalidValue;
+  }
+  return err;
 }
 
 }  // namespace kda

@@ -229,11 +229,34 @@ def window_np(win: "W.Window"):
 
 # ---------------------------------------------------------------- fused + convolution
 
-def conv_pool_layout(S, H, W, dim_first=True):
-    """Strides (slot, channel, tap) of a [S, 3HK, W] (dim-first) or [S, W, 3HK]
-    (window-major) window pool, in elements."""
+CONV_LAYOUTS = ("dim_first", "window_major", "dim_first_padded", "dim_first_slot_pad")
+
+
+def conv_pool_layout(S, H, W, dim_first=True, layout=None):
+    """Strides (slot, channel, tap) of a window pool, in elements: [S, 3HK, W]
+    (dim-first, the packed layout) or [S, W, 3HK] (window-major); layout, when
+    given, also names 'dim_first_padded' (channel stride W + 1) and
+    'dim_first_slot_pad' (slot stride 3HK*W + 4, not a multiple of 8), which the
+    library serves with its strided code."""
     hk3 = 3 * H * K
-    return (hk3 * W, W, 1) if dim_first else (hk3 * W, 1, hk3)
+    layout = layout or ("dim_first" if dim_first else "window_major")
+    return {"dim_first": (hk3 * W, W, 1), "window_major": (hk3 * W, 1, hk3),
+            "dim_first_padded": (hk3 * (W + 1), W + 1, 1),
+            "dim_first_slot_pad": (hk3 * W + 4, W, 1)}[layout]
+
+
+def conv_pool_build(win, strides, seed):
+    """A flat uint16 pool holding win [S, 3HK, W] (window values as BF16 bits) at
+    the given strides; the elements no window covers hold seeded random bits,
+    so that a test can see them stay untouched."""
+    S, C, Wn = win.shape
+    ss, cs, ts = strides
+    n = (S - 1) * ss + (C - 1) * cs + (Wn - 1) * ts + 1
+    pool = np.random.default_rng(seed).integers(0, 1 << 16, n, dtype=np.uint16)
+    idx = (np.arange(S)[:, None, None] * ss + np.arange(C)[None, :, None] * cs +
+           np.arange(Wn)[None, None, :] * ts)
+    pool[idx] = win
+    return pool
 
 
 def conv_written(slots, H, RQ, T, strides, null_slot, n_elems):

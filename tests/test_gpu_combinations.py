@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import workloads as W
-from _kda_cases import conv_pool_layout, run_conv_case, run_verify_case, window_np
+from _kda_cases import (CONV_LAYOUTS, conv_pool_build, conv_pool_layout, run_conv_case,
+                        run_verify_case, window_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,9 +113,9 @@ def test_random_conv_combination(seed):
     blens = r.integers(0, RQ + 2, B).astype(np.int32)
     win = window_np(W.draw_window(g, B, T, H))
     cv = W.draw_conv_inputs(W._gen(9000 + seed), B, T, H, RQ, S)
-    dim_first = bool(r.integers(2))
-    pool = W.bits(cv.window)
-    pool = (pool if dim_first else pool.transpose(0, 2, 1)).reshape(-1).copy()
+    layout = CONV_LAYOUTS[int(r.integers(len(CONV_LAYOUTS)))]
+    strides = conv_pool_layout(S, H, RQ + 2, layout=layout)
+    pool = conv_pool_build(W.bits(cv.window), strides, 9700 + seed)
     kw = {}
     if c["gated"]:
         gate, weight, eps = W.draw_output_stage(W._gen(9500 + seed), B, T, H)
@@ -126,8 +127,8 @@ def test_random_conv_combination(seed):
                   raw_g=win["raw_g"], raw_beta=win["raw_beta"], x=W.bits(cv.x), pitch=cv.pitch,
                   conv_w=W.bits(cv.weight),
                   conv_b=W.bits(cv.bias) if r.integers(2) else None, pool=pool,
-                  strides=conv_pool_layout(S, H, RQ + 2, dim_first), rows=rows, pending=pending,
-                  label=f"conv combination {seed}: {c}", **kw)
+                  strides=strides, rows=rows, pending=pending,
+                  label=f"conv combination {seed}: {c} {layout}", **kw)
 
 
 @pytest.mark.parametrize("seed", list(range(24)))

@@ -10,8 +10,9 @@ import torch
 import oracle
 import workloads as W
 from _compare import assert_exact, assert_f32_close
-from _kda_cases import (DEV, announce, conv_pool_layout, dev, dev_bf16, np_of,
-                        run_commit_case, run_conv_case, run_verify_case, window_np)
+from _kda_cases import (CONV_LAYOUTS, DEV, announce, conv_pool_build, conv_pool_layout, dev,
+                        dev_bf16, np_of, run_commit_case, run_conv_case, run_verify_case,
+                        window_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -272,12 +273,13 @@ def test_gated_output_stage(T, fused, bf16):
 
 # ---------------------------------------------------------------- fused + convolution
 
-def _conv_case(seed, H, B, T, RQ, S, bf16=False, dim_first=True, null_rows=(), norec_rows=()):
+def _conv_case(seed, H, B, T, RQ, S, bf16=False, dim_first=True, null_rows=(), norec_rows=(),
+               layout=None):
     c = _vf_case(seed, H, B, T, RQ, S, null_rows=null_rows, norec_rows=norec_rows, bf16=bf16)
     cv = W.draw_conv_inputs(W._gen(seed + 7), B, T, H, RQ, S)
     win = W.bits(cv.window)  # [S, 3HK, RQ + 2]
-    c["strides"] = conv_pool_layout(S, H, RQ + 2, dim_first)
-    c["pool"] = (win if dim_first else win.transpose(0, 2, 1)).reshape(-1).copy()
+    c["strides"] = conv_pool_layout(S, H, RQ + 2, dim_first, layout)
+    c["pool"] = conv_pool_build(win, c["strides"], seed + 11)
     c.update(x=W.bits(cv.x), pitch=cv.pitch, conv_w=W.bits(cv.weight), conv_b=W.bits(cv.bias))
     return c
 
@@ -316,6 +318,20 @@ def test_fused_conv_every_pending_count(dim_first):
     for b in range(B):
         pending[c["rows"][b]] = b
     _run_conv(c, H, B, T, RQ, pending, "fused conv n=0..8", bias=False)
+
+
+@pytest.mark.parametrize("layout", CONV_LAYOUTS)
+@pytest.mark.parametrize("T,RQ,bf16", [(8, 8, False), (3, 8, True), (2, 3, False), (5, 6, True)])
+def test_fused_conv_pool_layouts(layout, T, RQ, bf16):
+    """Every window pool layout: the packed dim-first blocks (including windows
+    of 5 and 8 entries, whose blocks are not a whole number of 64 chunks) and
+    the strided forms, with the padding between windows left alone."""
+    H, B = 3, 6
+    c = _conv_case(950 + T + RQ, H, B, T, RQ, 9, bf16=bf16, null_rows=(2,), norec_rows=(4,),
+                   layout=layout)
+    pending = np.random.default_rng(T + RQ).integers(0, RQ + 1, B).astype(np.int32)
+    pending[c["rows"][0]] = RQ
+    _run_conv(c, H, B, T, RQ, pending, f"fused conv {layout} T={T} RQ={RQ}")
 
 
 @pytest.mark.parametrize("T,bf16", [(3, False), (8, False), (4, True)])

@@ -40,11 +40,13 @@ K = V = 128
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("large_decode", "commit", "fused", "align"),
+    ap.add_argument("--workload", choices=("large_decode", "commit", "fused", "align", "verify"),
                     default="large_decode",
                     help="large_decode (default): the whole step on the large decode batch; "
                          "commit / fused / align: that kernel alone on the BF16 commit, "
-                         "fused replay+verify and 8-layer align commit workloads")
+                         "fused replay+verify and 8-layer align commit workloads; verify: "
+                         "the stock verify alone on the large decode batch (pool type from "
+                         "--state-dtype)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -291,6 +293,35 @@ def bench_kernel_workload(args):
                     if L == 1 else
                     "align_commit: L=8 H=32 B=256 window 8, BF16 pools of 641 slots, "
                     "128 boundary stores")
+        dtype = "f32"
+    elif args.workload == "verify":
+        w = W.config4(device=dev)
+        a = w.arrays
+        H, B, T, RQ = w.heads, w.batch, w.tokens, w.record_tokens
+        bf16 = args.state_dtype == "bf16"
+        state = a.pop("state")
+        if bf16:
+            state = state.to(torch.bfloat16)
+            torch.cuda.empty_cache()
+        slots, rows = i32(a["state_indices"]), i32(a["record_rows"])
+        corr, kg = a["corr"].to(dev), a["kg"].to(dev)
+        a_log, dt_bias = a["a_log"][0].contiguous().to(dev), a["dt_bias"][0].contiguous().to(dev)
+        new = w.windows["new"].to(dev)
+        out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=dev)
+        launch = lambda: kda.kda_verify(
+            heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v, raw_g=new.raw_g,
+            raw_beta=new.raw_beta, a_log=a_log, dt_bias=dt_bias, lower_bound=w.lower_bound,
+            state=state, state_slot_stride=H * V * K, state_indices=slots, corr=corr, kg=kg,
+            record_tokens=RQ, record_rows=rows, out=out)
+        # The stock verify moves the fused step's bytes with no replay: pages
+        # read, inputs, o and the new records.
+        st, tot = fused_bytes(a["state_indices"].numpy(), a["record_rows"].numpy(),
+                              np.zeros(B, np.int32), T, RQ, H, es=2 if bf16 else 4)
+        items = B * H
+        name = f"kda_verify ({'BF16' if bf16 else 'FP32'})"
+        workload = ("verify: the large decode batch, L=1 H=64 K=V=128 B=512 q=8, "
+                    f"{'BF16' if bf16 else 'FP32'} state 512 slots, ~5% no-op rows; the stock "
+                    "verify alone (reads the pages, writes o and the records)")
         dtype = "f32"
     else:  # fused
         w = W.config2(device=dev)

@@ -251,7 +251,12 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
  *                        must not overlap. Dim-first [slots][3*heads*128][W]:
  *                        strides (3*heads*128*W, W, 1); window-major
  *                        [slots][W][3*heads*128]: (3*heads*128*W, 1, 3*heads*128);
- *                        W >= record_tokens + 2
+ *                        W >= record_tokens + 2. A dim-first pool with
+ *                        W = record_tokens + 2 (tap stride 1, channel stride W),
+ *                        a slot stride that is a multiple of 8 and a 16-byte
+ *                        aligned base is moved in 16-byte chunks, each wave's
+ *                        64 windows as one block; other pools use 2-byte
+ *                        accesses
  *   q_scale              finite (the pages use 128^-1/2)
  *   raw_g, raw_beta, a_log, dt_bias, lower_bound, state_dtype, state,
  *   state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,

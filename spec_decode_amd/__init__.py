@@ -270,7 +270,8 @@ def kda_fused_conv_replay_verify(*, heads: int, tokens: int, batch: int, x, x_ro
                     (boundaries, "boundaries"), (boundary_lens, "boundary_lens")):
         _need(t, batch, name)
     _check(_lib.kda_fused_conv_replay_verify(
-        heads, tokens, batch, _ptr_rows(x, bf, int(x_row_stride), "x"), int(x_row_stride), _ptr(conv_weight, bf, "conv_weight"),
+        heads, tokens, batch, _ptr_rows(x, bf, int(x_row_stride), "x"), int(x_row_stride),
+        _ptr(conv_weight, bf, "conv_weight"),
         _ptr(conv_bias, bf, "conv_bias"), _ptr(conv_state, bf, "conv_state"),
         int(conv_slot_stride), int(conv_channel_stride), int(conv_tap_stride),
         float(q_scale), _ptr(raw_g, bf, "raw_g"), _ptr(raw_beta, bf, "raw_beta"),

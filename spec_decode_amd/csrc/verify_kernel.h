@@ -1,6 +1,7 @@
 // The verify kernel template: fused replay+verify and the stock verify over
 // FP32 or BF16 state pages, with the optional convolution prologue and gated
-// RMSNorm output stage. Instantiated by fused.hip and fused_conv.hip.
+// RMSNorm output stage. Instantiated by fused.hip, fused_conv.hip and
+// fused_conv_packed.hip.
 //
 // Method (the vLLM page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.
 // kda.fused", module docstring and KdaFused): per (request, head) item,
@@ -36,7 +37,9 @@
 // S_n is stored rounded to nearest even; the verify continues from the FP32
 // value, before that rounding.
 //
-// Convolution prologue (fused page, KdaFused.kernel; template flag CONV): q, k
+// Convolution prologue (fused page, KdaFused.kernel; template argument CONV, 0
+// without it, 1 for window pools of any strides, 2 for packed dim-first pools
+// whose per-wave window blocks move as 16-byte chunks through LDS): q, k
 // and v are computed in the kernel from a packed row x of pre-activations, each
 // channel's 4-tap causal convolution over its window in the conv pool followed
 // by SiLU. The window holds the previous step's [2 history values, its T
@@ -53,8 +56,10 @@
 // the new tokens (decays, key norms, Gamma, X, the T^2 pair products reduced
 // over channels by a transposing wave reduction); threads 128..255 do the old
 // records (decays, norms, kp_t = kn_t * prod_{t<s<n} d_s, D_n), the
-// corrections, v and beta. The small loads are issued before the page loads so
-// that the in-order return of loads lets the prologue start early.
+// corrections, v and beta. Loads return in order, so threads 0..127 issue their
+// small loads before the page and start the prologue while it streams in;
+// threads 128..255 issue the page first (their records are needed later), with
+// the convolution's v operands ahead of it.
 #pragma once
 
 #include <type_traits>
@@ -138,7 +143,8 @@ __device__ __forceinline__ void pair_stage_one(const float (&kn)[T], const float
   if constexpr (PS::STEPS >= 2) quad_transpose_step<PS::P2 / 2, 2>(pv);
   // Lane l now holds, in slot i, pair i + R*(bit1 of l) + 2R*(bit0 of l)
   // (only the bits the steps used), summed over its 2^STEPS lanes.
-  const int sel = PS::STEPS == 2 ? ((lane & 1) * 2 + ((lane >> 1) & 1)) : (PS::STEPS == 1 ? (lane & 1) : 0);
+  const int sel = PS::STEPS == 2 ? ((lane & 1) * 2 + ((lane >> 1) & 1))
+                  : (PS::STEPS == 1 ? (lane & 1) : 0);
   const int group = wave * (64 >> PS::STEPS) + (lane >> PS::STEPS);
 #pragma unroll
   for (int i = 0; i < PS::R; ++i) part[(i + PS::R * sel) * PS::PARTS + group] = pv[i];
@@ -384,8 +390,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   __shared__ float ssq_s[2][2][MAX_T];  // [new | old keys][wave of the half][token]
   __shared__ float qsq_s[2][MAX_T];     // convolution prologue: q sums of squares
   __shared__ float beta_s[MAX_T];
-  __shared__ uint32_t kg_s[T][K];
-  __shared__ float osq_s[2][T];  // output stage: per-wave sums of o_bf^2  // raw key | raw gate << 16 of the window, for the records
+  __shared__ uint32_t kg_s[T][K];  // raw key | raw gate << 16 of the window, for the records
+  __shared__ float osq_s[2][T];    // output stage: per-wave sums of o_bf^2
 
   const int c = tid & (K - 1);   // channel / state row of this thread's half
   const bool lower = wave < 2;   // threads 0..127: new tokens; 128..255: records, v, beta
@@ -467,7 +473,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     __builtin_amdgcn_sched_barrier(0);
     const float ea = __expf(a_log_h);
     if constexpr (CONV) {
-      conv_part<T, CONV>(p, cin0, slot, 0 * dim + head_row, conv_off, blk_s + 2 * wave * CONV_BLOCK, qb);
+      conv_part<T, CONV>(p, cin0, slot, 0 * dim + head_row, conv_off,
+                         blk_s + 2 * wave * CONV_BLOCK, qb);
       conv_part<T, CONV>(p, cin1, slot, 1 * dim + head_row, conv_off,
                          blk_s + (2 * wave + 1) * CONV_BLOCK, kb);
     }

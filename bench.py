@@ -40,13 +40,15 @@ K = V = 128
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=("large_decode", "commit", "fused", "align", "verify"),
+    ap.add_argument("--workload",
+                    choices=("large_decode", "commit", "fused", "align", "verify", "decay"),
                     default="large_decode",
                     help="large_decode (default): the whole step on the large decode batch; "
                          "commit / fused / align: that kernel alone on the BF16 commit, "
                          "fused replay+verify and 8-layer align commit workloads; verify: "
                          "the stock verify alone on the large decode batch (pool type from "
-                         "--state-dtype)")
+                         "--state-dtype); decay: kda_decay on the large decode batch's raw "
+                         "gates")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -305,6 +307,24 @@ def bench_kernel_workload(args):
                     "align_commit: L=8 H=32 B=256 window 8, BF16 pools of 641 slots, "
                     "128 boundary stores")
         dtype = "f32"
+    elif args.workload == "decay":
+        w = W.config4(device=dev)
+        a = w.arrays
+        H, B, T = w.heads, w.batch, w.tokens
+        raw_g = w.windows["new"].raw_g.to(dev)  # [B*T, H, 128] BF16
+        a_log, dt_bias = a["a_log"][0].contiguous().to(dev), a["dt_bias"][0].contiguous().to(dev)
+        del a["state"]
+        torch.cuda.empty_cache()
+        out = torch.empty(raw_g.shape, dtype=torch.float32, device=dev)
+        launch = lambda: kda.kda_decay(raw_g, a_log, dt_bias, w.lower_bound, out)
+        n = raw_g.numel()
+        st = 0  # no state bytes: value is the total rate
+        tot = n * 2 + n * 4 + H * 4 + H * K * 4  # BF16 in, FP32 out, parameters
+        items = B * H
+        name = "kda_decay"
+        workload = ("decay: the large decode batch's new raw gates, 4096 tokens x 64 heads x 128 "
+                    "channels, BF16 -> FP32")
+        dtype = "f32"
     elif args.workload == "verify":
         w = W.config4(device=dev)
         a = w.arrays
@@ -391,7 +411,8 @@ def bench_kernel_workload(args):
     ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
     mean_ms = sum(ms) / len(ms)
     achieved = tot / (mean_ms * 1e-3) / 1e9
-    value = st / (mean_ms * 1e-3) / 1e9  # over the timed launches alone
+    # over the timed launches alone; a kernel with no state bytes reports its total rate
+    value = (st if st else tot) / (mean_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "state GB/s (% of HBM peak) + (req,head) items/s, KDA commit & fused verify",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -24,6 +24,13 @@ state bytes (pages read + pages written, from the actual plan) per second.
 ``roofline`` is the fused kernel's algorithmic bytes per launch over its mean
 event-timed duration, against 8 TB/s. ``cpu_baseline`` times the FP64 oracle on
 a sample of the same step on the host cores.
+
+Variants of the step: --state-dtype bf16, --gated-output, --conv (with
+--conv-layout), --gate-proj. --workload commit|fused|align|verify|decay times
+one kernel alone on its own workload instead; before each of those launches,
+outside its events, a 1 GiB scratch read evicts the 256 MB MALL (--no-evict to
+skip), and ``value`` is the kernel's state rate (its total rate when it moves
+no state).
 """
 import argparse
 import hashlib

@@ -99,6 +99,24 @@ def source_digest(paths):
 FUSED_SOURCES = ["spec_decode_amd/csrc/fused.hip", "spec_decode_amd/csrc/verify_kernel.h",
                  "spec_decode_amd/csrc/kda_device.h"]
 COMMIT_SOURCES = ["spec_decode_amd/csrc/commit.hip", "spec_decode_amd/csrc/kda_device.h"]
+CONV_SOURCES = FUSED_SOURCES + ["spec_decode_amd/csrc/fused_conv.hip",
+                                "spec_decode_amd/csrc/fused_conv_packed.hip"]
+
+
+def fused_variant(args):
+    """Key in profiles/traffic.json and source files of the fused launch that a
+    large-decode run times: the default, or its variant."""
+    parts = []
+    if args.state_dtype == "bf16":
+        parts.append("bf16")
+    if args.gated_output:
+        parts.append("gated")
+    if args.conv:
+        parts.append("conv_" + args.conv_layout)
+    if args.gate_proj:
+        parts.append("gate_proj")
+    key = "/".join(["fused_replay_verify/large_decode"] + parts)
+    return key, (CONV_SOURCES if args.conv else FUSED_SOURCES)
 
 
 def measured_traffic(name, digest):
@@ -621,10 +639,8 @@ def main():
     commit_total = sum(c[1] for c in cb) / len(cb)
     commit_state = sum(c[0] for c in cb) / len(cb)
     achieved = fused_total / (fused_mean_ms * 1e-3) / 1e9
-    traffic = None
-    if not (bf16 or args.conv or args.gated_output or args.gate_proj):
-        traffic = measured_traffic("fused_replay_verify/large_decode",
-                                   source_digest(FUSED_SOURCES))
+    tkey, tsrc = fused_variant(args)
+    traffic = measured_traffic(tkey, source_digest(tsrc))
 
     result = {
         "metric": "state GB/s (% of HBM peak) + (req,head) items/s, KDA commit & fused verify",

@@ -113,11 +113,18 @@ __device__ __forceinline__ float pair_share(const float (&kn)[T], const float (&
   }
 }
 
-template <int T, int G0, int... Is>
-__device__ __forceinline__ void pair_group(float (&pv)[sizeof...(Is)], const float (&kn)[T],
-                                           const float (&q)[T], const float (&d)[T],
-                                           std::integer_sequence<int, Is...>) {
-  ((pv[Is] = pair_share<T, G0 + Is>(kn, q, d)), ...);
+// Pair products I and I + HALF folded by the first transposing step (lane pairs
+// l, l ^ 1): the lane keeps the one its bit 0 selects and adds its partner's
+// copy of it. Forming each pair just before it is folded keeps only HALF
+// partial sums live instead of all the products.
+template <int T, int HALF, int I>
+__device__ __forceinline__ float pair_fold_first(const float (&kn)[T], const float (&q)[T],
+                                                 const float (&d)[T]) {
+  const float lo = pair_share<T, I>(kn, q, d);
+  const float hi = pair_share<T, I + HALF>(kn, q, d);
+  const float keep = lane_pick<LANES_BIT0>(hi, lo);
+  const float send = lane_pick<LANES_BIT0>(lo, hi);
+  return keep + dpp_f<DPP_XOR1>(send);
 }
 
 // The pair products summed over the 128 channels, stage one (lower waves, one
@@ -132,15 +139,19 @@ struct PairStage {
   static constexpr int PARTS = 128 >> STEPS;      // partials per pair (both waves)
 };
 
+// Is: 0 .. P2/2 - 1 (one fold per index) when there is a step, else just 0.
 template <int T, int... Is>
 __device__ __forceinline__ void pair_stage_one(const float (&kn)[T], const float (&q)[T],
                                                const float (&d)[T], int lane, int wave,
                                                float* part, std::integer_sequence<int, Is...>) {
   using PS = PairStage<T>;
   float pv[PS::P2];
-  ((pv[Is] = pair_share<T, Is>(kn, q, d)), ...);
-  if constexpr (PS::STEPS >= 1) quad_transpose_step<PS::P2, 1>(pv);
-  if constexpr (PS::STEPS >= 2) quad_transpose_step<PS::P2 / 2, 2>(pv);
+  if constexpr (PS::STEPS >= 1) {
+    ((pv[Is] = pair_fold_first<T, PS::P2 / 2, Is>(kn, q, d)), ...);
+    if constexpr (PS::STEPS >= 2) quad_transpose_step<PS::P2 / 2, 2>(pv);
+  } else {
+    pv[0] = pair_share<T, 0>(kn, q, d);
+  }
   // Lane l now holds, in slot i, pair i + R*(bit1 of l) + 2R*(bit0 of l)
   // (only the bits the steps used), summed over its 2^STEPS lanes.
   const int sel = PS::STEPS == 2 ? ((lane & 1) * 2 + ((lane >> 1) & 1))
@@ -373,7 +384,9 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 
   // BF16 pages: LDS bounds the occupancy, so x_s (read only in the state pass)
   // and dots_s (written after it, behind a barrier) share their 8 KiB. With
-  // FP32 pages the registers bound it and they stay apart.
+  // FP32 pages they stay apart: the fused FP32 instance fits 4 workgroups per
+  // CU in registers (128 VGPRs) but ran slower with them than with the 3 its
+  // LDS allows.
   constexpr bool kShareXD = SB16;
   __shared__ __attribute__((aligned(16))) float x_s[16][K];  // Gamma_t kn_t | Gamma_t q_t | 0
   __shared__ __attribute__((aligned(16))) float dots_own[kShareXD ? 1 : V][16];
@@ -576,17 +589,22 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     // A_ts, B_ts summed over the 128 channels: each wave reduces groups of G
     // values with the transposing exchange, then the two waves' sums meet in LDS.
     pair_stage_one<T>(kn, qf, dnew, lane, wave, &part_s[0][0],
-                      std::make_integer_sequence<int, PI::P2>{});
+                      std::make_integer_sequence<int, (PairStage<T>::STEPS >= 1 ? PI::P2 / 2
+                                                                                : 1)>{});
   } else {
     if constexpr (FUSED) {
       if (replay) {
         // Suffix products over the fold's stages: stage two (tokens me..n-1,
         // all n without align) into kp_s / dn_s, stage one (tokens 0..me-1)
         // into kpm_s / dm_s.
+        // Two halves, so that at most 8 of the 16 sums of squares are live
+        // next to the page.
         float knr[MAX_T];
 #pragma unroll
-        for (int t = 0; t < MAX_T; ++t)
+        for (int t = 0; t < MAX_T; ++t) {
+          if (t == MAX_T / 2) __builtin_amdgcn_sched_barrier(0);
           knr[t] = okf[t] * __builtin_amdgcn_rsqf(ssq_s[1][0][t] + ssq_s[1][1][t] + 1e-6f);
+        }
         float pp = 1.f;
 #pragma unroll
         for (int t = MAX_T - 1; t >= 0; --t) {

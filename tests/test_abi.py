@@ -197,3 +197,31 @@ def test_binding_rejects_short_per_request_arrays(lib):
     with pytest.raises(ValueError, match="state_indices"):
         kda.kda_defer_commit(batch=B, state_indices=i32(B - 2), commit_lens=i32(B),
                              record_rows=i32(B), pending=i32(B))
+
+
+def test_product_path_is_independent_of_the_oracle():
+    """The binding and the HIP sources never load or name the oracle, and the
+    oracle never names the HIP library: the two share no code (only the seeded
+    input generators in workloads/ serve both)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import spec_decode_amd; "
+            "print('oracle' in sys.modules, any(m.startswith('oracle') for m in sys.modules))"
+            % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert out.stdout.split() == ["False", "False"], out.stdout
+    imports = re.compile(r"^\s*(import|from)\s+(\w+)", re.M)
+    pkg = os.path.join(ROOT, "spec_decode_amd")
+    for base, _, files in os.walk(pkg):
+        if "_build" in base:
+            continue
+        for f in files:
+            if f.endswith((".py", ".hip", ".h")):
+                text = open(os.path.join(base, f)).read()
+                assert "oracle" not in {m[1] for m in imports.findall(text)}, f
+                assert "kda_o_" not in text and "libkda_oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "spec_decode_amd" not in {m[1] for m in imports.findall(text)}, f
+            assert "libkda.so" not in text, f

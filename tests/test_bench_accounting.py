@@ -1,0 +1,99 @@
+"""The benchmark's host-side accounting, checked on CPU: algorithmic bytes
+against hand counts of tiny plans, its plan simulation against the oracle's
+defer and flush-plan steps, the percentile helper, and the one-GPU rule."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_fused_bytes_hand_count():
+    b = _bench()
+    K = V = 128
+    H, T, RQ = 2, 3, 4
+    # request 0: null slot; 1: rec row -1 (no replay, no records);
+    # 2: pending 9 clamped to RQ = 4; 3: pending 0 (page read only).
+    slots = [0, 5, 6, 7]
+    rows = [0, -1, 1, 2]
+    pending = np.array([1, 9, 0], np.int32)  # by record row
+    st, tot = b.fused_bytes(slots, rows, pending, T, RQ, H)
+    page = V * K * 4
+    rec_tok = V * 4 + 2 * K * 2          # one token's correction + key/gate record
+    inputs = T * (3 * K * 2 + V * 2) + T * 2
+    out = T * V * 2
+    want_state = H * (page + (page + page) + page)
+    want_tot = (H * out                                   # null slot: zero outputs
+                + H * (page + inputs + out)                # no record row
+                + H * (2 * page + 4 * rec_tok + T * rec_tok + inputs + out)
+                + H * (page + T * rec_tok + inputs + out))
+    assert (st, tot) == (want_state, want_tot)
+    # BF16 pages halve the page terms; the gated stage adds T*256 B per live item.
+    st16, _ = b.fused_bytes(slots, rows, pending, T, RQ, H, es=2)
+    assert st16 == want_state // 2
+    _, tot_g = b.fused_bytes(slots, rows, pending, T, RQ, H, gated=True)
+    assert tot_g - tot == 3 * H * T * V * 2
+    # The convolution adds, per live item, the 3 taps read and T + 2 entries
+    # written for 3*128 channels, and the weights and bias once.
+    _, tot_c = b.fused_bytes(slots, rows, pending, T, RQ, H, conv=True)
+    assert tot_c - tot == 3 * H * (3 * K * 3 * 2 + 3 * K * (T + 2) * 2) + 3 * 4 * H * K * 2 + 3 * H * K * 2
+
+
+def test_commit_bytes_hand_count():
+    b = _bench()
+    K = V = 128
+    H, Q = 3, 4
+    slots = [0, 4, 5, 6, 7]
+    lens = [2, 0, 9, 1, 3]
+    rows = [0, 1, 2, -1, 3]
+    st, tot = b.commit_bytes(slots, lens, rows, H, Q)
+    page = V * K * 4
+    rec_tok = V * 4 + 2 * K * 2
+    # live: request 2 (n = 4 after the clamp) and request 4 (n = 3)
+    assert st == H * 2 * page * 2
+    assert tot == H * (2 * page + 4 * rec_tok) + H * (2 * page + 3 * rec_tok)
+
+
+def test_plan_simulation_matches_the_oracle():
+    import oracle
+    b = _bench()
+    rng = np.random.default_rng(3)
+    B, q, null = 40, 8, 0
+    slots = rng.integers(0, 30, B).astype(np.int32)
+    rows = rng.permutation(B).astype(np.int32)
+    rows[rng.random(B) < 0.2] = -1
+    pending0 = rng.integers(-2, q + 3, B).astype(np.int32)
+    accepted = rng.integers(0, q + 1, B).astype(np.int32)
+    sim = b.simulate_plan(slots, rows, pending0, accepted, 3, q, null)
+    pending = pending0.copy()
+    for fused_pending, lens in sim:
+        assert np.array_equal(np.asarray(fused_pending), pending)
+        commit_lens = accepted.copy()
+        oracle.defer(slots, commit_lens, rows, pending, null_slot=null)
+        flush = oracle.flush_plan(slots, rows, pending, q, null_slot=null)
+        assert list(flush[0]) == list(lens)
+
+
+def test_spread():
+    b = _bench()
+    assert b.spread([3.0]) == {"median_ms": 3.0, "p90_ms": 3.0}
+    assert b.spread(list(range(10, 0, -1))) == {"median_ms": 5, "p90_ms": 9}
+    assert b.spread(list(range(20))) == {"median_ms": 9, "p90_ms": 17}
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

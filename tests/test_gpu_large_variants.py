@@ -42,10 +42,10 @@ def _sample(seed, slots, rows, pending_row):
     return list(dict.fromkeys(R))
 
 
-def _compact(R, slots, rows, pending_row, corr, kg, pages):
+def _compact(R, slots, rows, pending_row, corr, kg, pages, state_dtype=np.float32):
     nR = len(R)
     page = H * V * K
-    m = dict(state=np.zeros((nR + 1) * page, np.float32),
+    m = dict(state=np.zeros((nR + 1) * page, state_dtype),
              slots=np.array([j + 1 if slots[b] > 0 else 0 for j, b in enumerate(R)], np.int32),
              rows=np.array([j if rows[b] >= 0 else -1 for j, b in enumerate(R)], np.int32),
              corr=np.zeros((nR, H, RQ, V), np.float32), kg=np.zeros((nR, H, RQ, 2 * K), np.uint16),
@@ -59,14 +59,15 @@ def _compact(R, slots, rows, pending_row, corr, kg, pages):
     return m
 
 
-def _check(label, R, m, m_out, g_out, g_pages, g_corr, g_kg, slots, rows, ulps):
+def _check(label, R, m, m_out, g_out, g_pages, g_corr, g_kg, slots, rows, ulps, bf16=False):
     page = H * V * K
+    close = assert_bf16_close if bf16 else assert_f32_close
     for j, b in enumerate(R):
         assert_bf16_close(f"{label} out request {b}", g_out[b * T:(b + 1) * T],
                           m_out[j * T:(j + 1) * T], ulps)
         if slots[b] > 0:
-            assert_f32_close(f"{label} page request {b}", g_pages(int(slots[b])),
-                             m["state"][(j + 1) * page:(j + 2) * page])
+            close(f"{label} page request {b}", g_pages(int(slots[b])),
+                  m["state"][(j + 1) * page:(j + 2) * page])
         if slots[b] > 0 and rows[b] >= 0:
             assert_f32_close(f"{label} corrections request {b}", g_corr[rows[b]], m["corr"][j])
             assert_exact(f"{label} key/gate request {b}", g_kg[rows[b]], m["kg"][j])
@@ -79,8 +80,9 @@ def _untouched(label, d_state, before, slots, rows, pending_row):
         if slots[b] > 0 and rows[b] >= 0 and min(pending_row[rows[b]], RQ) > 0:
             touched[int(slots[b])] = True
     keep = (~touched).nonzero().flatten().to(DEV)
-    assert torch.equal(d_state.view(S, page).index_select(0, keep).view(torch.int32),
-                       before.view(S, page).index_select(0, keep).view(torch.int32)), label
+    bits = torch.int16 if d_state.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(d_state.view(S, page).index_select(0, keep).view(bits),
+                       before.view(S, page).index_select(0, keep).view(bits)), label
 
 
 def test_large_decode_gated_output_sampled():
@@ -125,7 +127,8 @@ def test_large_decode_gated_output_sampled():
     torch.cuda.empty_cache()
 
 
-def test_large_decode_conv_prologue_packed_pool_sampled():
+@pytest.mark.parametrize("bf16", [False, True])
+def test_large_decode_conv_prologue_packed_pool_sampled(bf16):
     import spec_decode_amd as kda
     g, slots, rows, pending_row, a_log, dtb, corr, kg = _plan(940)
     page = H * V * K
@@ -134,11 +137,12 @@ def test_large_decode_conv_prologue_packed_pool_sampled():
     x, w_bits, b_bits = W.bits(cv.x), W.bits(cv.weight), W.bits(cv.bias)
     pool = W.bits(cv.window)  # [S, 3HK, RQ + 2]: the packed dim-first layout
     strides = conv_pool_layout(S, H, RQ + 2)
-    d_state = W.draw_state(942, S * page, torch.float32, DEV)
+    d_state = W.draw_state(942, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
     before = d_state.clone()
     d_corr, d_kg, d_pool = dev(corr), dev_bf16(kg), dev_bf16(pool.reshape(-1))
     out = torch.zeros((B * T, H * V), dtype=torch.bfloat16, device=DEV)
-    announce("large decode, convolution prologue, packed dim-first window pool")
+    announce(f"large decode, convolution prologue, packed dim-first window pool, "
+             f"{'BF16' if bf16 else 'FP32'} state pool")
     kda.kda_fused_conv_replay_verify(
         heads=H, tokens=T, batch=B, x=dev_bf16(x), x_row_stride=cv.pitch,
         conv_weight=dev_bf16(w_bits), conv_bias=dev_bf16(b_bits), conv_state=d_pool,
@@ -157,7 +161,8 @@ def test_large_decode_conv_prologue_packed_pool_sampled():
     R = _sample(943, slots, rows, pending_row)
     nR = len(R)
     m = _compact(R, slots, rows, pending_row, corr, kg,
-                 lambda sl: np_of(before[sl * page:(sl + 1) * page]))
+                 lambda sl: np_of(before[sl * page:(sl + 1) * page]),
+                 np.uint16 if bf16 else np.float32)
     m_pool = np.zeros((nR + 1, 3 * H * K, RQ + 2), np.uint16)
     for j, b in enumerate(R):
         if slots[b] > 0:
@@ -176,7 +181,7 @@ def test_large_decode_conv_prologue_packed_pool_sampled():
         state_indices=m["slots"], corr=m["corr"], kg=m["kg"], record_tokens=RQ,
         record_rows=m["rows"], pending=m["pend"], out=m_out)
     _check("conv", R, m, m_out, np_of(out), lambda sl: np_of(d_state[sl * page:(sl + 1) * page]),
-           np_of(d_corr), np_of(d_kg), slots, rows, 1)
+           np_of(d_corr), np_of(d_kg), slots, rows, 1, bf16)
     m_pool = flat.reshape(nR + 1, 3 * H * K, RQ + 2)
     for j, b in enumerate(R):
         if slots[b] > 0:

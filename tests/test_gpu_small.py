@@ -362,7 +362,8 @@ def _gate_proj_gpu(fa_bits, pitch, col0, fb_bits, N, H):
 
 
 @pytest.mark.parametrize("N,H,pitch,col0", [(1, 1, 128, 0), (17, 3, 136, 8), (64, 2, 128, 0),
-                                            (100, 3, 1000, 600), (257, 2, 264, 128)])
+                                            (100, 3, 1000, 600), (257, 2, 264, 128),
+                                            (130, 5, 256, 64), (129, 9, 128, 0)])
 def test_gate_projection_exact_grid(N, H, pitch, col0):
     """On the generator's exact grid every FP32 partial sum is exact, so the
     BF16 result is bit-identical to the oracle's."""

@@ -75,7 +75,6 @@ struct Pairs {
   static constexpr int NP = T * T;            // then B_ts, s <= t
   static constexpr int P2 = NP <= 1 ? 1 : NP <= 2 ? 2 : NP <= 4 ? 4 : NP <= 8 ? 8
                           : NP <= 16 ? 16 : NP <= 32 ? 32 : 64;
-  static constexpr int G = P2 < 16 ? P2 : 16;  // values reduced per exchange group
   __device__ static constexpr int a(int t, int s) { return t * (t - 1) / 2 + s; }
   __device__ static constexpr int b(int t, int s) { return NA + t * (t + 1) / 2 + s; }
 };
@@ -586,25 +585,26 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
 #pragma unroll
     for (int j = 2 * T; j < 16; ++j) x_s[j][c] = 0.f;
-    // A_ts, B_ts summed over the 128 channels: each wave reduces groups of G
-    // values with the transposing exchange, then the two waves' sums meet in LDS.
+    // A_ts, B_ts summed over the 128 channels: two transposing steps in
+    // registers (the first folds each pair as it is formed), then the two
+    // waves' partial sums meet in LDS.
     pair_stage_one<T>(kn, qf, dnew, lane, wave, &part_s[0][0],
                       std::make_integer_sequence<int, (PairStage<T>::STEPS >= 1 ? PI::P2 / 2
                                                                                 : 1)>{});
   } else {
     if constexpr (FUSED) {
       if (replay) {
-        // Suffix products over the fold's stages: stage two (tokens me..n-1,
-        // all n without align) into kp_s / dn_s, stage one (tokens 0..me-1)
-        // into kpm_s / dm_s.
-        // Two halves, so that at most 8 of the 16 sums of squares are live
-        // next to the page.
+        // The recorded keys' norms, in two halves, so that at most 8 of the 16
+        // sums of squares are live next to the page.
         float knr[MAX_T];
 #pragma unroll
         for (int t = 0; t < MAX_T; ++t) {
           if (t == MAX_T / 2) __builtin_amdgcn_sched_barrier(0);
           knr[t] = okf[t] * __builtin_amdgcn_rsqf(ssq_s[1][0][t] + ssq_s[1][1][t] + 1e-6f);
         }
+        // Suffix products over the fold's stages: stage two (tokens me..n-1,
+        // all n without align) into kp_s / dn_s, stage one (tokens 0..me-1)
+        // into kpm_s / dm_s.
         float pp = 1.f;
 #pragma unroll
         for (int t = MAX_T - 1; t >= 0; --t) {

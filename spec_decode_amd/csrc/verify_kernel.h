@@ -403,7 +403,6 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   __shared__ float qsq_s[2][MAX_T];     // convolution prologue: q sums of squares
   __shared__ float beta_s[MAX_T];
   __shared__ uint32_t kg_s[T][K];  // raw key | raw gate << 16 of the window, for the records
-  __shared__ float osq_s[2][T];    // output stage: per-wave sums of o_bf^2
 
   const int c = tid & (K - 1);   // channel / state row of this thread's half
   const bool lower = wave < 2;   // threads 0..127: new tokens; 128..255: records, v, beta
@@ -416,14 +415,20 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // then theirs (their prologue needs the records, which arrive after).
   const float a_log_h = p.a_log[h];
   const float dtb = p.dt_bias[head_row];
-  // Output stage inputs (compiled in only for the gated instances).
-  constexpr bool gated = GATED;
-  float nw = 1.f;
-  uint32_t gtb[T];
+  // Output stage inputs (compiled in only for the gated instances): wave w
+  // finishes tokens 2w and 2w + 1, each lane rows lane and lane + 64 of them.
+  float nw[2] = {1.f, 1.f};
+  uint32_t gtb[2][2];
   if constexpr (GATED) {
-    nw = p.norm_w[c];
 #pragma unroll
-    for (int t = 0; t < T; ++t) gtb[t] = p.gate[(tok0 + (t < L ? t : last)) * H * V + head_row];
+    for (int i = 0; i < 2; ++i) nw[i] = p.norm_w[lane + 64 * i];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = 2 * wave + j;
+      const int64_t row = (tok0 + (t < L ? t : last)) * H * V + (int64_t)h * V;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) gtb[j][i] = p.gate[row + lane + 64 * i];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   uint32_t kb[T], gb[T], qb[T];  // lower: new raw key, gate, q bits
@@ -746,7 +751,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   __syncthreads();
 
   // ---- 6. Per state row: the T x T forward substitution, outputs, records.
-  float ob[T];
+  // The gated output stage keeps the BF16-rounded o in kp_s, whose last reads
+  // were in the state pass.
+  float (*const ob_s)[V] = reinterpret_cast<float (*)[V]>(&kp_s[0][0]);
+  static_assert(MAX_T * K >= T * V, "o of the window fits in kp_s");
   if (lower) {
     const int vrow = c;
     float us[T];
@@ -770,9 +778,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       }
       if constexpr (GATED) {
         // The output stage normalises the BF16-rounded o over the head's rows.
-        ob[t] = bf16_bits_to_f32(f32_to_bf16_bits(o));
-        const float sq = wave_sum(ob[t] * ob[t]);
-        if (lane == 0) osq_s[wave][t] = sq;
+        ob_s[t][vrow] = bf16_bits_to_f32(f32_to_bf16_bits(o));
       } else {
         if (t < L) p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
       }
@@ -790,15 +796,21 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
   }
   if constexpr (GATED) {
+    // All four waves finish the output: wave w tokens 2w and 2w + 1, the
+    // sums of squares over the 128 rows by one wave reduction each.
     __syncthreads();
-    if (lower) {
-      const float inv_v = 1.0f / V;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float rstd =
-            __builtin_amdgcn_rsqf((osq_s[0][t] + osq_s[1][t]) * inv_v + p.norm_eps);
-        const float sg = sigmoidf_fast(bf16_bits_to_f32(gtb[t]));
-        if (t < L) p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(ob[t] * rstd * nw * sg);
+    for (int j = 0; j < 2; ++j) {
+      const int t = 2 * wave + j;  // uniform
+      if (t < L) {
+        const float x0 = ob_s[t][lane], x1 = ob_s[t][lane + 64];
+        const float ss = wave_sum(x0 * x0 + x1 * x1);
+        const float rstd = __builtin_amdgcn_rsqf(ss * (1.0f / V) + p.norm_eps);
+        uint16_t* const dst = p.out + (tok0 + t) * H * V + (int64_t)h * V;
+        dst[lane] = (uint16_t)f32_to_bf16_bits(x0 * rstd * nw[0] *
+                                               sigmoidf_fast(bf16_bits_to_f32(gtb[j][0])));
+        dst[lane + 64] = (uint16_t)f32_to_bf16_bits(x1 * rstd * nw[1] *
+                                                    sigmoidf_fast(bf16_bits_to_f32(gtb[j][1])));
       }
     }
   }

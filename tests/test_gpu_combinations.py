@@ -36,7 +36,7 @@ def _draw(seed):
                    align=bool(r.integers(2)), pad=int(r.integers(2)))
 
 
-@pytest.mark.parametrize("seed", list(range(48)))
+@pytest.mark.parametrize("seed", list(range(80)))
 def test_random_combination(seed):
     r, c = _draw(2000 + seed)
     T, RQ, H, B, bf16 = c["T"], c["RQ"], c["H"], c["B"], c["bf16"]
@@ -88,7 +88,7 @@ def test_random_combination(seed):
                     out_rows=out_rows, label=f"combination {seed}: {c}", **kw)
 
 
-@pytest.mark.parametrize("seed", list(range(16)))
+@pytest.mark.parametrize("seed", list(range(32)))
 def test_random_conv_combination(seed):
     r, c = _draw(6000 + seed)
     T, RQ, H, B, bf16 = c["T"], c["RQ"], c["H"], c["B"], c["bf16"]
@@ -131,7 +131,7 @@ def test_random_conv_combination(seed):
                   label=f"conv combination {seed}: {c} {layout}", **kw)
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
+@pytest.mark.parametrize("seed", list(range(32)))
 def test_random_commit_combination(seed):
     """kda_commit over random layer counts (up to 18, more than one launch),
     windows, pool types, padded per-layer strides, in-place or src -> dst,

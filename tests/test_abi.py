@@ -71,6 +71,8 @@ def test_rejects_bad_arguments_without_launch(lib):
     lib.kda_fused_replay_verify.restype = ctypes.c_int
     assert lib.kda_verify(*_verify_args(9)) == 1
     assert "tokens must be in 1..8" in _err(lib)
+    assert lib.kda_verify(*_verify_args(0)) == 1
+    assert "tokens must be in 1..8" in _err(lib)
 
     assert lib.kda_fused_replay_verify(*_verify_args(4, rq=4, fused=True)) == 1
     assert "record_rows and pending are required" in _err(lib)
@@ -161,6 +163,7 @@ def test_commit_rejects_bad_tables(lib):
                               P(None))
 
     assert call(window=9) == 1 and "window" in _err(lib)
+    assert call(window=0) == 1 and "window" in _err(lib)
     assert call(stride=100) == 1 and "slot stride" in _err(lib)
     assert call(stride=2 * 128 * 128 + 3) == 1 and "slot stride" in _err(lib)
     assert call(bnd=0x5000) == 1 and "together" in _err(lib)
@@ -177,6 +180,14 @@ def test_zero_batch_is_a_no_op(lib):
     lib.kda_flush_plan.restype = ctypes.c_int
     assert lib.kda_flush_plan(ctypes.c_int(0), ctypes.c_int(4), *([P(None)] * 7),
                               ctypes.c_int(0), P(None)) == 0
+    # The window length is checked before the batch shortcut.
+    for bad in (0, 9):
+        assert lib.kda_flush_plan(ctypes.c_int(0), ctypes.c_int(bad), *([P(None)] * 7),
+                                  ctypes.c_int(0), P(None)) == 1
+        assert "spec_query_len" in _err(lib)
+    assert lib.kda_flush_plan(ctypes.c_int(-1), ctypes.c_int(4), *([P(None)] * 7),
+                              ctypes.c_int(0), P(None)) == 1
+    assert "batch" in _err(lib)
 
 
 def test_binding_rejects_short_per_request_arrays(lib):

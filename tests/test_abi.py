@@ -236,3 +236,24 @@ def test_product_path_is_independent_of_the_oracle():
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "spec_decode_amd" not in {m[1] for m in imports.findall(text)}, f
             assert "libkda.so" not in text, f
+
+
+def test_build_scripts_load_without_the_built_library():
+    """build() must work on a fresh checkout, where libkda.so does not exist yet:
+    it loads the two build scripts by path and never imports the package (whose
+    __init__ refuses to load without the library) before compiling."""
+    import subprocess
+    import sys
+
+    code = (
+        "import os, sys\n"
+        "sys.path.insert(0, %r)\n"
+        "import __graft_entry__ as g\n"
+        "m = g._load_script(os.path.join(%r, 'spec_decode_amd', 'build.py'), '_b1')\n"
+        "o = g._load_script(os.path.join(%r, 'oracle', 'build.py'), '_b2')\n"
+        "assert callable(m.build) and callable(o.build)\n"
+        "assert 'spec_decode_amd' not in sys.modules, 'package imported before the build'\n"
+        "assert m.LIB.endswith('libkda.so') and o.LIB.endswith('libkda_oracle.so')\n"
+    ) % (ROOT, ROOT, ROOT)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr

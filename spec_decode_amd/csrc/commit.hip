@@ -52,28 +52,38 @@ __device__ __forceinline__ void fold_stage(float (&s)[PASSES][EPC], const float*
 }
 
 // The page's 16-byte chunks, rounded to the state dtype (BF16: nearest-even).
-template <bool BF16, int EPC, int PASSES, int RPP, typename Elem>
+// STREAM: non-temporal stores (see commit_kernel).
+template <bool BF16, bool STREAM, int EPC, int PASSES, int RPP, typename Elem>
 __device__ __forceinline__ void store_page(const float (&s)[PASSES][EPC], Elem* pg, int c0,
                                            int r0) {
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
-    uint4 w;
+    u32x4 w;
     if constexpr (BF16) {
-      w.x = pack_bf16x2(s[i][0], s[i][1]);
-      w.y = pack_bf16x2(s[i][2], s[i][3]);
-      w.z = pack_bf16x2(s[i][4], s[i][5]);
-      w.w = pack_bf16x2(s[i][6], s[i][7]);
+      w[0] = pack_bf16x2(s[i][0], s[i][1]);
+      w[1] = pack_bf16x2(s[i][2], s[i][3]);
+      w[2] = pack_bf16x2(s[i][4], s[i][5]);
+      w[3] = pack_bf16x2(s[i][6], s[i][7]);
     } else {
-      w.x = __float_as_uint(s[i][0]);
-      w.y = __float_as_uint(s[i][1]);
-      w.z = __float_as_uint(s[i][2]);
-      w.w = __float_as_uint(s[i][3]);
+      w[0] = __float_as_uint(s[i][0]);
+      w[1] = __float_as_uint(s[i][1]);
+      w[2] = __float_as_uint(s[i][2]);
+      w[3] = __float_as_uint(s[i][3]);
     }
-    *reinterpret_cast<uint4*>(pg + (r0 + RPP * i) * K + c0) = w;
+    u32x4* const dst = reinterpret_cast<u32x4*>(pg + (r0 + RPP * i) * K + c0);
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(w, dst);
+    else
+      *dst = w;
   }
 }
 
-template <bool BF16, int Q, bool ALIGN>
+// STREAM selects non-temporal page loads and stores (the nt cache-policy bit).
+// They pay off only when a launch's pages far exceed the 256 MB MALL: on a
+// 2 GiB FP32 pool folded in place the launch is 8% faster, while launches
+// whose pages fit in the MALL are about 5% slower with them. The launcher
+// chooses by the page bytes the launch can read.
+template <bool BF16, int Q, bool ALIGN, bool STREAM>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   using Elem = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int EPC = 16 / (int)sizeof(Elem);  // elements per 16-byte chunk
@@ -146,7 +156,11 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < PASSES; ++i)
-    raw[i] = *reinterpret_cast<const uint4*>(srcp + (r0 + RPP * i) * K + c0);
+  {
+    const u32x4* const ptr = reinterpret_cast<const u32x4*>(srcp + (r0 + RPP * i) * K + c0);
+    const u32x4 w = STREAM ? __builtin_nontemporal_load(ptr) : *ptr;
+    raw[i] = uint4{w[0], w[1], w[2], w[3]};
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 3. Per-channel coefficients.
@@ -229,21 +243,22 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   if constexpr (ALIGN) {
     if (mm > 0) {
       fold_stage<EPC, PASSES, RPP, Q>(s, &dm_s[0], &kpm_s[0][0], &u_s[0][0], 0, mm, c0, r0);
-      store_page<BF16, EPC, PASSES, RPP>(s, base + (int64_t)bnd * L.state_stride + (int64_t)h * PAGE,
+      store_page<BF16, STREAM, EPC, PASSES, RPP>(s, base + (int64_t)bnd * L.state_stride + (int64_t)h * PAGE,
                                          c0, r0);
     }
   }
   fold_stage<EPC, PASSES, RPP, Q>(s, &dn_s[0], &kp_s[0][0], &u_s[0][0], mm, ne, c0, r0);
-  store_page<BF16, EPC, PASSES, RPP>(s, base + (int64_t)dst * L.state_stride + (int64_t)h * PAGE,
+  store_page<BF16, STREAM, EPC, PASSES, RPP>(s, base + (int64_t)dst * L.state_stride + (int64_t)h * PAGE,
                                      c0, r0);
 }
 
-template <bool BF16, bool ALIGN>
+template <bool BF16, bool ALIGN, bool STREAM>
 static hipError_t launch_q(const CommitParams& p, int window, dim3 grid, hipStream_t stream) {
   switch (window) {
-#define KDA_COMMIT_CASE(QQ)                                                                \
-  case QQ:                                                                                \
-    hipLaunchKernelGGL((commit_kernel<BF16, QQ, ALIGN>), grid, dim3(256), 0, stream, p); \
+#define KDA_COMMIT_CASE(QQ)                                                                 \
+  case QQ:                                                                                 \
+    hipLaunchKernelGGL((commit_kernel<BF16, QQ, ALIGN, STREAM>), grid, dim3(256), 0, stream, \
+                       p);                                                                 \
     break;
     KDA_COMMIT_CASE(1)
     KDA_COMMIT_CASE(2)
@@ -260,13 +275,25 @@ static hipError_t launch_q(const CommitParams& p, int window, dim3 grid, hipStre
   return hipGetLastError();
 }
 
+// Streaming page accesses once the source pages a launch can read (every
+// request live) reach the MALL's 256 MB.
+constexpr int64_t COMMIT_STREAM_MIN_BYTES = int64_t(256) << 20;
+
 hipError_t launch_commit(const CommitParams& p, int window, bool bf16, bool align, int batch,
                          int layers, hipStream_t stream) {
   const dim3 grid(p.heads, batch, layers);
-  if (bf16) return align ? launch_q<true, true>(p, window, grid, stream)
-                         : launch_q<true, false>(p, window, grid, stream);
-  return align ? launch_q<false, true>(p, window, grid, stream)
-               : launch_q<false, false>(p, window, grid, stream);
+  const int64_t page_bytes = (int64_t)batch * p.heads * layers * PAGE * (bf16 ? 2 : 4);
+  const bool stream_pages = page_bytes >= COMMIT_STREAM_MIN_BYTES;
+  if (bf16) {
+    if (align) return stream_pages ? launch_q<true, true, true>(p, window, grid, stream)
+                                   : launch_q<true, true, false>(p, window, grid, stream);
+    return stream_pages ? launch_q<true, false, true>(p, window, grid, stream)
+                        : launch_q<true, false, false>(p, window, grid, stream);
+  }
+  if (align) return stream_pages ? launch_q<false, true, true>(p, window, grid, stream)
+                                 : launch_q<false, true, false>(p, window, grid, stream);
+  return stream_pages ? launch_q<false, false, true>(p, window, grid, stream)
+                      : launch_q<false, false, false>(p, window, grid, stream);
 }
 
 }  // namespace kda

@@ -79,10 +79,11 @@ __device__ __forceinline__ void store_page(const float (&s)[PASSES][EPC], Elem* 
 }
 
 // STREAM selects non-temporal page loads and stores (the nt cache-policy bit).
-// They pay off only when a launch's pages far exceed the 256 MB MALL: on a
-// 2 GiB FP32 pool folded in place the launch is 8% faster, while launches
-// whose pages fit in the MALL are about 5% slower with them. The launcher
-// chooses by the page bytes the launch can read.
+// They pay off only when a launch's pages exceed the 256 MB MALL: on a 2 GiB
+// FP32 pool folded in place the launch is faster, and so is the next launch
+// on the pool (it finds no dirty lines of this one to write back), while
+// launches whose pages fit in the MALL are about 5% slower with them. The
+// launcher chooses by the page bytes the launch can read.
 template <bool BF16, int Q, bool ALIGN, bool STREAM>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   using Elem = typename std::conditional<BF16, uint16_t, float>::type;
@@ -275,25 +276,21 @@ static hipError_t launch_q(const CommitParams& p, int window, dim3 grid, hipStre
   return hipGetLastError();
 }
 
-// Streaming page accesses once the source pages a launch can read (every
-// request live) reach the MALL's 256 MB.
-constexpr int64_t COMMIT_STREAM_MIN_BYTES = int64_t(256) << 20;
-
 hipError_t launch_commit(const CommitParams& p, int window, bool bf16, bool align, int batch,
                          int layers, hipStream_t stream) {
   const dim3 grid(p.heads, batch, layers);
-  const int64_t page_bytes = (int64_t)batch * p.heads * layers * PAGE * (bf16 ? 2 : 4);
-  const bool stream_pages = page_bytes >= COMMIT_STREAM_MIN_BYTES;
+  // The source pages the launch can read (every request taken as live).
+  const bool st = stream_pages((int64_t)batch * p.heads * layers * PAGE * (bf16 ? 2 : 4));
   if (bf16) {
-    if (align) return stream_pages ? launch_q<true, true, true>(p, window, grid, stream)
-                                   : launch_q<true, true, false>(p, window, grid, stream);
-    return stream_pages ? launch_q<true, false, true>(p, window, grid, stream)
-                        : launch_q<true, false, false>(p, window, grid, stream);
+    if (align) return st ? launch_q<true, true, true>(p, window, grid, stream)
+                         : launch_q<true, true, false>(p, window, grid, stream);
+    return st ? launch_q<true, false, true>(p, window, grid, stream)
+              : launch_q<true, false, false>(p, window, grid, stream);
   }
-  if (align) return stream_pages ? launch_q<false, true, true>(p, window, grid, stream)
-                                 : launch_q<false, true, false>(p, window, grid, stream);
-  return stream_pages ? launch_q<false, false, true>(p, window, grid, stream)
-                      : launch_q<false, false, false>(p, window, grid, stream);
+  if (align) return st ? launch_q<false, true, true>(p, window, grid, stream)
+                       : launch_q<false, true, false>(p, window, grid, stream);
+  return st ? launch_q<false, false, true>(p, window, grid, stream)
+            : launch_q<false, false, false>(p, window, grid, stream);
 }
 
 }  // namespace kda

@@ -10,7 +10,9 @@ static hipError_t launch_t(const VerifyParams& p, int tokens, dim3 grid, hipStre
   switch (tokens) {
 #define KDA_VERIFY_CASE(TT)                                                                   \
   case TT:                                                                                   \
-    hipLaunchKernelGGL((verify_kernel<TT, FUSED, GATED, SB16, CONV_NONE>), grid, dim3(256), 0, \
+    if constexpr (FUSED)                                                                     \
+      return launch_fused_instance<TT, GATED, SB16, CONV_NONE>(p, grid, stream);             \
+    hipLaunchKernelGGL((verify_kernel<TT, false, GATED, SB16, CONV_NONE>), grid, dim3(256), 0, \
                        stream, p);                                                           \
     break;
     KDA_VERIFY_CASE(1)

@@ -16,6 +16,29 @@ constexpr int WAVE = 64;
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// ---------------------------------------------------------------- page stores
+
+// Cache-policy bits of gfx950 vector memory instructions.
+constexpr int CPOL_NT = 2;    // no reuse expected
+constexpr int CPOL_SC1 = 16;  // device scope: a store writes through the XCD's L2
+constexpr int BUF_DWORD3 = 0x00020000;  // gfx9 buffer descriptor word 3: 32-bit data format
+
+// The MI355X memory-side cache (MALL). Launches whose state pages exceed it
+// gain nothing from keeping written pages in the caches: their page accesses
+// stream (commit: non-temporal loads and stores; fused: write-through stores).
+constexpr int64_t MALL_BYTES = int64_t(256) << 20;
+inline bool stream_pages(int64_t page_bytes) { return page_bytes > MALL_BYTES; }
+
+// Buffer descriptor of one page (the base must be uniform over the wave).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(void* page, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(page, 0, (int)bytes, BUF_DWORD3);
+}
+template <int CPOL>
+__device__ __forceinline__ void store_page16(u32x4 v, __amdgpu_buffer_rsrc_t page,
+                                             uint32_t byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, page, (int)byte_off, 0, CPOL);
+}
+
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

@@ -500,12 +500,15 @@ def test_maximum_batch_grid_fused_sampled():
     torch.cuda.empty_cache()
 
 
-def test_large_decode_ragged_windows_and_boundaries_bf16_sampled():
-    """The large decode shape (H=64, B=512, q=8) on a BF16 pool of 1040 slots
-    (2 GiB): window lengths 0..8 through query_start_loc and boundary stores
-    for half the requests (m in 1..9); 30 sampled requests against the oracle
-    and the pages nobody writes compared bit for bit."""
+@pytest.mark.parametrize("pool", ["bf16", "f32"])
+def test_large_decode_ragged_windows_and_boundaries_sampled(pool):
+    """The large decode shape (H=64, B=512, q=8) on a pool of 1040 slots (2 GiB
+    BF16, 4 GiB FP32: the FP32 launch takes the streaming instance, whose S_n
+    stores write through): window lengths 0..8 through query_start_loc and
+    boundary stores for half the requests (m in 1..9); 30 sampled requests
+    against the oracle and the pages nobody writes compared bit for bit."""
     import spec_decode_amd as kda
+    bf16 = pool == "bf16"
     H, B, T, RQ, S = 64, 512, 8, 8, 1040
     page = H * V * K
     g = W._gen(910)
@@ -527,11 +530,11 @@ def test_large_decode_ragged_windows_and_boundaries_bf16_sampled():
     corr, kg = W.draw_records(g, B, H, RQ)
     corr, kg = corr.numpy(), W.bits(kg)
     win = {k: np.ascontiguousarray(v[:total]) for k, v in window_np(W.draw_window(g, B, T, H)).items()}
-    d_state = W.draw_state(911, S * page, torch.bfloat16, DEV)
+    d_state = W.draw_state(911, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
     before = d_state.clone()
     d_corr, d_kg = dev(corr), dev_bf16(kg)
     out = torch.zeros((total, H * V), dtype=torch.bfloat16, device=DEV)
-    announce("large decode ragged + boundaries, BF16 pool")
+    announce(f"large decode ragged + boundaries, {pool} pool")
     kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]),
                                 k=dev_bf16(win["k"]), v=dev_bf16(win["v"]),
                                 raw_g=dev_bf16(win["raw_g"]), raw_beta=dev_bf16(win["raw_beta"]),
@@ -550,8 +553,9 @@ def test_large_decode_ragged_windows_and_boundaries_bf16_sampled():
             if bounds[b] > 0:
                 touched[int(bounds[b])] = True
     keep = (~touched).nonzero().flatten().to(DEV)
-    assert torch.equal(d_state.view(S, page).index_select(0, keep).view(torch.int16),
-                       before.view(S, page).index_select(0, keep).view(torch.int16))
+    bits = torch.int16 if bf16 else torch.int32
+    assert torch.equal(d_state.view(S, page).index_select(0, keep).view(bits),
+                       before.view(S, page).index_select(0, keep).view(bits))
     rng = np.random.default_rng(912)
     live = [b for b in range(B) if slots[b] > 0 and rows[b] >= 0]
     by_len = {}
@@ -564,9 +568,10 @@ def test_large_decode_ragged_windows_and_boundaries_bf16_sampled():
     m = sampled_fused_oracle(R=R, H=H, T=T, RQ=RQ, state_pages=s_host, slots=slots, rows=rows,
                              pending_row=pending_row, corr=corr, kg=kg, win=win,
                              a_log=a_log[0].numpy(), dt_bias=dtb[0].numpy(), lb=W.LOWER_BOUND,
-                             qsl=qsl, bounds=bounds, blens=blens, state_dtype=np.uint16)
+                             qsl=qsl, bounds=bounds, blens=blens,
+                             state_dtype=np.uint16 if bf16 else np.float32)
     g_pages = lambda sl: np_of(d_state[sl * page:(sl + 1) * page])
     _check_sampled("ragged+bnd", R, m, np_of(out), g_pages, np_of(d_corr), np_of(d_kg), slots,
-                   rows, bounds, T, True, page)
+                   rows, bounds, T, bf16, page)
     del d_state, before
     torch.cuda.empty_cache()

@@ -57,7 +57,7 @@ def parse_args():
                          "--state-dtype); decay: kda_decay on the large decode batch's raw "
                          "gates")
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-requests", type=int, default=512,

@@ -52,10 +52,11 @@ __device__ __forceinline__ void fold_stage(float (&s)[PASSES][EPC], const float*
 }
 
 // The page's 16-byte chunks, rounded to the state dtype (BF16: nearest-even).
-// STREAM: non-temporal stores (see commit_kernel).
+// STREAM: write-through no-reuse stores (see commit_kernel).
 template <bool BF16, bool STREAM, int EPC, int PASSES, int RPP, typename Elem>
 __device__ __forceinline__ void store_page(const float (&s)[PASSES][EPC], Elem* pg, int c0,
                                            int r0) {
+  const __amdgpu_buffer_rsrc_t rs = page_rsrc(pg, PAGE * (int)sizeof(Elem));
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
     u32x4 w;
@@ -70,20 +71,18 @@ __device__ __forceinline__ void store_page(const float (&s)[PASSES][EPC], Elem* 
       w[2] = __float_as_uint(s[i][2]);
       w[3] = __float_as_uint(s[i][3]);
     }
-    u32x4* const dst = reinterpret_cast<u32x4*>(pg + (r0 + RPP * i) * K + c0);
-    if constexpr (STREAM)
-      __builtin_nontemporal_store(w, dst);
-    else
-      *dst = w;
+    const uint32_t off = (uint32_t)(((r0 + RPP * i) * K + c0) * (int)sizeof(Elem));
+    store_page16<STREAM ? (CPOL_NT | CPOL_SC1) : 0>(w, rs, off);
   }
 }
 
-// STREAM selects non-temporal page loads and stores (the nt cache-policy bit).
-// They pay off only when a launch's pages exceed the 256 MB MALL: on a 2 GiB
-// FP32 pool folded in place the launch is faster, and so is the next launch
-// on the pool (it finds no dirty lines of this one to write back), while
-// launches whose pages fit in the MALL are about 5% slower with them. The
-// launcher chooses by the page bytes the launch can read.
+// STREAM selects no-reuse page loads (nt) and write-through no-reuse page
+// stores (sc1 nt), launched at two workgroups per CU. They pay off only when
+// a launch's pages exceed the 256 MB MALL: on the 2 GiB FP32 pool folded in
+// place the launch is 9% faster, and so is the next launch on the pool (it
+// finds no dirty lines of this one to write back), while launches whose pages
+// fit in the MALL are about 5% slower with them. The launcher chooses by the
+// page bytes the launch can read.
 template <bool BF16, int Q, bool ALIGN, bool STREAM>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   using Elem = typename std::conditional<BF16, uint16_t, float>::type;
@@ -257,10 +256,13 @@ template <bool BF16, bool ALIGN, bool STREAM>
 static hipError_t launch_q(const CommitParams& p, int window, dim3 grid, hipStream_t stream) {
   switch (window) {
 #define KDA_COMMIT_CASE(QQ)                                                                 \
-  case QQ:                                                                                 \
-    hipLaunchKernelGGL((commit_kernel<BF16, QQ, ALIGN, STREAM>), grid, dim3(256), 0, stream, \
-                       p);                                                                 \
-    break;
+  case QQ: {                                                                               \
+    static const size_t pad =                                                              \
+        STREAM ? two_per_cu_lds(&commit_kernel<BF16, QQ, ALIGN, STREAM>) : 0;              \
+    hipLaunchKernelGGL((commit_kernel<BF16, QQ, ALIGN, STREAM>), grid, dim3(256), pad,     \
+                       stream, p);                                                         \
+    break;                                                                                 \
+  }
     KDA_COMMIT_CASE(1)
     KDA_COMMIT_CASE(2)
     KDA_COMMIT_CASE(3)

@@ -25,9 +25,22 @@ constexpr int BUF_DWORD3 = 0x00020000;  // gfx9 buffer descriptor word 3: 32-bit
 
 // The MI355X memory-side cache (MALL). Launches whose state pages exceed it
 // gain nothing from keeping written pages in the caches: their page accesses
-// stream (commit: non-temporal loads and stores; fused: write-through stores).
+// stream (write-through, no-reuse page stores; the commit also loads its pages
+// with the no-reuse hint), at two workgroups per CU.
 constexpr int64_t MALL_BYTES = int64_t(256) << 20;
 inline bool stream_pages(int64_t page_bytes) { return page_bytes > MALL_BYTES; }
+
+// Dynamic LDS that holds a kernel to at most two workgroups per CU (160 KiB of
+// LDS per CU): the streaming instances move their pages faster with two than
+// with three or more. Computed from the kernel's static LDS.
+template <typename Kernel>
+size_t two_per_cu_lds(Kernel kernel) {
+  hipFuncAttributes a{};
+  if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel)) != hipSuccess) return 0;
+  constexpr size_t LDS_PER_CU = 160 * 1024;
+  constexpr size_t WANT = LDS_PER_CU / 3 + 256;  // three no longer fit, two do
+  return a.sharedSizeBytes >= WANT ? 0 : WANT - a.sharedSizeBytes;
+}
 
 // Buffer descriptor of one page (the base must be uniform over the wave).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(void* page, uint32_t bytes) {

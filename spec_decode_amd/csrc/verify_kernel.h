@@ -833,18 +833,6 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
 }
 
-// Dynamic LDS that holds a kernel to at most two workgroups per CU (160 KiB of
-// LDS per CU): the write-through instances move their pages faster with two
-// than with three. Computed once per instance from its static LDS.
-template <typename Kernel>
-size_t two_per_cu_lds(Kernel kernel) {
-  hipFuncAttributes a{};
-  if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel)) != hipSuccess) return 0;
-  constexpr size_t LDS_PER_CU = 160 * 1024;
-  constexpr size_t WANT = LDS_PER_CU / 3 + 256;  // three no longer fit, two do
-  return a.sharedSizeBytes >= WANT ? 0 : WANT - a.sharedSizeBytes;
-}
-
 // Launch of one fused instance: over FP32 pages, the streaming one at two
 // workgroups per CU when the grid's pages (batch x heads x 64 KiB) exceed the
 // MALL. On the 2 GiB pool of the large decode batch that makes the step 2.4%

@@ -782,18 +782,42 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         // The output stage normalises the BF16-rounded o over the head's rows.
         ob_s[t][vrow] = bf16_bits_to_f32(f32_to_bf16_bits(o));
       } else {
-        if (t < L) p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
+        if (t < L) {
+          if constexpr (STREAM) {
+            // Write-through like the pages; the descriptor spans the item's
+            // T token rows of this head.
+            const __amdgpu_buffer_rsrc_t out_rs =
+                page_rsrc(p.out + tok0 * H * V + (int64_t)h * V, (uint32_t)(T * H * V * 2));
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o), out_rs,
+                                                  (t * H * V + vrow) * 2, 0, CPOL_NT | CPOL_SC1);
+          } else {
+            p.out[(tok0 + t) * H * V + head_row] = f32_to_bf16_bits(o);
+          }
+        }
       }
     }
     if (rec >= 0) {
       const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
+      // STREAM: write-through stores within the item's record block.
+      const __amdgpu_buffer_rsrc_t corr_rs = page_rsrc(p.corr + rbase * V, p.rq * V * 4);
+      const __amdgpu_buffer_rsrc_t kg_rs = page_rsrc(p.kg + rbase * 2 * K, p.rq * 2 * K * 2);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         if (t >= L) break;  // uniform
-        p.corr[(rbase + t) * V + vrow] = us[t];
         const uint32_t bits = kg_s[t][c];
-        p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(bits & 0xffffu);
-        p.kg[(rbase + t) * 2 * K + K + c] = (uint16_t)(bits >> 16);
+        if constexpr (STREAM) {
+          constexpr int CP = CPOL_NT | CPOL_SC1;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(us[t]), corr_rs,
+                                                (t * V + vrow) * 4, 0, CP);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(bits & 0xffffu), kg_rs,
+                                                (t * 2 * K + c) * 2, 0, CP);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(bits >> 16), kg_rs,
+                                                (t * 2 * K + K + c) * 2, 0, CP);
+        } else {
+          p.corr[(rbase + t) * V + vrow] = us[t];
+          p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(bits & 0xffffu);
+          p.kg[(rbase + t) * 2 * K + K + c] = (uint16_t)(bits >> 16);
+        }
       }
     }
   }

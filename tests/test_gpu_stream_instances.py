@@ -1,0 +1,121 @@
+"""The streaming instances compute the same bits as the plain ones.
+
+A launch whose state pages exceed the 256 MB MALL runs the streaming instance
+(write-through, no-reuse stores at two workgroups per CU); a smaller launch
+runs the plain one. Items are independent, so the same requests run as one
+launch (streaming) and as two launches of half the batch (plain) must leave
+the pool, the records and the outputs bit for bit equal. Neither side is the
+oracle: the oracle pins both through the other GPU tests; this one pins that
+the instance choice changes nothing but the cache policy.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _kda_cases import DEV, announce
+
+pytestmark = pytest.mark.gpu
+K = V = 128
+H = 64
+MALL = 256 << 20
+
+
+def _bits(t):
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy()
+
+
+def _assert_same(a, b, names):
+    for name in names:
+        assert np.array_equal(_bits(a[name]), _bits(b[name])), f"{name} differs"
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_fused_streaming_instance_matches_plain(gated):
+    import spec_decode_amd as kda
+    B, T, RQ = 80, 8, 8
+    page = H * V * K
+    assert B * page * 4 > MALL >= (B // 2) * page * 4
+    S = B + 9
+    g = W._gen(950 + gated)
+    slots = (W.permutation(g, S - 1) + 1)[:B].to(torch.int32)
+    slots[[7, 45]] = 0
+    rows = W.permutation(g, B).to(torch.int32)
+    rows[[12, 60]] = -1
+    pending = W.uniform_int(g, 0, RQ, B).to(torch.int32)
+    corr, kg = W.draw_records(g, B, H, RQ)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    w = W.draw_window(g, B, T, H).to(DEV)
+    extra = {}
+    if gated:
+        gate, weight, eps = W.draw_output_stage(W._gen(952), B, T, H)
+        extra = dict(gate=gate.to(DEV), norm_weight=weight.to(DEV), norm_eps=eps)
+    state0 = W.draw_state(953 + gated, S * page, torch.float32, DEV)
+
+    def fresh():
+        return dict(state=state0.clone(), corr=corr.to(DEV), kg=kg.to(DEV),
+                    pending=pending.to(DEV),
+                    out=torch.zeros((B * T, H * V), dtype=torch.bfloat16, device=DEV))
+
+    def call(m, lo, hi):
+        n = hi - lo
+        ex = dict(extra)
+        if gated:
+            ex["gate"] = extra["gate"][lo * T:hi * T]
+        kda.kda_fused_replay_verify(
+            heads=H, tokens=T, batch=n, q=w.q[lo * T:hi * T], k=w.k[lo * T:hi * T],
+            v=w.v[lo * T:hi * T], raw_g=w.raw_g[lo * T:hi * T],
+            raw_beta=w.raw_beta[lo * T:hi * T], a_log=a_log[0].contiguous().to(DEV),
+            dt_bias=dtb[0].contiguous().to(DEV), lower_bound=W.LOWER_BOUND, state=m["state"],
+            state_slot_stride=page, state_indices=slots[lo:hi].to(DEV), corr=m["corr"],
+            kg=m["kg"], record_tokens=RQ, record_rows=rows[lo:hi].to(DEV),
+            pending=m["pending"], out=m["out"][lo * T:hi * T], **ex)
+
+    announce(f"fused, streaming vs plain instance, H={H} B={B} q={T}, gated={gated}")
+    one, two = fresh(), fresh()
+    call(one, 0, B)
+    call(two, 0, B // 2)
+    call(two, B // 2, B)
+    torch.cuda.synchronize()
+    assert not torch.equal(one["state"], state0)  # pages were written
+    _assert_same(one, two, ("state", "corr", "kg", "out"))
+
+
+@pytest.mark.parametrize("pool", ["f32", "bf16"])
+def test_commit_streaming_instance_matches_plain(pool):
+    import spec_decode_amd as kda
+    bf16 = pool == "bf16"
+    es = 2 if bf16 else 4
+    B, Q = (160 if bf16 else 80), 8
+    page = H * V * K
+    assert B * page * es > MALL >= (B // 2) * page * es
+    S = B + 5
+    g = W._gen(960 + bf16)
+    src = (W.permutation(g, S - 1) + 1)[:B].to(torch.int32)
+    src[[3, 50]] = 0
+    rows = W.permutation(g, B).to(torch.int32)
+    lens = W.uniform_int(g, 0, Q, B).to(torch.int32)
+    corr, kg = W.draw_records(g, B, H, Q)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    state0 = W.draw_state(962 + bf16, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
+    d_corr, d_kg = corr.to(DEV), kg.to(DEV)
+
+    def call(state, lo, hi):
+        s = src[lo:hi].to(DEV)
+        kda.kda_commit(heads=H, window=Q, batch=hi - lo,
+                       state_dtype=kda.KDA_STATE_BF16 if bf16 else kda.KDA_STATE_F32,
+                       state_addrs=[state.data_ptr()], state_slot_strides=[page],
+                       corr_addrs=[d_corr.data_ptr()], corr_row_strides=[H * Q * V],
+                       kg_addrs=[d_kg.data_ptr()], kg_row_strides=[H * Q * 2 * K],
+                       a_log=a_log.to(DEV), dt_bias=dtb.to(DEV), sources=s,
+                       commit_lens=lens[lo:hi].to(DEV), destinations=s,
+                       record_rows=rows[lo:hi].to(DEV), lower_bound=W.LOWER_BOUND)
+
+    announce(f"commit, streaming vs plain instance, H={H} B={B} window {Q}, {pool} pool")
+    one, two = state0.clone(), state0.clone()
+    call(one, 0, B)
+    call(two, 0, B // 2)
+    call(two, B // 2, B)
+    torch.cuda.synchronize()
+    assert not torch.equal(one, state0)
+    assert np.array_equal(_bits(one), _bits(two))

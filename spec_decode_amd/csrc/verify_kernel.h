@@ -798,23 +798,28 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
     if (rec >= 0) {
       const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
-      // STREAM: write-through stores within the item's record block.
-      const __amdgpu_buffer_rsrc_t corr_rs = page_rsrc(p.corr + rbase * V, p.rq * V * 4);
-      const __amdgpu_buffer_rsrc_t kg_rs = page_rsrc(p.kg + rbase * 2 * K, p.rq * 2 * K * 2);
+      if constexpr (STREAM) {
+        // Write-through like the pages, within the item's record block.
+        constexpr int CP = CPOL_NT | CPOL_SC1;
+        const __amdgpu_buffer_rsrc_t corr_rs = page_rsrc(p.corr + rbase * V, p.rq * V * 4);
+        const __amdgpu_buffer_rsrc_t kg_rs = page_rsrc(p.kg + rbase * 2 * K, p.rq * 2 * K * 2);
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        if (t >= L) break;  // uniform
-        const uint32_t bits = kg_s[t][c];
-        if constexpr (STREAM) {
-          constexpr int CP = CPOL_NT | CPOL_SC1;
+        for (int t = 0; t < T; ++t) {
+          if (t >= L) break;  // uniform
+          const uint32_t bits = kg_s[t][c];
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(us[t]), corr_rs,
                                                 (t * V + vrow) * 4, 0, CP);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(bits & 0xffffu), kg_rs,
                                                 (t * 2 * K + c) * 2, 0, CP);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(bits >> 16), kg_rs,
                                                 (t * 2 * K + K + c) * 2, 0, CP);
-        } else {
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          if (t >= L) break;  // uniform
           p.corr[(rbase + t) * V + vrow] = us[t];
+          const uint32_t bits = kg_s[t][c];
           p.kg[(rbase + t) * 2 * K + c] = (uint16_t)(bits & 0xffffu);
           p.kg[(rbase + t) * 2 * K + K + c] = (uint16_t)(bits >> 16);
         }

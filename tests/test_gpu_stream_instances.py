@@ -31,9 +31,10 @@ def _assert_same(a, b, names):
 
 
 @pytest.mark.parametrize("gated", [False, True])
-def test_fused_streaming_instance_matches_plain(gated):
+@pytest.mark.parametrize("T", [3, 8])
+def test_fused_streaming_instance_matches_plain(gated, T):
     import spec_decode_amd as kda
-    B, T, RQ = 80, 8, 8
+    B, RQ = 80, 8
     page = H * V * K
     assert B * page * 4 > MALL >= (B // 2) * page * 4
     S = B + 9
@@ -119,3 +120,57 @@ def test_commit_streaming_instance_matches_plain(pool):
     torch.cuda.synchronize()
     assert not torch.equal(one, state0)
     assert np.array_equal(_bits(one), _bits(two))
+
+
+@pytest.mark.parametrize("layout", ["dim_first", "window_major"])
+def test_fused_conv_streaming_instance_matches_plain(layout):
+    """The same with the convolution prologue, over the packed dim-first window
+    pool and the window-major one (the strided code); the window pool, which
+    the step rewrites in place, is compared too."""
+    import spec_decode_amd as kda
+    from _kda_cases import conv_pool_layout
+    B, T, RQ = 80, 8, 8
+    page = H * V * K
+    S = B + 7
+    g = W._gen(970)
+    slots = (W.permutation(g, S - 1) + 1)[:B].to(torch.int32)
+    slots[[9, 44]] = 0
+    rows = W.permutation(g, B).to(torch.int32)
+    rows[[21, 70]] = -1
+    pending = W.uniform_int(g, 0, RQ, B).to(torch.int32)
+    corr, kg = W.draw_records(g, B, H, RQ)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    w = W.draw_window(g, B, T, H).to(DEV)
+    cv = W.draw_conv_inputs(W._gen(971), B, T, H, RQ, S)
+    pool0 = cv.window if layout == "dim_first" else cv.window.permute(0, 2, 1).contiguous()
+    pool0 = pool0.reshape(-1).to(DEV)
+    strides = conv_pool_layout(S, H, RQ + 2, layout=layout)
+    x = cv.x.to(DEV)
+    state0 = W.draw_state(972, S * page, torch.float32, DEV)
+
+    def fresh():
+        return dict(state=state0.clone(), pool=pool0.clone(), corr=corr.to(DEV), kg=kg.to(DEV),
+                    pending=pending.to(DEV),
+                    out=torch.zeros((B * T, H * V), dtype=torch.bfloat16, device=DEV))
+
+    def call(m, lo, hi):
+        kda.kda_fused_conv_replay_verify(
+            heads=H, tokens=T, batch=hi - lo, x=x[lo * T:hi * T], x_row_stride=cv.pitch,
+            conv_weight=cv.weight.to(DEV), conv_bias=cv.bias.to(DEV), conv_state=m["pool"],
+            conv_slot_stride=strides[0], conv_channel_stride=strides[1],
+            conv_tap_stride=strides[2], q_scale=K ** -0.5, raw_g=w.raw_g[lo * T:hi * T],
+            raw_beta=w.raw_beta[lo * T:hi * T], a_log=a_log[0].contiguous().to(DEV),
+            dt_bias=dtb[0].contiguous().to(DEV), lower_bound=W.LOWER_BOUND, state=m["state"],
+            state_slot_stride=page, state_indices=slots[lo:hi].to(DEV), corr=m["corr"],
+            kg=m["kg"], record_tokens=RQ, record_rows=rows[lo:hi].to(DEV),
+            pending=m["pending"], out=m["out"][lo * T:hi * T])
+
+    announce(f"fused conv ({layout} windows), streaming vs plain instance, H={H} B={B} q={T}")
+    one, two = fresh(), fresh()
+    call(one, 0, B)
+    call(two, 0, B // 2)
+    call(two, B // 2, B)
+    torch.cuda.synchronize()
+    assert not torch.equal(one["state"], state0)
+    assert not torch.equal(one["pool"], pool0)
+    _assert_same(one, two, ("state", "pool", "corr", "kg", "out"))

@@ -15,8 +15,10 @@ pytestmark = pytest.mark.gpu
 K = V = 128
 
 
-def _case(bf16, seed=31):
-    H, B, T, RQ, S = 4, 24, 8, 8, 40
+def _case(bf16, seed=31, large=False):
+    # large: 64 heads x 80 requests of FP32 pages (320 MiB, above the MALL's
+    # 256 MB), so the fused step and the commit run their streaming instances.
+    H, B, T, RQ, S = (64, 80, 8, 8, 90) if large else (4, 24, 8, 8, 40)
     g = W._gen(seed)
     page = H * V * K
     state = W.draw_state(seed + 1, S * page, torch.float32)
@@ -76,11 +78,12 @@ def _snapshot(m):
             for k, v in m.items()}
 
 
-@pytest.mark.parametrize("bf16", [False, True])
-def test_captured_step_replays_match_eager_steps(bf16):
-    announce(f"graph capture: step of H=4 B=24 q=8, {'BF16' if bf16 else 'FP32'} pool")
-    fixed, eager = _case(bf16)
-    _, graphed = _case(bf16)
+@pytest.mark.parametrize("bf16,large", [(False, False), (True, False), (False, True)])
+def test_captured_step_replays_match_eager_steps(bf16, large):
+    announce(f"graph capture: step of {'H=64 B=80' if large else 'H=4 B=24'} q=8, "
+             f"{'BF16' if bf16 else 'FP32'} pool")
+    fixed, eager = _case(bf16, large=large)
+    _, graphed = _case(bf16, large=large)
     ref = []
     for _ in range(3):
         _step(fixed, eager)
@@ -94,7 +97,8 @@ def test_captured_step_replays_match_eager_steps(bf16):
         _step(fixed, graphed)
     torch.cuda.synchronize()
     # Capture executes nothing: the graphed buffers still hold their inputs.
-    assert np.array_equal(_snapshot(graphed)["pending"], _case(bf16)[1]["pending"].cpu().numpy())
+    assert np.array_equal(_snapshot(graphed)["pending"],
+                          _case(bf16, large=large)[1]["pending"].cpu().numpy())
     scratch = torch.ones(1 << 20, device=DEV)
     for r in range(3):
         graph.replay()

@@ -16,8 +16,9 @@
  *    128 x 128, contiguous; a slot holds H pages: state[slot][h][v][c].
  *  - Every pointer argument is a DEVICE pointer unless it says "host". Buffers
  *    are owned by the caller; the library allocates nothing, keeps no state
- *    between calls and never synchronises: work is enqueued on `stream` (a
- *    hipStream_t, NULL for the default stream) and the call returns.
+ *    of the computation between calls and never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t, NULL for the default stream) and
+ *    the call returns.
  *  - BF16 tensors are passed as uint16_t bit patterns; index arrays are int32.
  *  - Return value: KDA_OK (0), KDA_EINVAL for a bad argument (nothing is
  *    launched), KDA_ELAUNCH when the HIP launch fails. kda_last_error() gives a
@@ -32,6 +33,13 @@
  *    access aligned; the library rejects them otherwise.
  *  - A slot index <= null_slot means "no state" (padding rows).
  *  - batch == 0 (or tokens == 0 for kda_decay) returns KDA_OK with no launch.
+ *  - Launches whose state pages exceed the GPU's 256 MB memory-side cache
+ *    (kda_commit: batch x heads x layers pages; kda_fused_replay_verify and
+ *    kda_fused_conv_replay_verify on FP32 pools: batch x heads pages) write
+ *    their pages with write-through, no-reuse stores, at two workgroups per
+ *    CU (extra dynamic LDS, sized on the first such launch of each kernel
+ *    from its static LDS; this is the library's only retained host data).
+ *    The results are bit-identical to those of smaller launches.
  */
 #ifndef KDA_H
 #define KDA_H

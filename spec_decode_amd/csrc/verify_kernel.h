@@ -28,6 +28,10 @@
 //    with M = j (2T <= 16 rows of X, zero above 2T), N = v, and the 4 values of a
 //    lane as 4 consecutive K steps (key channels 16cb + 4(l/16) + i);
 // so no lane ever exchanges state values and every state byte is read once.
+// S_n replaces the loaded page in the same registers and is stored from them
+// as the kernel's last instructions; over FP32 pools larger than the MALL
+// (template argument STREAM) those stores, o and the records write through
+// the L2 with the no-reuse hint, at two workgroups per CU.
 //
 // BF16 pages hold the same register layout after conversion, with the key
 // channels permuted inside each group of 32: one 16-byte load brings 8 channels

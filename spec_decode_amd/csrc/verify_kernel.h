@@ -29,9 +29,10 @@
 //    lane as 4 consecutive K steps (key channels 16cb + 4(l/16) + i);
 // so no lane ever exchanges state values and every state byte is read once.
 // S_n replaces the loaded page in the same registers and is stored from them
-// as the kernel's last instructions; over FP32 pools larger than the MALL
-// (template argument STREAM) those stores, o and the records write through
-// the L2 with the no-reuse hint, at two workgroups per CU.
+// as the kernel's last instructions. With the template argument STREAM (launches
+// whose pages exceed the MALL) o and the records, and in the fused step over
+// FP32 pools S_n too, write through the L2 with the no-reuse hint; the fused
+// step then runs at two workgroups per CU.
 //
 // BF16 pages hold the same register layout after conversion, with the key
 // channels permuted inside each group of 32: one 16-byte load brings 8 channels
@@ -324,7 +325,6 @@ __device__ __forceinline__ constexpr int chan0(int cb, int g) {
 
 template <int T, bool FUSED, bool GATED, bool SB16, int CONV, bool STREAM = false>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
-  static_assert(FUSED || !STREAM, "only the fused step writes pages");
   static_assert(FUSED || !CONV, "the convolution prologue is a fused-step prologue");
   using PI = Pairs<T>;
   const int h = blockIdx.x;

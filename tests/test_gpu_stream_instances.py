@@ -174,3 +174,54 @@ def test_fused_conv_streaming_instance_matches_plain(layout):
     assert not torch.equal(one["state"], state0)
     assert not torch.equal(one["pool"], pool0)
     _assert_same(one, two, ("state", "pool", "corr", "kg", "out"))
+
+
+@pytest.mark.parametrize("pool", ["f32", "bf16"])
+def test_verify_streaming_instance_matches_plain(pool):
+    """The stock verify: above the MALL's size it writes o and the records
+    through the L2; the pool is only read, on both instances."""
+    import spec_decode_amd as kda
+    bf16 = pool == "bf16"
+    es = 2 if bf16 else 4
+    B, T, RQ = (160 if bf16 else 80), 8, 8
+    page = H * V * K
+    assert B * page * es > MALL >= (B // 2) * page * es
+    S = B + 5
+    g = W._gen(980 + bf16)
+    slots = (W.permutation(g, S - 1) + 1)[:B].to(torch.int32)
+    slots[[4, 33]] = 0
+    rows = W.permutation(g, B).to(torch.int32)
+    rows[[8, 61]] = -1
+    corr, kg = W.draw_records(g, B, H, RQ)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    w = W.draw_window(g, B, T, H).to(DEV)
+    state = W.draw_state(982 + bf16, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
+    before = state.clone()
+
+    def fresh():
+        return dict(corr=corr.to(DEV), kg=kg.to(DEV),
+                    out=torch.zeros((B * T, H * V), dtype=torch.bfloat16, device=DEV))
+
+    def call(m, lo, hi):
+        kda.kda_verify(
+            heads=H, tokens=T, batch=hi - lo, q=w.q[lo * T:hi * T], k=w.k[lo * T:hi * T],
+            v=w.v[lo * T:hi * T], raw_g=w.raw_g[lo * T:hi * T],
+            raw_beta=w.raw_beta[lo * T:hi * T], a_log=a_log[0].contiguous().to(DEV),
+            dt_bias=dtb[0].contiguous().to(DEV), lower_bound=W.LOWER_BOUND, state=state,
+            state_slot_stride=page, state_indices=slots[lo:hi].to(DEV), corr=m["corr"],
+            kg=m["kg"], record_tokens=RQ, record_rows=rows[lo:hi].to(DEV),
+            out=m["out"][lo * T:hi * T])
+
+    announce(f"verify, streaming vs plain instance, H={H} B={B} q={T}, {pool} pool")
+    one, two = fresh(), fresh()
+    call(one, 0, B)
+    call(two, 0, B // 2)
+    call(two, B // 2, B)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits_t(state), _bits_t(before))
+    assert not torch.equal(one["corr"], corr.to(DEV))  # records were written
+    _assert_same(one, two, ("corr", "kg", "out"))
+
+
+def _bits_t(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)

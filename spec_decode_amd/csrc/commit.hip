@@ -91,8 +91,19 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   constexpr int RPP = 256 / CPR;               // rows per pass of the workgroup
   constexpr int PASSES = V / RPP;
 
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  // Item order. Workgroups are dealt to the 8 XCDs round-robin by linear
+  // index; the streaming instances remap that index so that XCD x takes the
+  // x-th eighth of the layer's (head, request) items, i.e. whole requests'
+  // pages in turn, instead of every eighth head of the requests in flight
+  // (large decode FP32 commit 0.662 -> 0.650 ms, 8-layer align 1.050 ->
+  // 0.975 ms; the 1 GiB BF16 in-place commit 0.347 -> 0.357 ms).
+  int lin = blockIdx.x + blockIdx.y * gridDim.x;
+  if constexpr (STREAM) {
+    const int per_layer = gridDim.x * gridDim.y;
+    if ((per_layer & 7) == 0) lin = (lin & 7) * (per_layer >> 3) + (lin >> 3);
+  }
+  const int h = lin % gridDim.x;
+  const int b = lin / gridDim.x;
   const int l = blockIdx.z;
   const int tid = threadIdx.x;
 

@@ -31,8 +31,9 @@
 // S_n replaces the loaded page in the same registers and is stored from them
 // as the kernel's last instructions. With the template argument STREAM (launches
 // whose pages exceed the MALL) o and the records, and in the fused step over
-// FP32 pools S_n too, write through the L2 with the no-reuse hint; the fused
-// step then runs at two workgroups per CU.
+// FP32 pools S_n too, write through the L2 with the no-reuse hint, the window's
+// inputs and the old records load with the no-reuse hint, and the fused step
+// runs at two workgroups per CU.
 //
 // BF16 pages hold the same register layout after conversion, with the key
 // channels permuted inside each group of 32: one 16-byte load brings 8 channels
@@ -481,9 +482,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int64_t idx = (tok0 + (t < L ? t : last)) * H * K + head_row;
-        kb[t] = p.k[idx];
-        gb[t] = p.g[idx];
-        qb[t] = p.q[idx];
+        // STREAM: the window's inputs are read once (no-reuse hint).
+        kb[t] = STREAM ? __builtin_nontemporal_load(p.k + idx) : p.k[idx];
+        gb[t] = STREAM ? __builtin_nontemporal_load(p.g + idx) : p.g[idx];
+        qb[t] = STREAM ? __builtin_nontemporal_load(p.q + idx) : p.q[idx];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -528,7 +530,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!CONV) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) vb[t] = p.v[(tok0 + (t < L ? t : last)) * H * V + head_row];
+      for (int t = 0; t < T; ++t) {
+        const int64_t idx = (tok0 + (t < L ? t : last)) * H * V + head_row;
+        vb[t] = STREAM ? __builtin_nontemporal_load(p.v + idx) : p.v[idx];
+      }
     }
     rbb = p.rb[(tok0 + (c < L ? c : last)) * H + h];  // unconditional: no divergent load
     if constexpr (CONV) {
@@ -547,9 +552,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         ogb[t] = 0;
         ou[t] = 0.f;
         if (t < n) {
-          okb[t] = p.kg[(rbase + t) * 2 * K + c];
-          ogb[t] = p.kg[(rbase + t) * 2 * K + K + c];
-          ou[t] = p.corr[(rbase + t) * V + c];
+          // STREAM: the old records are read once (no-reuse hint).
+          const uint16_t* const kgp = p.kg + (rbase + t) * 2 * K + c;
+          const float* const up = p.corr + (rbase + t) * V + c;
+          okb[t] = STREAM ? __builtin_nontemporal_load(kgp) : kgp[0];
+          ogb[t] = STREAM ? __builtin_nontemporal_load(kgp + K) : kgp[K];
+          ou[t] = STREAM ? __builtin_nontemporal_load(up) : up[0];
         }
       }
     }

@@ -30,10 +30,10 @@
 // so no lane ever exchanges state values and every state byte is read once.
 // S_n replaces the loaded page in the same registers and is stored from them
 // as the kernel's last instructions. With the template argument STREAM (launches
-// whose pages exceed the MALL) o and the records, and in the fused step over
-// FP32 pools S_n too, write through the L2 with the no-reuse hint, the window's
-// inputs and the old records load with the no-reuse hint, and the fused step
-// runs at two workgroups per CU.
+// whose pages exceed the MALL) the window's inputs and the old records load
+// with the no-reuse hint; o and the records (the stock verify), or S_n, o and
+// the records (the fused step over FP32 pools, then at two workgroups per CU)
+// write through the L2 with the no-reuse hint.
 //
 // BF16 pages hold the same register layout after conversion, with the key
 // channels permuted inside each group of 32: one 16-byte load brings 8 channels
@@ -327,6 +327,11 @@ __device__ __forceinline__ constexpr int chan0(int cb, int g) {
 template <int T, bool FUSED, bool GATED, bool SB16, int CONV, bool STREAM = false>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   static_assert(FUSED || !CONV, "the convolution prologue is a fused-step prologue");
+  // Write-through stores (STREAM): the stock verify's o and records on either
+  // pool; the fused step's S_n, o and records on FP32 pools only (on BF16
+  // pools its streaming instance keeps plain stores and only loads with the
+  // no-reuse hint).
+  constexpr bool kWriteThrough = STREAM && !(FUSED && SB16);
   using PI = Pairs<T>;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -795,7 +800,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
         ob_s[t][vrow] = bf16_bits_to_f32(f32_to_bf16_bits(o));
       } else {
         if (t < L) {
-          if constexpr (STREAM) {
+          if constexpr (kWriteThrough) {
             // Write-through like the pages; the descriptor spans the item's
             // T token rows of this head.
             const __amdgpu_buffer_rsrc_t out_rs =
@@ -810,7 +815,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
     if (rec >= 0) {
       const int64_t rbase = ((int64_t)rec * H + h) * p.rq;
-      if constexpr (STREAM) {
+      if constexpr (kWriteThrough) {
         // Write-through like the pages, within the item's record block.
         constexpr int CP = CPOL_NT | CPOL_SC1;
         const __amdgpu_buffer_rsrc_t corr_rs = page_rsrc(p.corr + rbase * V, p.rq * V * 4);
@@ -862,7 +867,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // no-reuse hint (nt) and leave no dirty lines behind.
   if constexpr (FUSED) {
     if (replay) {
-      constexpr int CPOL = STREAM ? (CPOL_NT | CPOL_SC1) : 0;
+      constexpr int CPOL = kWriteThrough ? (CPOL_NT | CPOL_SC1) : 0;
       const __amdgpu_buffer_rsrc_t page_rs = page_rsrc(page, PAGE * ES);
       const uint32_t tile_off = (uint32_t)(tile0 - page);
 #pragma unroll
@@ -874,22 +879,23 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
 }
 
-// Launch of one fused instance: over FP32 pages, the streaming one at two
-// workgroups per CU when the grid's pages (batch x heads x 64 KiB) exceed the
-// MALL. On the 2 GiB pool of the large decode batch that makes the step 2.4%
-// faster (the commit after it finds no dirty lines to write back), while
-// pages that fit in the MALL are best kept there. BF16 pages gain nothing
-// from it (the fused launch loses what the commit gains, and at two
-// workgroups per CU the step is 9% slower), so they keep plain stores.
+// Launch of one fused instance: the streaming one when the grid's pages (batch
+// x heads pages of 64 or 32 KiB) exceed the MALL. Over FP32 pages it writes
+// through at two workgroups per CU: on the 2 GiB pool of the large decode
+// batch the step is 2.4% faster (the commit after it finds no dirty lines to
+// write back), while pages that fit in the MALL are best kept there. BF16
+// pages gain nothing from the write-through stores (the fused launch loses
+// what the commit gains, and at two workgroups per CU the step is 9% slower):
+// their streaming instance keeps plain stores at its natural occupancy and
+// only loads its inputs and old records with the no-reuse hint (1% faster).
 template <int TT, bool G, bool B, int MODE>
 hipError_t launch_fused_instance(const VerifyParams& p, dim3 grid, hipStream_t stream) {
-  if constexpr (!B) {
-    if (stream_pages((int64_t)grid.x * grid.y * PAGE * 4)) {
-      static const size_t pad = two_per_cu_lds(&verify_kernel<TT, true, G, B, MODE, true>);
-      hipLaunchKernelGGL((verify_kernel<TT, true, G, B, MODE, true>), grid, dim3(256), pad,
-                         stream, p);
-      return hipGetLastError();
-    }
+  if (stream_pages((int64_t)grid.x * grid.y * PAGE * (B ? 2 : 4))) {
+    static const size_t pad =
+        B ? 0 : two_per_cu_lds(&verify_kernel<TT, true, G, B, MODE, true>);
+    hipLaunchKernelGGL((verify_kernel<TT, true, G, B, MODE, true>), grid, dim3(256), pad, stream,
+                       p);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((verify_kernel<TT, true, G, B, MODE, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();

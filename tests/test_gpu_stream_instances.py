@@ -30,19 +30,22 @@ def _assert_same(a, b, names):
         assert np.array_equal(_bits(a[name]), _bits(b[name])), f"{name} differs"
 
 
-@pytest.mark.parametrize("gated", [False, True])
-@pytest.mark.parametrize("T", [3, 8])
-def test_fused_streaming_instance_matches_plain(gated, T):
+@pytest.mark.parametrize("gated,T,pool", [(False, 3, "f32"), (True, 3, "f32"),
+                                          (False, 8, "f32"), (True, 8, "f32"),
+                                          (False, 8, "bf16"), (True, 5, "bf16")])
+def test_fused_streaming_instance_matches_plain(gated, T, pool):
     import spec_decode_amd as kda
-    B, RQ = 80, 8
+    bf16 = pool == "bf16"
+    es = 2 if bf16 else 4
+    B, RQ = (160 if bf16 else 80), 8
     page = H * V * K
-    assert B * page * 4 > MALL >= (B // 2) * page * 4
+    assert B * page * es > MALL >= (B // 2) * page * es
     S = B + 9
     g = W._gen(950 + gated)
     slots = (W.permutation(g, S - 1) + 1)[:B].to(torch.int32)
-    slots[[7, 45]] = 0
+    slots[[7, 45, B - 3]] = 0
     rows = W.permutation(g, B).to(torch.int32)
-    rows[[12, 60]] = -1
+    rows[[12, 60, B - 7]] = -1
     pending = W.uniform_int(g, 0, RQ, B).to(torch.int32)
     corr, kg = W.draw_records(g, B, H, RQ)
     a_log, dtb = W.draw_gate_params(g, 1, H)
@@ -51,7 +54,7 @@ def test_fused_streaming_instance_matches_plain(gated, T):
     if gated:
         gate, weight, eps = W.draw_output_stage(W._gen(952), B, T, H)
         extra = dict(gate=gate.to(DEV), norm_weight=weight.to(DEV), norm_eps=eps)
-    state0 = W.draw_state(953 + gated, S * page, torch.float32, DEV)
+    state0 = W.draw_state(953 + gated, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
 
     def fresh():
         return dict(state=state0.clone(), corr=corr.to(DEV), kg=kg.to(DEV),
@@ -72,7 +75,7 @@ def test_fused_streaming_instance_matches_plain(gated, T):
             kg=m["kg"], record_tokens=RQ, record_rows=rows[lo:hi].to(DEV),
             pending=m["pending"], out=m["out"][lo * T:hi * T], **ex)
 
-    announce(f"fused, streaming vs plain instance, H={H} B={B} q={T}, gated={gated}")
+    announce(f"fused, streaming vs plain instance, H={H} B={B} q={T}, gated={gated}, {pool}")
     one, two = fresh(), fresh()
     call(one, 0, B)
     call(two, 0, B // 2)

@@ -29,6 +29,12 @@
  *    the record arrays. Requests of one call must not share a destination,
  *    boundary or record row, and no request's source may be another request's
  *    destination (their pages would race).
+ *  - For that reason the pool's slot count and the record arrays' row count
+ *    are not arguments: the kernels would only carry them, since the indices
+ *    that must stay below them are device data that validation does not read.
+ *    The caller sizes the pool and the records; a Python binding that sees
+ *    the tensors can check them (spec_decode_amd checks the per-request arrays'
+ *    lengths against batch).
  *  - Base pointers, strides and row pitches must keep every 16-byte vector
  *    access aligned; the library rejects them otherwise.
  *  - A slot index <= null_slot means "no state" (padding rows).

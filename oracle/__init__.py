@@ -63,7 +63,7 @@ def _load():
                              d, _vp, ctypes.c_int64, _i32p, i, _fp, _u16p, i, _i32p,
                              _i32p, i, _u16p, _i64p, l, i, _u16p, _fp, d, i, _u16p,
                              ctypes.c_int64, _u16p, _u16p, _u16p, ctypes.c_int64,
-                             ctypes.c_int64, ctypes.c_int64, d, _i32p, _i32p, _i32p]),
+                             ctypes.c_int64, ctypes.c_int64, d, _i32p, _i32p, _i32p, _dp]),
         "kda_o_exp_f32": (ctypes.c_float, [ctypes.c_float]),
         "kda_o_silu_bf16": (ctypes.c_uint16, [ctypes.c_float]),
         "kda_o_conv_silu": (None, [i, _fp, _fp, ctypes.c_float, _u16p]),
@@ -259,7 +259,7 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
                 corr, kg, record_tokens, record_rows, pending, out, null_slot,
                 key_dim, value_dim, items, threads, gate=None, norm_weight=None,
                 norm_eps=1e-5, conv=None, query_start_loc=None, boundaries=None,
-                boundary_lens=None):
+                boundary_lens=None, o_raw=None):
     state_bf16 = isinstance(state, np.ndarray) and state.dtype == np.uint16
     qsl = None if query_start_loc is None else _c(query_start_loc, np.int32)
     if (boundaries is None) != (boundary_lens is None):
@@ -270,6 +270,10 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
     _check_inplace(corr, np.float32, "corr")
     _check_inplace(kg, np.uint16, "kg")
     _check_inplace(out, np.uint16, "out")
+    if o_raw is not None:
+        _check_inplace(o_raw, np.float64, "o_raw")
+        if o_raw.shape != out.shape:
+            raise ValueError("o_raw must have the shape of out")
     q, k, v, g = (None if x is None else _c(x, np.uint16) for x in (q, k, v, raw_g))
     if conv is None:
         cx = cw = cb = cs = None
@@ -304,17 +308,18 @@ def _verify_buf(fused, *, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
         _ptr(out, _u16p), ip, ni, default_threads() if threads is None else int(threads),
         _ptr(gt, _u16p), _ptr(nw, _fp), float(norm_eps), int(state_bf16),
         _ptr(cx, _u16p), cxs, _ptr(cw, _u16p), _ptr(cb, _u16p), _ptr(cs, _u16p), css, ccs,
-        cts, qsc, _ptr(qsl, _i32p), _ptr(bnd, _i32p), _ptr(blen, _i32p))
+        cts, qsc, _ptr(qsl, _i32p), _ptr(bnd, _i32p), _ptr(blen, _i32p), _ptr(o_raw, _dp))
 
 
 def verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log, dt_bias,
            lower_bound, state, state_slot_stride, state_indices, corr, kg,
            record_tokens, out, record_rows=None, null_slot=0, key_dim=128,
            value_dim=128, items=None, threads=None, gate=None, norm_weight=None,
-           norm_eps=1e-5, query_start_loc=None):
+           norm_eps=1e-5, query_start_loc=None, o_raw=None):
     """Stock verify: o (or, with gate and norm_weight, the gated RMSNorm of o)
     and records; the state is never written. The pool is FP32 (float32) or
-    BF16 (uint16 bits), by the dtype of ``state``."""
+    BF16 (uint16 bits), by the dtype of ``state``. ``o_raw`` (float64, the
+    shape of ``out``), when given, receives o before any rounding."""
     _verify_buf(False, heads=heads, tokens=tokens, batch=batch, q=q, k=k, v=v,
                 raw_g=raw_g, raw_beta=raw_beta, a_log=a_log, dt_bias=dt_bias,
                 lower_bound=lower_bound, state=state, state_slot_stride=state_slot_stride,
@@ -322,7 +327,7 @@ def verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log, dt_bias,
                 record_rows=record_rows, pending=None, out=out, null_slot=null_slot,
                 key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
                 gate=gate, norm_weight=norm_weight, norm_eps=norm_eps,
-                query_start_loc=query_start_loc)
+                query_start_loc=query_start_loc, o_raw=o_raw)
 
 
 def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log,
@@ -330,7 +335,7 @@ def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log
                         corr, kg, record_tokens, record_rows, pending, out, null_slot=0,
                         key_dim=128, value_dim=128, items=None, threads=None, gate=None,
                         norm_weight=None, norm_eps=1e-5, query_start_loc=None,
-                        boundaries=None, boundary_lens=None):
+                        boundaries=None, boundary_lens=None, o_raw=None):
     """Replay the pending tokens from the old records (writing S_n when n > 0,
     and S_min(m, n) to the boundary slot with boundaries), then the stock verify
     from S_n, rewriting the records."""
@@ -344,7 +349,7 @@ def fused_replay_verify(*, heads, tokens, batch, q, k, v, raw_g, raw_beta, a_log
                 key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
                 gate=gate, norm_weight=norm_weight, norm_eps=norm_eps,
                 query_start_loc=query_start_loc, boundaries=boundaries,
-                boundary_lens=boundary_lens)
+                boundary_lens=boundary_lens, o_raw=o_raw)
 
 
 def fused_conv_replay_verify(*, heads, tokens, batch, x, x_row_stride, conv_weight,
@@ -354,7 +359,7 @@ def fused_conv_replay_verify(*, heads, tokens, batch, x, x_row_stride, conv_weig
                              record_tokens, record_rows, pending, out, conv_bias=None,
                              null_slot=0, key_dim=128, value_dim=128, items=None,
                              threads=None, gate=None, norm_weight=None, norm_eps=1e-5,
-                             boundaries=None, boundary_lens=None):
+                             boundaries=None, boundary_lens=None, o_raw=None):
     """The fused step with the convolution prologue: q, k, v are the SiLU of a
     4-tap causal convolution of x (rows of ``x_row_stride``: q | k | v parts of
     H*K channels each) over each channel's window in ``conv_state`` (uint16 BF16,
@@ -375,7 +380,7 @@ def fused_conv_replay_verify(*, heads, tokens, batch, x, x_row_stride, conv_weig
                 record_rows=record_rows, pending=pending, out=out, null_slot=null_slot,
                 key_dim=key_dim, value_dim=value_dim, items=items, threads=threads,
                 gate=gate, norm_weight=norm_weight, norm_eps=norm_eps, conv=conv,
-                boundaries=boundaries, boundary_lens=boundary_lens)
+                boundaries=boundaries, boundary_lens=boundary_lens, o_raw=o_raw)
 
 
 def exp_f32(x):

@@ -545,6 +545,7 @@ struct verify_ctx {
   uint16_t* conv;         /* BF16 window pool */
   int64_t conv_ss, conv_cs, conv_ts; /* slot, channel, tap strides (elements) */
   double q_scale;
+  double* o_raw;          /* optional: o before any rounding, laid out as out (a check aid) */
 };
 
 /* The prologue of one item: per part p (0 q, 1 k, 2 v) and channel, the window
@@ -620,8 +621,10 @@ static void verify_item(void* p, long it) {
   int slot = c->slots[b];
   if (slot <= c->null_slot) {
     for (int t = 0; t < T; ++t)
-      for (int v = 0; v < V; ++v)
+      for (int v = 0; v < V; ++v) {
         c->out[(tok0 + t) * H * V + (int64_t)h * V + v] = kda_o_double_to_bf16(0.0);
+        if (c->o_raw) c->o_raw[(tok0 + t) * H * V + (int64_t)h * V + v] = 0.0;
+      }
     return;
   }
   int rec = c->rows ? c->rows[b] : b;
@@ -708,6 +711,8 @@ static void verify_item(void* p, long it) {
 
   for (int t = 0; t < T; ++t) {
     uint16_t* orow = c->out + (tok0 + t) * H * V + (int64_t)h * V;
+    if (c->o_raw)
+      for (int v = 0; v < V; ++v) c->o_raw[(tok0 + t) * H * V + (int64_t)h * V + v] = o[t * V + v];
     if (c->gate && c->norm_w) {
       gated_rmsnorm(V, o + t * V, c->gate + (tok0 + t) * H * V + (int64_t)h * V,
                     c->norm_w, c->norm_eps, orow);
@@ -751,7 +756,7 @@ int kda_o_verify(int H, int T, int B, int K, int V, const uint16_t* q, const uin
                  const uint16_t* conv_w, const uint16_t* conv_b, uint16_t* conv,
                  int64_t conv_ss, int64_t conv_cs, int64_t conv_ts, double q_scale,
                  const int32_t* query_start_loc, const int32_t* boundaries,
-                 const int32_t* boundary_lens) {
+                 const int32_t* boundary_lens, double* o_raw) {
   struct verify_ctx c = {H,          T,          B,       K,          V,
                          RQ,         fused,      state_bf16, q,       k,          v,
                          raw_g,      raw_beta,   a_log,   dt_bias,    lower_bound,
@@ -760,7 +765,7 @@ int kda_o_verify(int H, int T, int B, int K, int V, const uint16_t* q, const uin
                          gate,       norm_w,     norm_eps, query_start_loc, boundaries,
                          boundary_lens, x, x_stride,
                          conv_w,     conv_b,     conv,    conv_ss,    conv_cs,
-                         conv_ts,    q_scale};
+                         conv_ts,    q_scale,    o_raw};
   long count = items ? n_items : (long)B * H;
   parallel_for(count, threads, verify_item, &c);
   return 0;
@@ -779,42 +784,74 @@ void kda_o_decay_buf(long N, int H, int K, const uint16_t* raw_g, const float* a
       }
 }
 
-/* Defer step ([kernels page] _defer_commit_kernel): for each request with a
- * record row >= 0 and a state slot > null, its commit length becomes the
- * pending count of its record row and its commit length becomes 0; an eager
- * request instead gets pending 0 and keeps its commit length. Other requests
- * change nothing. */
+/* Plan steps of deferred RecoverSSM ([kernels page], the descriptions of
+ * _defer_commit_kernel and _prepare_flush_plan_kernel), stated as a table:
+ * every request is first given a class from its inputs, and each class then has
+ * one fixed effect on the plan arrays. */
+enum kda_o_plan_class {
+  PLAN_UNTOUCHED, /* no state slot (padding, dummy rows) or no record slot */
+  PLAN_DEFERRED,  /* its accepted tokens wait in its record slot */
+  PLAN_COMMITTED  /* committed now by the caller (eager) */
+};
+
+static enum kda_o_plan_class plan_class(int slot, int record_row, int eager, int null_slot) {
+  if (slot <= null_slot || record_row < 0) return PLAN_UNTOUCHED;
+  return eager ? PLAN_COMMITTED : PLAN_DEFERRED;
+}
+
+/* Defer: a deferred request's commit length becomes the pending replay of its
+ * record slot and no commit runs for it (its length becomes 0); a committed
+ * one leaves nothing pending and keeps its plan; an untouched one changes no
+ * pending count and no length. */
 void kda_o_defer(int B, const int32_t* state_indices, int32_t* commit_lens,
                  const int32_t* record_rows, int32_t* pending, const int32_t* eager,
                  int null_slot) {
+  enum kda_o_plan_class* cls = (enum kda_o_plan_class*)malloc(sizeof(*cls) * (size_t)(B > 0 ? B : 1));
+  for (int b = 0; b < B; ++b)
+    cls[b] = plan_class(state_indices[b], record_rows[b], eager ? eager[b] != 0 : 0, null_slot);
   for (int b = 0; b < B; ++b) {
-    int rec = record_rows[b];
-    if (rec < 0 || state_indices[b] <= null_slot) continue;
-    if (eager && eager[b] != 0) {
-      pending[rec] = 0;
-    } else {
-      pending[rec] = commit_lens[b];
-      commit_lens[b] = 0;
+    switch (cls[b]) {
+      case PLAN_DEFERRED:
+        pending[record_rows[b]] = commit_lens[b];
+        commit_lens[b] = 0;
+        break;
+      case PLAN_COMMITTED:
+        pending[record_rows[b]] = 0;
+        break;
+      case PLAN_UNTOUCHED:
+        break;
     }
   }
+  free(cls);
 }
 
-/* Flush plan ([kernels page] _prepare_flush_plan_kernel): the plan of an
- * in-place commit of every request's pending replay. pending is only read. */
+/* Flush plan: the commit that folds each request's pending replay into its
+ * own checkpoint in place. Request b's entry: the commit reads and writes its
+ * own slot (final index = its slot), stores no boundary (null slot, length
+ * 0), and replays the pending count of its record slot, clamped to the window
+ * [0, spec_query_len]; a request without a state slot, without a record slot
+ * or with nothing pending replays nothing. The pending counts are read only. */
+struct kda_o_flush_entry {
+  int32_t len, final_slot, boundary, boundary_len;
+};
+
 void kda_o_flush_plan(int B, int spec_query_len, const int32_t* state_indices,
                       const int32_t* record_rows, const int32_t* pending, int32_t* commit_lens,
                       int32_t* final_indices, int32_t* boundaries, int32_t* boundary_lens,
                       int null_slot) {
   for (int b = 0; b < B; ++b) {
-    int src = state_indices[b];
-    int rec = record_rows[b];
-    int n = rec >= 0 ? pending[rec] : 0;
-    if (n < 0) n = 0;
-    if (n > spec_query_len) n = spec_query_len;
-    commit_lens[b] = (src > null_slot && n > 0) ? n : 0;
-    final_indices[b] = src;
-    boundaries[b] = null_slot;
-    boundary_lens[b] = 0;
+    const int slot = state_indices[b];
+    const int waiting = record_rows[b] >= 0 ? pending[record_rows[b]] : 0;
+    const int replay = waiting < 0 ? 0 : (waiting > spec_query_len ? spec_query_len : waiting);
+    struct kda_o_flush_entry e;
+    e.final_slot = slot;
+    e.boundary = null_slot;
+    e.boundary_len = 0;
+    e.len = (slot > null_slot) ? replay : 0;
+    commit_lens[b] = e.len;
+    final_indices[b] = e.final_slot;
+    boundaries[b] = e.boundary;
+    boundary_lens[b] = e.boundary_len;
   }
 }
 

@@ -97,13 +97,14 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   // pages in turn, instead of every eighth head of the requests in flight
   // (large decode FP32 commit 0.662 -> 0.650 ms, 8-layer align 1.050 ->
   // 0.975 ms; the 1 GiB BF16 in-place commit 0.347 -> 0.357 ms).
-  int lin = blockIdx.x + blockIdx.y * gridDim.x;
+  // Unsigned: heads x batch reaches 65535^2, above INT_MAX but below 2^32.
+  uint32_t lin = blockIdx.x + blockIdx.y * gridDim.x;
   if constexpr (STREAM) {
-    const int per_layer = gridDim.x * gridDim.y;
-    if ((per_layer & 7) == 0) lin = (lin & 7) * (per_layer >> 3) + (lin >> 3);
+    const uint32_t per_layer = gridDim.x * gridDim.y;
+    if ((per_layer & 7u) == 0) lin = (lin & 7u) * (per_layer >> 3) + (lin >> 3);
   }
-  const int h = lin % gridDim.x;
-  const int b = lin / gridDim.x;
+  const int h = (int)(lin % gridDim.x);
+  const int b = (int)(lin / gridDim.x);
   const int l = blockIdx.z;
   const int tid = threadIdx.x;
 

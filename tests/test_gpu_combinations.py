@@ -66,6 +66,11 @@ def test_random_combination(seed):
     qsl = None
     out_rows = B * T
     win = window_np(W.draw_window(g, B, T, H))
+    # Half the combinations also rescale every key, in the window and in the
+    # records, to norms from W.KEY_NORMS (drawn apart, so the other draws stay).
+    keyscale = bool(np.random.default_rng(2500 + seed).integers(2))
+    if keyscale:
+        kg = W.rescale_record_keys(W._gen(2600 + seed), kg)
     if c["varlen"]:
         lens = r.integers(0, T + 2, B)
         qsl = np.zeros(B + 1, np.int32)
@@ -73,6 +78,10 @@ def test_random_combination(seed):
         out_rows = int(qsl[-1]) + 1
         big = window_np(W.draw_window(g, max(out_rows // T + 1, B), T, H))
         win = {k: np.ascontiguousarray(v[:out_rows]) for k, v in big.items()}
+    if keyscale:
+        kt = torch.from_numpy(win["k"].view(np.int16)).view(torch.bfloat16)
+        win["k"] = W.bits(W.rescale_keys(W._gen(2700 + seed), kt))
+        c["keyscale"] = True
     kw = {}
     if c["gated"]:
         gate, weight, eps = W.draw_output_stage(W._gen(5000 + seed), max(out_rows // T + 1, B),

@@ -200,6 +200,41 @@ def test_large_decode_gate_projection_sampled():
 
 # ---------------------------------------------------------------- config 3
 
+def test_large_decode_gate_projection_general_factors():
+    """The gate projection at the large decode batch's size with general BF16
+    factors, as the benchmark step draws them (F_A = BF16(N(0, 1)), F_B =
+    BF16(N(0, 1) / sqrt(128))): the kernel sums in FP32 on matrix cores and
+    rounds once (fused page, KdaFused.kernel, the gate projection), so an
+    element whose exact sum lies within FP32 error of a BF16 rounding boundary
+    may round to the other neighbour. Against the oracle on 512 sampled
+    tokens: within one ulp everywhere and at least 99.9% bit-equal; every
+    token against the FP64 product rounded once: within one ulp."""
+    import spec_decode_amd as kda
+    from _compare import bf16_mismatch
+    N, H = 512 * 8, 64
+    hk = H * K
+    pitch = (4 * hk + 128 + H + 7) // 8 * 8
+    fa, fb = W.draw_gate_factors(W._gen(4 + 410), N, H, exact=False)
+    packed = W.bf16(W.normal(W._gen(4 + 411), (N, pitch))).to(DEV)
+    packed[:, 4 * hk:4 * hk + K] = fa.to(DEV)
+    out = torch.zeros((N, hk), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(0x7FFF)
+    announce("large decode gate projection, general factors")
+    kda.kda_gate_projection(tokens=N, heads=H, f_a=packed[:, 4 * hk:], f_a_row_stride=pitch,
+                            f_b=fb.to(DEV), raw_g=out)
+    torch.cuda.synchronize()
+    got = np_of(out)
+    fa_b, fb_b = W.bits(fa), W.bits(fb)
+    pick = np.random.default_rng(8).choice(N, 512, replace=False)
+    want = oracle.gate_projection(fa_b[pick], fb_b)
+    assert not bf16_mismatch(got[pick], want).any()
+    equal = float(np.mean(got[pick] == want))
+    announce(f"gate projection, general factors: {100 * equal:.4f}% bit-equal to the oracle")
+    assert equal >= 0.999
+    prod = oracle.bf16_to_f64(fa_b) @ oracle.bf16_to_f64(fb_b).T
+    assert not bf16_mismatch(got, oracle.round_bf16(prod)).any()
+
+
 def test_config3_align_commit_full_size_sampled():
     import spec_decode_amd as kda
 

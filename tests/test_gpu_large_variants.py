@@ -10,8 +10,9 @@ import torch
 
 import oracle
 import workloads as W
-from _compare import GATED_OUT_ULPS, assert_bf16_close, assert_exact, assert_f32_close
-from _kda_cases import DEV, announce, conv_pool_layout, dev, dev_bf16, np_of, window_np
+from _compare import assert_bf16_close, assert_exact, assert_f32_close, assert_gated_close
+from _kda_cases import (DEV, announce, check_conv_keys_plain, conv_pool_layout, dev, dev_bf16,
+                        np_of, window_np)
 
 pytestmark = pytest.mark.gpu
 K = V = 128
@@ -59,12 +60,18 @@ def _compact(R, slots, rows, pending_row, corr, kg, pages, state_dtype=np.float3
     return m
 
 
-def _check(label, R, m, m_out, g_out, g_pages, g_corr, g_kg, slots, rows, ulps, bf16=False):
+def _check(label, R, m, m_out, g_out, g_pages, g_corr, g_kg, slots, rows, o_raw=None,
+           bf16=False):
+    """o_raw: the oracle's unrounded o of the gated stage (else plain o)."""
     page = H * V * K
     close = assert_bf16_close if bf16 else assert_f32_close
     for j, b in enumerate(R):
-        assert_bf16_close(f"{label} out request {b}", g_out[b * T:(b + 1) * T],
-                          m_out[j * T:(j + 1) * T], ulps)
+        if o_raw is not None:
+            assert_gated_close(f"{label} out request {b}", g_out[b * T:(b + 1) * T],
+                               m_out[j * T:(j + 1) * T], o_raw[j * T:(j + 1) * T])
+        else:
+            assert_bf16_close(f"{label} out request {b}", g_out[b * T:(b + 1) * T],
+                              m_out[j * T:(j + 1) * T])
         if slots[b] > 0:
             close(f"{label} page request {b}", g_pages(int(slots[b])),
                   m["state"][(j + 1) * page:(j + 2) * page])
@@ -112,6 +119,7 @@ def test_large_decode_gated_output_sampled():
                  lambda sl: np_of(before[sl * page:(sl + 1) * page]))
     m_win = {k: np.ascontiguousarray(v[m["tok"]]) for k, v in win.items()}
     m_out = np.zeros((len(R) * T, H * V), np.uint16)
+    o_raw = np.zeros((len(R) * T, H * V), np.float64)
     announce(f"large decode gated: oracle on {len(R)} sampled requests")
     oracle.fused_replay_verify(heads=H, tokens=T, batch=len(R), q=m_win["q"], k=m_win["k"],
                                v=m_win["v"], raw_g=m_win["raw_g"], raw_beta=m_win["raw_beta"],
@@ -120,9 +128,9 @@ def test_large_decode_gated_output_sampled():
                                corr=m["corr"], kg=m["kg"], record_tokens=RQ,
                                record_rows=m["rows"], pending=m["pend"], out=m_out,
                                gate=np.ascontiguousarray(gate_bits[m["tok"]]),
-                               norm_weight=weight.numpy(), norm_eps=eps)
+                               norm_weight=weight.numpy(), norm_eps=eps, o_raw=o_raw)
     _check("gated", R, m, m_out, np_of(out), lambda sl: np_of(d_state[sl * page:(sl + 1) * page]),
-           np_of(d_corr), np_of(d_kg), slots, rows, GATED_OUT_ULPS)
+           np_of(d_corr), np_of(d_kg), slots, rows, o_raw)
     del d_state, before
     torch.cuda.empty_cache()
 
@@ -181,10 +189,16 @@ def test_large_decode_conv_prologue_packed_pool_sampled(bf16):
         state_indices=m["slots"], corr=m["corr"], kg=m["kg"], record_tokens=RQ,
         record_rows=m["rows"], pending=m["pend"], out=m_out)
     _check("conv", R, m, m_out, np_of(out), lambda sl: np_of(d_state[sl * page:(sl + 1) * page]),
-           np_of(d_corr), np_of(d_kg), slots, rows, 1, bf16)
+           np_of(d_corr), np_of(d_kg), slots, rows, bf16=bf16)
     m_pool = flat.reshape(nR + 1, 3 * H * K, RQ + 2)
     for j, b in enumerate(R):
         if slots[b] > 0:
             assert_exact(f"conv windows request {b}", g_pool[int(slots[b])], m_pool[j + 1])
+    # The recorded keys against the plain FP64 convolution and SiLU.
+    share = check_conv_keys_plain("conv", np_of(d_kg), H=H, T=T, RQ=RQ, x=x, pitch=cv.pitch,
+                                  conv_w=w_bits, conv_b=b_bits, pool=pool, strides=strides,
+                                  slots=slots[R], rows=rows[R], pending=pending_row,
+                                  tok_of=lambda j: R[j] * T)
+    announce(f"large decode conv: keys match the plain SiLU ({100 * share:.3f}% near a tie)")
     del d_state, before
     torch.cuda.empty_cache()

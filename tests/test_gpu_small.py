@@ -173,6 +173,46 @@ def _vf_case(seed, H, B, T, RQ, S, null_rows=(), norec_rows=(), bf16=False):
                 win=window_np(c["window"]))
 
 
+def _rescaled(bits_np, seed, records=False):
+    """Window keys [N, H, K] or key/gate records [..., 2K] (uint16 bits) with
+    each key rescaled to a norm from W.KEY_NORMS (0, 1e-4, 1e-2, 1, 30)."""
+    t = torch.from_numpy(bits_np.view(np.int16)).view(torch.bfloat16)
+    g = W._gen(seed)
+    return W.bits(W.rescale_record_keys(g, t) if records else W.rescale_keys(g, t))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("kind", ["verify", "fused", "commit"])
+def test_key_norm_edge(kind, bf16):
+    """Keys of norm 0, 1e-4, 1e-2, 1 and 30, in the window and in the records:
+    every use normalises k by (sum k^2 + 1e-6)^-1/2 (commit page, KdaCommit
+    kernel; fused page, KdaFused.kernel, the new and the recorded keys), so the
+    eps dominates at 1e-4, matters at 1e-2, and a zero key contributes nothing."""
+    H, T, RQ = 3, 8, 8
+    if kind == "commit":
+        B, L, S = 6, 1, 16
+        states, strides, corrs, kgs, a_log, dtb = _commit_inputs(1300, L, H, B, RQ, bf16, S)
+        kgs = [_rescaled(kgs[0], 1301, records=True)]
+        src = np.arange(1, B + 1, dtype=np.int32)
+        lens = np.array([8, 8, 5, 3, 1, 8], np.int32)
+        run_commit_case(H=H, B=B, Q=RQ, bf16=bf16, layers_state=states, strides=strides,
+                        corr_layers=corrs, kg_layers=kgs, a_log=a_log, dt_bias=dtb, src=src,
+                        lens=lens, dst=src.copy(), label=f"commit key norms bf16={bf16}")
+        return
+    B = 6
+    c = _vf_case(1310 + bf16, H, B, T, RQ, 10, bf16=bf16)
+    win = dict(c["win"])
+    win["k"] = _rescaled(win["k"], 1320)
+    kg = _rescaled(c["kg"], 1321, records=True)
+    pending = np.full(B, RQ, np.int32)
+    pending[:3] = [0, 3, 5]
+    run_verify_case(fused=kind == "fused", H=H, B=B, T=T, RQ=RQ, state=c["state"],
+                    slots=c["slots"], corr=c["corr"], kg=kg, a_log=c["a_log"],
+                    dt_bias=c["dt_bias"], win=win, rows=c["rows"],
+                    pending=pending if kind == "fused" else None,
+                    label=f"{kind} key norms bf16={bf16}")
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_verify_windows(T, bf16):
@@ -269,6 +309,31 @@ def test_gated_output_stage(T, fused, bf16):
                     win=c["win"], rows=c["rows"], pending=pending if fused else None,
                     gate=W.bits(gate), norm_weight=weight.numpy(), norm_eps=eps,
                     label=f"gated output fused={fused} T={T}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_gated_output_rounding_point_exact(fused):
+    """The hand-derived case whose gated output depends on rounding o to BF16
+    both in the sum of squares and in the product (fused page, KdaFused.kernel,
+    the output stage): the kernel must give the closed-form bits exactly."""
+    import spec_decode_amd as kda
+    from _pinned_cases import gated_rounding_case
+    args, want, _ = gated_rounding_case()
+    announce(f"gated output rounding point, fused={fused}")
+    out = torch.zeros((1, V), dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(0x7FFF)
+    d = {}
+    for name, val in args.items():
+        if isinstance(val, np.ndarray):
+            d[name] = dev_bf16(val) if val.dtype == np.uint16 else dev(val)
+        else:
+            d[name] = val
+    if fused:
+        kda.kda_fused_replay_verify(out=out, pending=dev(np.zeros(1, np.int32)), **d)
+    else:
+        kda.kda_verify(out=out, **d)
+    torch.cuda.synchronize()
+    assert_exact("gated rounding-point output", np_of(out)[0], want)
 
 
 # ---------------------------------------------------------------- fused + convolution

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import workloads as W
+from _pinned_cases import gated_rounding_case
 
 K = V = 128
 
@@ -380,6 +381,31 @@ def test_gated_rmsnorm_eps_dominated_exact():
     gated = _gated_run(c, H, B, T, RQ, s0.copy(), gate_val=60.0, eps=2.0 ** 24)
     _, _, _, plain = _run_verify(c, H, B, T, RQ, False, state=s0.copy())
     assert np.array_equal(oracle.bf16_to_f64(gated), oracle.bf16_to_f64(plain) * 2.0 ** -12)
+
+
+def test_gated_rmsnorm_rounds_o_before_both_uses():
+    """The output stage's BF16 rounding of o, pinned at both of its uses by the
+    hand-derived case above: exact expected bits, and the raw o exported for
+    the GPU tests' near-tie flags equals S_0[:, 0] exactly."""
+    args, want, a = gated_rounding_case()
+    out = np.zeros((1, V), np.uint16)
+    o_raw = np.zeros((1, V), np.float64)
+    oracle.verify(out=out, o_raw=o_raw, **args)
+    assert np.array_equal(out[0], want), [hex(x) for x in out[0, :4]]
+    assert o_raw[0, 0] == a and o_raw[0, 1] == 2.0 ** -4 and not o_raw[0, 2:].any()
+    # The fused step from the same slot with nothing pending gives the same row.
+    out_f = np.zeros((1, V), np.uint16)
+    oracle.fused_replay_verify(out=out_f, pending=np.zeros(1, np.int32),
+                               **{k: (v.copy() if isinstance(v, np.ndarray) else v)
+                                  for k, v in args.items()})
+    assert np.array_equal(out_f, out)
+    # The case discriminates: the values each dropped rounding would give lie on
+    # the other side of a rounding boundary (closed forms from the docstring).
+    bf = lambda x: int(oracle.round_bf16(np.array([x]))[0])
+    rstd = np.sqrt(128.0 / (1.0 + 2.0 ** -8))
+    w = args["norm_weight"].astype(np.float64)
+    assert bf(2.0 ** -4 * np.sqrt(128.0 / (a * a + 2.0 ** -8)) * w[1]) == 0x3F7F
+    assert bf(a * rstd * w[0]) == 0x3F81
 
 
 def test_fused_bf16_state_matches_fp32_state():

@@ -316,3 +316,34 @@ def test_q_normalisation_and_scale_closed_form(tiny):
             want = oracle.round_bf16(beta * yv * scale * ss / (ss + EPS))
             got = out[b, h * V:(h + 1) * V]
             assert np.all(_ulps(got, want) <= 1), (b, h)
+
+
+@pytest.mark.parametrize("dim_first", [True, False])
+def test_plain_silu_key_check_on_the_oracle(dim_first):
+    """The GPU tests' check of the recorded keys against the plain FP64
+    convolution and SiLU (check_conv_keys_plain) passes on the oracle's own
+    records for every window offset, with a small near-tie share; and it fails
+    when a key is one ulp off outside the band."""
+    from _kda_cases import check_conv_keys_plain
+    H, B, T, RQ, S = 2, 4, 4, 6, 6
+    c, cv, pool, strides = _setup(29, H, B, T, RQ, S, dim_first)
+    rows = _np(c["record_rows"])
+    pending = np.zeros(B, np.int32)
+    pending[rows] = np.array([0, 1, 4, RQ])
+    before = pool.copy()
+    _, _, kg, _ = _run(c, cv, pool, strides, H, B, T, RQ, pending.copy())
+    kw = dict(H=H, T=T, RQ=RQ, x=_np(cv.x), pitch=cv.pitch, conv_w=_np(cv.weight),
+              conv_b=_np(cv.bias), pool=before, strides=strides,
+              slots=_np(c["state_indices"]), rows=rows, pending=pending)
+    share = check_conv_keys_plain("oracle", kg, **kw)
+    assert share < 0.01
+    # a planted one-ulp error on a key far from a tie is caught
+    from _kda_cases import silu_keys_plain
+    want, near = silu_keys_plain(H=H, T=T, RQ=RQ, x=kw["x"], pitch=cv.pitch, conv_w=kw["conv_w"],
+                                 conv_b=kw["conv_b"], pool=before, strides=strides,
+                                 slot=int(kw["slots"][0]), n=int(pending[rows[0]]), tok0=0)
+    h, t, ch = np.argwhere(~near & (want != 0))[0]
+    bad = kg.copy()
+    bad[rows[0], h, t, ch] ^= 1
+    with pytest.raises(AssertionError):
+        check_conv_keys_plain("planted", bad, **kw)

@@ -13,7 +13,9 @@ Distributions (sigma is the standard deviation):
   rounded to BF16; q = BF16(N(0, 1) * 128^-0.5); v, raw_g, raw_beta = BF16(N(0, 1));
 * A_log ~ N(0, 0.5), dt_bias ~ N(0, 0.1) (FP32), lower bound -5, null slot 0;
 * records: corrections ~ N(0, 0.5) FP32; key/gate = unit keys as above, then
-  raw gates BF16(N(0, 1)).
+  raw gates BF16(N(0, 1));
+* for the key-normalisation edge cases, keys rescaled per vector to a norm
+  drawn from KEY_NORMS (0, 1e-4, 1e-2, 1, 30).
 
 BF16 rounding is round-to-nearest-even (torch's FP32 -> BF16 conversion).
 Everything is drawn from ``torch.Generator`` objects seeded per workload; the
@@ -145,6 +147,27 @@ def draw_records(gen, rows: int, H: int, RQ: int):
     gates = bf16(normal(gen, (rows, H, RQ, K)))
     kg = torch.cat([keys, gates], dim=-1).contiguous()
     return corr, kg
+
+
+# Key norms for the normalisation edge: the all-zero key, norms whose squares
+# (1e-8, 1e-4) are below or near the 1e-6 added inside the root, the unit
+# norm of the workloads, and a large one.
+KEY_NORMS = (0.0, 1e-4, 1e-2, 1.0, 30.0)
+
+
+def rescale_keys(gen, keys: torch.Tensor, norms=KEY_NORMS) -> torch.Tensor:
+    """BF16 keys (last axis K, unit norm) rescaled per vector to a norm drawn
+    uniformly from ``norms`` (0 gives the all-zero key), rounded to BF16 again."""
+    idx = torch.randint(0, len(norms), keys.shape[:-1], generator=gen)
+    scale = torch.tensor(norms, dtype=torch.float32)[idx]
+    return bf16(keys.float() * scale[..., None])
+
+
+def rescale_record_keys(gen, kg: torch.Tensor, norms=KEY_NORMS) -> torch.Tensor:
+    """Key/gate records [..., 2K] with their key halves rescaled as rescale_keys."""
+    out = kg.clone()
+    out[..., :K] = rescale_keys(gen, kg[..., :K], norms)
+    return out
 
 
 def draw_state(seed: int, n_elems: int, dtype, device="cpu", chunk=1 << 26) -> torch.Tensor:

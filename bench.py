@@ -72,7 +72,7 @@ def parse_args():
     ap.add_argument("--conv", action="store_true",
                     help="run the fused step with its convolution prologue (q, k, v from "
                          "packed pre-activations and a window pool)")
-    ap.add_argument("--conv-layout", choices=("dim_first", "window_major"), default="dim_first",
+    ap.add_argument("--conv-layout", choices=("dim_first", "window_major"), default="window_major",
                     help="window pool layout with --conv: [slot][3HK][RQ+2] (each channel's "
                          "window contiguous) or [slot][RQ+2][3HK] (each window entry a "
                          "contiguous row of channels)")
@@ -85,7 +85,46 @@ def parse_args():
                          "outside the timed events)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 2 GiB device copy (streaming ceiling)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="no GPU run: summarise a rocprofv3 kernel-trace or counter-collection "
+                         "CSV of a run of this script (per kernel: launches, then the mean "
+                         "duration and counters of the last --steps launches, i.e. the timed "
+                         "steps without the warm-up ones)")
     return ap.parse_args()
+
+
+def trace_summary(path, last):
+    """Per-kernel figures from a rocprofv3 CSV of a run of this script: a
+    --kernel-trace CSV gives durations, a --pmc counter-collection CSV gives
+    counter values per dispatch. Reported: all launches, and the mean (min,
+    max for durations) over the last `last` launches of each kernel (the run's
+    timed steps, without its warm-up launches)."""
+    import csv
+    disp = {}  # kernel -> {dispatch id: {"t": (t0, t1), counter: value}}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("KernelName") or row.get("Name")
+            did = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            rec = disp.setdefault(name, {}).setdefault(did, {})
+            rec["t"] = (int(row.get("Start_Timestamp")), int(row.get("End_Timestamp")))
+            if row.get("Counter_Name"):
+                c = row["Counter_Name"]
+                rec[c] = rec.get(c, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for name, recs in disp.items():
+        order = sorted(recs.values(), key=lambda r: r["t"][0])
+        tail = order[-last:]
+        d = [(r["t"][1] - r["t"][0]) / 1e3 for r in order]
+        dt = d[-last:]
+        o = {"launches": len(d), "all_mean_us": round(sum(d) / len(d), 2),
+             "timed_launches": len(dt), "timed_mean_us": round(sum(dt) / len(dt), 2),
+             "timed_min_us": round(min(dt), 2), "timed_max_us": round(max(dt), 2)}
+        counters = sorted({k for r in tail for k in r if k != "t"})
+        if counters:
+            o["counters_timed_mean"] = {c: round(sum(r.get(c, 0.0) for r in tail) / len(tail), 1)
+                                        for c in counters}
+        out[name] = o
+    return out
 
 
 def source_digest(paths):
@@ -445,6 +484,7 @@ def bench_kernel_workload(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic", "config": {"workload": workload, "kernel": name,
                                         "mall_evicted": scratch is not None},
+        "library": os.path.relpath(kda.library_path(), ROOT),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "items_per_s": round(items / (mean_ms * 1e-3), 1),
         "kernels": {name: {"mean_ms": round(mean_ms, 4), "min_ms": round(min(ms), 4),
@@ -461,6 +501,11 @@ def bench_kernel_workload(args):
 
 def main():
     args = parse_args()
+    if args.trace_summary:
+        for name, rec in sorted(trace_summary(args.trace_summary, args.steps).items(),
+                                key=lambda kv: -kv[1]["timed_mean_us"]):
+            print(json.dumps({"kernel": name, **rec}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
               "shards by request or head with no collective: run one process per GPU)",
@@ -669,6 +714,7 @@ def main():
             "conv_layout": args.conv_layout if args.conv else None,
             "gate_projection": bool(args.gate_proj),
         },
+        "library": os.path.relpath(kda.library_path(), ROOT),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "items_per_s": round(items / (wall / args.steps), 1),
         "kernels": {

@@ -350,8 +350,10 @@ int kda_flush_plan(int batch, int spec_query_len, const int32_t* state_indices,
 /*
  * kda_page_rw_probe — measurement aid, not a step of the method: loads every
  * page of every named slot (state_indices[b] > null_slot, all heads) and stores
- * it back unchanged, in the fused kernel's access pattern (16x16 tiles, one
- * 16-byte load and store per lane and tile, one workgroup per page). Its rate
+ * it back unchanged, in the access pattern of the fused kernel over FP32 pools
+ * larger than the memory-side cache (contiguous 1 KiB pieces per wave load
+ * with the no-reuse hint, an LDS transpose to 16x16 tiles, one write-through
+ * 16-byte store per lane and tile, one workgroup per page). Its rate
  * is the in-place read+write ceiling of the pool on the running GPU; the
  * benchmark reports its kernels against it next to the HBM peak. The pool's
  * contents are unchanged. Arguments as kda_fused_replay_verify's state,

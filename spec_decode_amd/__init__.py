@@ -24,7 +24,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkda.so")
+# KDA_LIBRARY names another build of the same library (a measurement variant,
+# see build.py); by default the in-tree libkda.so.
+_LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_EINVAL, KDA_ELAUNCH = 0, 1, 2
 KDA_STATE_F32, KDA_STATE_BF16 = 0, 1

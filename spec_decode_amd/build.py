@@ -43,20 +43,35 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+# Measurement variants: built on request only, each into a directory of its own
+# (load one with KDA_LIBRARY=<path> to time it in place of the product library).
+VARIANTS = {
+    # the verify kernel's row dots on plain FP32 FMAs instead of MFMA
+    "valu_dots": ["-DKDA_VALU_DOTS=1"],
+}
+
+
+def build(verbose: bool = False, extra=(), variant: str = "") -> str:
+    obj_dir, lib = OBJ, LIB
+    if variant:
+        extra = (*extra, *VARIANTS[variant])
+        obj_dir = os.path.join(OBJ, variant)
+        lib = os.path.join(HERE, "_variants", variant, "libkda.so")
+        os.makedirs(os.path.dirname(lib), exist_ok=True)
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     cmds = [[HIPCC, *FLAGS, *extra, "-c", "-o", o, os.path.join(CSRC, s)]
             for s, o in zip(SOURCES, objs)]
     jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(jobs) as pool:
         for f in [pool.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    var = next((a.split("=", 1)[1] for a in sys.argv[1:] if a.startswith("--variant=")), "")
+    print(build(verbose="-v" in sys.argv, variant=var))

@@ -75,7 +75,20 @@
 
 #include "kda_device.h"
 
+// A measurement variant, never built by default: with -DKDA_VALU_DOTS=1 the
+// instances over FP32 pages form the 2T row dots ([V x K] x [K x 2T] per item)
+// with plain FP32 FMAs instead of MFMA: after the state pass, one dot column
+// at a time, each lane sums its 32 channels of its two rows from the page
+// registers and the row's four lane groups add their sums by lane exchanges
+// (the replay keeps its MFMAs). It exists to time the MFMA choice for this
+// product against the vector ALU on the same kernel.
+#ifndef KDA_VALU_DOTS
+#define KDA_VALU_DOTS 0
+#endif
+
 namespace kda {
+
+constexpr bool kValuDots = KDA_VALU_DOTS != 0;
 
 template <int T>
 struct Pairs {
@@ -261,12 +274,6 @@ __device__ __forceinline__ void conv_load(const VerifyParams& p, ConvIn<T>& ci, 
   }
 }
 
-// Orders one wave's LDS accesses across its lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // The window write-back [tap 1, tap 2, x_0 .. x_{T-1}] (entries past T + 1 keep
 // their values; the thread rewrites only entries of its own channel), then the
@@ -317,47 +324,6 @@ __device__ __forceinline__ void conv_part(const VerifyParams& p, const ConvIn<T>
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = bf16_bits_to_f32(ci.w[i]);
   conv_silu<T>(seq, w, bf16_bits_to_f32(ci.bias), y);
-}
-
-// Contiguous page loads (the streaming instances over FP32 pages).
-// Wave w loads its 32 rows (16 KiB) as 16 contiguous 1 KiB pieces with the
-// no-reuse hint: piece j, lane l holds row 32w + 2j + l/32, channels
-// 4(l%32) .. +3. On the large decode pool this order moves 6.15-6.29 TB/s
-// in place (with the tile-order write-through stores), against 5.69-5.73 for
-// plain tile-order loads and 5.82-5.86 for no-reuse tile-order loads. The
-// pieces then pass through a per-wave LDS area into the tile layout.
-__device__ __forceinline__ void load_page_contig(const void* page, int wave, int lane,
-                                                 u32x4 (&cont)[16]) {
-  const __amdgpu_buffer_rsrc_t rs = page_rsrc(const_cast<void*>(page), PAGE * 4);
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    cont[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, ((32 * wave + 2 * j) * K) * 4 + lane * 16,
-                                                    0, CPOL_NT);
-}
-
-// The contiguous pieces into the tile layout (lane l of tile (r, cb): row
-// 32w + 16r + l%16, channels 16cb + 4(l/16) .. +3), 16 rows at a time through
-// the wave's LDS area of 16 rows x 32 chunks of 16 bytes. Chunk g of local row
-// rho sits at slot g ^ rho of that row, so that neither the row-wise writes
-// nor the column-wise tile reads meet two lanes on one bank group within a
-// group of 16 lanes.
-__device__ __forceinline__ void transpose_page(const u32x4 (&cont)[16], u32x4* area, int lane,
-                                               u32x4 (&st)[2][8]) {
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rho = 2 * i + (lane >> 5), g = lane & 31;
-      area[rho * 32 + (g ^ rho)] = cont[8 * r + i];
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const int rho = lane & 15, g = 4 * cb + (lane >> 4);
-      st[r][cb] = area[rho * 32 + (g ^ rho)];
-    }
-    wave_lds_sync();
-  }
 }
 
 // First key channel of lane group g (= lane / 16) in tile cb: values i = 0..3
@@ -747,6 +713,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
   }
   floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  constexpr bool kValu = kValuDots && !SB16;  // the measurement variant's VALU dots
   u32x4 sn[2];  // BF16 pages: S_n of the even tile, stored with the odd one
   u32x4 sb[2];  // BF16 pages, align: S_me likewise
   char* const btile0 = static_cast<char*>(p.state) +
@@ -810,10 +777,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
             st[r][cb] = __builtin_bit_cast(u32x4, s);
           }
         }
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[0], s[0], acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[1], s[1], acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[2], s[2], acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[3], s[3], acc[r], 0, 0, 0);
+        if constexpr (!kValu) {
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[0], s[0], acc[r], 0, 0, 0);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[1], s[1], acc[r], 0, 0, 0);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[2], s[2], acc[r], 0, 0, 0);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[3], s[3], acc[r], 0, 0, 0);
+        }
       }
     }
   };
@@ -827,9 +796,33 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
   // acc[r], lane l, value i: column j = 4(l/16) + i of state row 16(2w+r) + l%16.
   if constexpr (kShareXD) __syncthreads();  // every wave has read x_s: it now holds the dots
+  if constexpr (kValu) {
+    // The VALU variant's dots from S_n in the page registers (FP32 pages).
+#pragma unroll 1
+    for (int j = 0; j < 2 * T; ++j) {
+      float a[2] = {0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
-    *reinterpret_cast<floatx4*>(&dots_s[16 * (2 * wave + r) + lr][4 * lq]) = acc[r];
+      for (int cb = 0; cb < 8; ++cb) {
+        const floatx4 x4 = *reinterpret_cast<const floatx4*>(&x_s[j][chan0<SB16>(cb, lq)]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const floatx4 sv = __builtin_bit_cast(floatx4, st[r][cb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[r] = fmaf(x4[i], sv[i], a[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        a[r] += __shfl_xor(a[r], 16);
+        a[r] += __shfl_xor(a[r], 32);
+        if (lq == 0) dots_s[16 * (2 * wave + r) + lr][j] = a[r];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      *reinterpret_cast<floatx4*>(&dots_s[16 * (2 * wave + r) + lr][4 * lq]) = acc[r];
+  }
   __syncthreads();
 
   // ---- 6. Per state row: the T x T forward substitution, outputs, records.

@@ -411,10 +411,15 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // CU in registers (128 VGPRs) but ran slower with them than with the 3 its
   // LDS allows.
   constexpr bool kShareXD = SB16;
-  __shared__ __attribute__((aligned(16))) float x_s[16][K];  // Gamma_t kn_t | Gamma_t q_t | 0
-  __shared__ __attribute__((aligned(16))) float dots_own[kShareXD ? 1 : V][16];
-  float (*const dots_s)[16] =
-      kShareXD ? reinterpret_cast<float (*)[16]>(&x_s[0][0]) : dots_own;  // w_t | y_t per row
+  // Rows padded by 4 floats (16 bytes): the state pass reads x_s as 16-byte
+  // pieces of 16 different rows per instruction, and the solve reads dots_s
+  // down a column (one state row per lane); with 512-byte rows both would meet
+  // every lane on the same banks.
+  constexpr int XP = K + 4;
+  __shared__ __attribute__((aligned(16))) float x_s[16][XP];  // Gamma_t kn_t | Gamma_t q_t | 0
+  __shared__ __attribute__((aligned(16))) float dots_own[kShareXD ? 1 : 16][XP];
+  float (*const dots_s)[XP] =
+      kShareXD ? x_s : dots_own;  // [j][state row]: w_t (j = t) | y_t (j = T + t)
   __shared__ __attribute__((aligned(16))) float kp_s[MAX_T][K];  // replay kn_t P_t (0 past n)
   __shared__ __attribute__((aligned(16))) float u_s[MAX_T][V];   // replay u_t (0 past n)
   __shared__ __attribute__((aligned(16))) float dn_s[K];
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // prologue's part one: areas 2w, 2w + 1 (q, k) of lower wave w, w + 2 (v) of
   // upper wave w, 6 * CONV_BLOCK <= sizeof x_s.
   uint8_t* const blk_s = reinterpret_cast<uint8_t*>(&x_s[0][0]);
-  static_assert(6 * CONV_BLOCK <= 16 * K * sizeof(float), "window blocks fit in x_s");
+  static_assert(6 * CONV_BLOCK <= 16 * XP * sizeof(float), "window blocks fit in x_s");
   uint32_t okb[MAX_T], ogb[MAX_T];
   float ou[MAX_T];
   uint32_t rbb = 0;
@@ -815,13 +820,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       for (int r = 0; r < 2; ++r) {
         a[r] += __shfl_xor(a[r], 16);
         a[r] += __shfl_xor(a[r], 32);
-        if (lq == 0) dots_s[16 * (2 * wave + r) + lr][j] = a[r];
+        if (lq == 0) dots_s[j][16 * (2 * wave + r) + lr] = a[r];
       }
     }
   } else {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
-      *reinterpret_cast<floatx4*>(&dots_s[16 * (2 * wave + r) + lr][4 * lq]) = acc[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dots_s[4 * lq + i][16 * (2 * wave + r) + lr] = acc[r][i];
   }
   __syncthreads();
 
@@ -835,7 +841,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     float us[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float a = v_s[t][vrow] - dots_s[vrow][t];
+      float a = v_s[t][vrow] - dots_s[t][vrow];
 #pragma unroll
       for (int s = 0; s < t; ++s) {
         const int ia = PI::a(t, s);
@@ -845,7 +851,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float o = dots_s[vrow][T + t];
+      float o = dots_s[T + t][vrow];
 #pragma unroll
       for (int s = 0; s <= t; ++s) {
         const int ib = PI::b(t, s);

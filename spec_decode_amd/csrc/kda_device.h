@@ -102,6 +102,62 @@ __device__ __forceinline__ void transpose_page(const u32x4 (&cont)[16], u32x4* a
   }
 }
 
+// The FP32 page in two halves (the streaming instances over FP32 pages).
+// Rows 0..15 of wave w's 32 go straight into the wave's LDS area (buffer loads
+// to LDS, no-reuse hint; each 1 KiB piece j lands at area + 1 KiB * j, lane l
+// at byte 16 l of it): lane l of piece j fetches row 32w + rho, rho = 2j +
+// l/32, the chunk g = (l % 32) ^ rho whose slot in the swizzled layout of
+// transpose_page is l % 32, so each piece is still 1 KiB of contiguous page.
+// Rows 16..31 load into registers as contiguous pieces (cont[i]: row
+// 32w + 16 + 2i + l/32, channels 4(l % 32) .. +3). On the large decode pool
+// this moves 6.32-6.36 TB/s in place against 6.11-6.12 for both halves through
+// registers (same session); the whole page straight into LDS (6.32-6.42)
+// would need 64 KiB of LDS per workgroup.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void load_page_halves(const void* page, int wave, int lane,
+                                                 u32x4* area, u32x4 (&cont)[8]) {
+  const __amdgpu_buffer_rsrc_t rs = page_rsrc(const_cast<void*>(page), PAGE * 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rho = 2 * j + (lane >> 5);
+    const int g = (lane & 31) ^ rho;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(area + 64 * j), 16,
+                                             ((32 * wave + rho) * K) * 4 + g * 16, 0, 0, CPOL_NT);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    cont[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, ((32 * wave + 16 + 2 * i) * K) * 4 + lane * 16, 0, CPOL_NT);
+}
+
+// Both halves into the tile layout: wait for every load of the wave (the LDS
+// half is not tracked by the compiler), read tiles (0, cb) from the area, then
+// pass the register half through the same area into tiles (1, cb).
+__device__ __forceinline__ void transpose_page_halves(const u32x4 (&cont)[8], u32x4* area,
+                                                      int lane, u32x4 (&st)[2][8]) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (gfx9 encoding; expcnt, lgkmcnt not waited)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const int rho = lane & 15, g = 4 * cb + (lane >> 4);
+    st[0][cb] = area[rho * 32 + (g ^ rho)];
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rho = 2 * i + (lane >> 5), g = lane & 31;
+    area[rho * 32 + (g ^ rho)] = cont[i];
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const int rho = lane & 15, g = 4 * cb + (lane >> 4);
+    st[1][cb] = area[rho * 32 + (g ^ rho)];
+  }
+  wave_lds_sync();
+}
+
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

@@ -490,7 +490,15 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
                      ((int64_t)slot * p.slot_stride + (int64_t)h * PAGE) * ES;
   char* const tile0 = page + ((16 * (2 * wave) + lr) * K + LDC * lq) * ES;
   u32x4 st[2][NLD];
-  u32x4 cont[kContig ? 16 : 1];  // kContig: the page as loaded, before the transpose
+  // kContig: the page pieces as loaded into registers. The stock verify loads
+  // half of each wave's share straight into the wave's LDS area instead
+  // (load_page_halves; 0.480 -> 0.471 ms on the large decode batch). The fused
+  // step keeps both halves in registers: a workgroup barrier waits for a
+  // wave's outstanding loads to LDS, and its waves reach their barriers before
+  // they need the page (with the LDS half: 0.781-0.786 -> 0.785-0.790 ms,
+  // gated 0.785 -> 0.797 ms).
+  constexpr bool kHalves = kContig && !FUSED;
+  u32x4 cont[kContig ? 16 : 1];
   float kf[T], qf[T], dnew[T];
   float okf[MAX_T], od[MAX_T];
   // ---- 3. Prologue, part one: decays, key sums of squares, staging; with the
@@ -516,7 +524,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kContig) {
-      load_page_contig(page, wave, lane, cont);
+      if constexpr (kHalves)
+        load_page_halves(page, wave, lane, &xt_s[wave][0], reinterpret_cast<u32x4(&)[8]>(cont));
+      else
+        load_page_contig(page, wave, lane, cont);
     } else {
 #pragma unroll
       for (int r = 0; r < 2; ++r)
@@ -553,7 +564,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kContig) {
-      load_page_contig(page, wave, lane, cont);
+      if constexpr (kHalves)
+        load_page_halves(page, wave, lane, &xt_s[wave][0], reinterpret_cast<u32x4(&)[8]>(cont));
+      else
+        load_page_contig(page, wave, lane, cont);
     } else {
 #pragma unroll
       for (int r = 0; r < 2; ++r)
@@ -687,7 +701,13 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // The contiguous pieces into the tile layout, each wave its own rows (no
   // workgroup barrier), before the barrier that the record waves reach first.
   if constexpr (kContig) {
-    if constexpr (!SB16) transpose_page(cont, &xt_s[wave][0], lane, st);
+    if constexpr (!SB16) {
+      if constexpr (kHalves)
+        transpose_page_halves(reinterpret_cast<const u32x4(&)[8]>(cont), &xt_s[wave][0], lane,
+                              st);
+      else
+        transpose_page(cont, &xt_s[wave][0], lane, st);
+    }
   }
   __syncthreads();
 

@@ -10,11 +10,16 @@
 
 The gated RMSNorm output stage (assert_gated_close) is held to 1 BF16 ulp as
 well, except at elements whose FP64 o (exported by the oracle before any
-rounding) lies within the FP32 tolerance above of a BF16 rounding boundary:
+rounding) lies within GATED_TIE_ATOL + GATED_TIE_RTOL |o| of a BF16 rounding
+boundary. That band covers the FP32 evaluation error of o with a margin: o is
+a 128-term FP32 dot product plus a solve sum of at most 8 terms, with terms
+below 1 in these workloads, so its FP32 error is of order 1e-7, ten times
+below the band. At such elements
 the stage first rounds o to BF16 (a rounding point of the method), and there
-the kernel's FP32 o may round to the other neighbour; that one-ulp difference
-of its input carries into the output, whose own rounding can add a second
-ulp, so those elements (and only those) are allowed 2 ulps.
+the stage's BF16 rounding of the kernel's FP32 o may go to the other
+neighbour; that one-ulp difference of its input carries into the output,
+whose own rounding can add a second ulp, so those elements (and only those)
+are allowed 2 ulps.
 
 The reference side is the FP64 oracle's output rounded once to the stored type.
 """
@@ -25,6 +30,8 @@ F32_ATOL = 1e-5
 BF16_ULPS = 1
 BF16_ATOL = 1e-5
 GATED_OUT_ULPS = 2
+GATED_TIE_ATOL = 1e-6
+GATED_TIE_RTOL = 1e-5
 
 
 def _bf16_ordered(bits: np.ndarray) -> np.ndarray:
@@ -60,11 +67,12 @@ def bf16_tie_distance(o: np.ndarray) -> np.ndarray:
     return np.abs(o - 0.5 * (lo + hi))
 
 
-def bf16_near_tie(o: np.ndarray) -> np.ndarray:
-    """Boolean mask of FP64 values within F32_ATOL + F32_RTOL |o| of a BF16
-    rounding boundary."""
+def bf16_near_tie(o: np.ndarray, atol: float = GATED_TIE_ATOL,
+                  rtol: float = GATED_TIE_RTOL) -> np.ndarray:
+    """Boolean mask of FP64 values within atol + rtol |o| of a BF16 rounding
+    boundary."""
     o = np.asarray(o, dtype=np.float64)
-    return bf16_tie_distance(o) <= F32_ATOL + F32_RTOL * np.abs(o)
+    return bf16_tie_distance(o) <= atol + rtol * np.abs(o)
 
 
 def f32_mismatch(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:

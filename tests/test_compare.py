@@ -12,11 +12,11 @@ def _bits(x):
 def test_near_tie_flags_midpoints_only():
     one_ulp = 2.0 ** -7  # BF16 spacing in [1, 2)
     o = np.array([1.0 + 0.5 * one_ulp,            # exactly a midpoint
-                  1.0 + 0.5 * one_ulp + 5e-5,     # inside the band (1e-5 + 1e-4 |o|)
-                  1.0 + 0.5 * one_ulp + 3e-4,     # outside it
+                  1.0 + 0.5 * one_ulp + 5e-6,     # inside the band (1e-6 + 1e-5 |o|)
+                  1.0 + 0.5 * one_ulp + 3e-5,     # outside it
                   1.0,                            # a BF16 value: half an ulp away
                   -(3.0 + 0.5 * 2.0 ** -6),       # a negative midpoint in [2, 4)
-                  4e-6, 0.0])                     # tiny values: within the absolute band
+                  4e-7, 0.0])                     # tiny values: within the absolute band
     assert list(bf16_near_tie(o)) == [True, True, False, False, True, True, True]
 
 

@@ -97,3 +97,45 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_trace_summary_averages_the_timed_launches(tmp_path):
+    """bench.py --trace-summary: per kernel, the mean over its last N launches
+    (in start-time order, whatever the CSV's row order), and counter values
+    summed per dispatch before they are averaged."""
+    import csv
+    b = _bench()
+    trace = tmp_path / "kda_kernel_trace.csv"
+    rows = []
+    # kernel A: 4 warm-up launches of 10 us, then 3 timed ones of 2, 4, 6 us;
+    # rows written out of order
+    t = 0
+    for d in [10, 10, 10, 10, 2, 4, 6]:
+        rows.append({"Kernel_Name": "A", "Dispatch_Id": str(len(rows)), "Start_Timestamp": str(t),
+                     "End_Timestamp": str(t + d * 1000)})
+        t += 100000
+    rows.append({"Kernel_Name": "B", "Dispatch_Id": "99", "Start_Timestamp": "5",
+                 "End_Timestamp": "1005"})
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        for r in reversed(rows):
+            w.writerow(r)
+    s = b.trace_summary(str(trace), 3)
+    assert s["A"]["launches"] == 7 and s["A"]["timed_launches"] == 3
+    assert s["A"]["timed_mean_us"] == 4.0 and s["A"]["timed_min_us"] == 2.0
+    assert s["A"]["all_mean_us"] == round((40 + 12) / 7, 2)
+    assert s["B"]["timed_mean_us"] == 1.0
+    # counters: two counter rows per dispatch (e.g. per XCD) are summed first
+    ctr = tmp_path / "kda_counter_collection.csv"
+    with open(ctr, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Dispatch_Id", "Start_Timestamp",
+                                          "End_Timestamp", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for did, (t0, v) in enumerate([(0, 100.0), (10, 200.0), (20, 300.0)]):
+            for part in (0.25, 0.75):
+                w.writerow({"Kernel_Name": "A", "Dispatch_Id": str(did),
+                            "Start_Timestamp": str(t0), "End_Timestamp": str(t0 + 1000),
+                            "Counter_Name": "FETCH_SIZE", "Counter_Value": str(v * part)})
+    c = b.trace_summary(str(ctr), 2)
+    assert c["A"]["counters_timed_mean"]["FETCH_SIZE"] == 250.0

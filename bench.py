@@ -127,11 +127,42 @@ def trace_summary(path, last):
     return out
 
 
+def strip_comments(text):
+    """C++ source without its comments, blank lines and indentation (string and
+    character literals kept), so that the digest below follows the code and
+    not its prose."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            if j < 0:
+                raise ValueError("unterminated block comment")
+            out.append(" ")
+            i = j + 2
+        elif ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(ch)
+            i += 1
+    lines = (line.strip() for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest(paths):
+    """Digest of the code (comments excluded) of the given source files: the
+    key under which profiles/traffic.json holds a kernel's measured traffic."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

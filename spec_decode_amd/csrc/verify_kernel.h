@@ -493,10 +493,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // kContig: the page pieces as loaded into registers. The stock verify loads
   // half of each wave's share straight into the wave's LDS area instead
   // (load_page_halves; 0.480 -> 0.471 ms on the large decode batch). The fused
-  // step keeps both halves in registers: a workgroup barrier waits for a
-  // wave's outstanding loads to LDS, and its waves reach their barriers before
-  // they need the page (with the LDS half: 0.781-0.786 -> 0.785-0.790 ms,
-  // gated 0.785 -> 0.797 ms).
+  // step keeps both halves in registers: with the LDS half it is slower on
+  // that batch (0.784-0.786 -> 0.787-0.791 ms, gated 0.785 -> 0.797 ms), also
+  // when the barrier that closes the prologue waits for LDS accesses only
+  // instead of for the wave's loads into LDS too.
   constexpr bool kHalves = kContig && !FUSED;
   u32x4 cont[kContig ? 16 : 1];
   float kf[T], qf[T], dnew[T];

@@ -139,3 +139,30 @@ def test_trace_summary_averages_the_timed_launches(tmp_path):
                             "Counter_Name": "FETCH_SIZE", "Counter_Value": str(v * part)})
     c = b.trace_summary(str(ctr), 2)
     assert c["A"]["counters_timed_mean"]["FETCH_SIZE"] == 250.0
+
+
+def test_source_digest_follows_code_not_comments(tmp_path, monkeypatch):
+    b = _bench()
+    src = ('#include "a.h"  // header\n'
+           '/* block\n   comment */ int f(int x) {\n'
+           '  const char* s = "http://not/a/comment";  // trailing\n'
+           "  return x + '/';\n}\n")
+    stripped = b.strip_comments(src)
+    assert "header" not in stripped and "block" not in stripped and "trailing" not in stripped
+    assert '"http://not/a/comment"' in stripped and "'/'" in stripped
+    assert '#include "a.h"' in stripped.splitlines()
+
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    path = tmp_path / "k.hip"
+
+    def digest(text):
+        path.write_text(text)
+        return b.source_digest(["k.hip"])
+
+    base = digest(src)
+    # a comment edit, a new comment line, blank lines and indentation: same code
+    assert digest(src.replace("// trailing", "// reworded note")) == base
+    assert digest("// new first line\n\n" + src.replace("  return", "      return")) == base
+    # any code edit changes it, also one inside a string literal
+    assert digest(src.replace("x + '/'", "x - '/'")) != base
+    assert digest(src.replace("not/a", "not/b")) != base

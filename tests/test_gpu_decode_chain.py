@@ -1,0 +1,155 @@
+"""Several decode steps in a row through deferred RecoverSSM, on the GPU and in
+the oracle side by side (kernels page: the deferred RecoverSSM plan steps;
+fused page: KdaFused, replay of the pending commit before the verify).
+
+Each step runs the fused replay+verify (it replays what the previous step
+accepted from the records that step wrote, then verifies a new window and
+rewrites the records), the defer step over that step's accepted counts with a
+mix of eager and deferred requests, and the commit of the eager requests. A
+flush (plan, then commit) ends the run. The GPU chain and the oracle chain run
+independently from the same seeded inputs: nothing the GPU produces is fed to
+the oracle. The pool is FP32, where the two chains stay within FP32 rounding
+of each other from step to step; a BF16 pool's legitimate one-ulp differences
+are scaled by the decays and can cancel in the next fold, so no per-step ulp
+bound holds over a chain of BF16 pages.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _compare import assert_bf16_close, assert_exact, assert_f32_close
+from _kda_cases import DEV, announce, dev, dev_bf16, np_of, window_np
+
+pytestmark = pytest.mark.gpu
+
+K = V = 128
+
+
+def _commit_args(kda, H, RQ, B, d, sources, lens, rows):
+    return dict(heads=H, window=RQ, batch=B, state_dtype=kda.KDA_STATE_F32,
+                state_addrs=[d["state"].data_ptr()], state_slot_strides=[H * V * K],
+                corr_addrs=[d["corr"].data_ptr()], corr_row_strides=[H * RQ * V],
+                kg_addrs=[d["kg"].data_ptr()], kg_row_strides=[H * RQ * 2 * K],
+                a_log=d["a_log"][None], dt_bias=d["dt_bias"][None], sources=sources,
+                commit_lens=lens, destinations=sources, record_rows=rows,
+                lower_bound=W.LOWER_BOUND)
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_decode_steps_chain_against_oracle(seed):
+    import spec_decode_amd as kda
+
+    H, B, T, RQ, S, STEPS = 4, 24, 8, 8, 32, 4
+    page = H * V * K
+    c = W.small_fused_case(seed, H, B, T, RQ, S, null_rows=(3, 17), no_record_rows=(5, 20))
+    slots = c["state_indices"].numpy().astype(np.int32)
+    rows = c["record_rows"].numpy().astype(np.int32)
+    a_log = c["a_log"][0].numpy()
+    dtb = c["dt_bias"][0].numpy()
+    g = W._gen(seed + 1000)
+    windows = [window_np(c["window"])] + [window_np(W.draw_window(W._gen(seed + 100 + i), B, T, H))
+                                          for i in range(1, STEPS)]
+    accepted = [W.uniform_int(g, 0, T, B).numpy().astype(np.int32) for _ in range(STEPS)]
+    eager = [(W.uniform_int(g, 0, 2, B).numpy() == 0).astype(np.int32) for _ in range(STEPS)]
+
+    # The oracle chain's buffers and the GPU chain's, from the same host inputs.
+    ref = dict(state=c["state"].numpy().astype(np.float32).copy(),
+               corr=c["corr"].numpy().copy(), kg=W.bits(c["kg"]).copy(),
+               pending=c["pending"].numpy().astype(np.int32).copy())
+    d = dict(state=dev(ref["state"]), corr=dev(ref["corr"]), kg=dev_bf16(ref["kg"]),
+             pending=dev(ref["pending"]), a_log=dev(a_log), dt_bias=dev(dtb))
+    d_slots, d_rows = dev(slots), dev(rows)
+    out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=DEV)
+    first = ref["state"].copy()
+
+    def compare(label):
+        assert_f32_close(f"{label} state pool", np_of(d["state"]), ref["state"])
+        assert_f32_close(f"{label} corrections", np_of(d["corr"]), ref["corr"])
+        assert_exact(f"{label} key/gate records", np_of(d["kg"]), ref["kg"])
+        assert_exact(f"{label} pending", np_of(d["pending"]), ref["pending"])
+
+    replayed = eager_commits = 0
+    for i in range(STEPS):
+        win = windows[i]
+        live = [b for b in range(B) if slots[b] > 0 and rows[b] >= 0]
+        replayed += sum(int(min(ref["pending"][rows[b]], RQ) > 0) for b in live)
+        announce(f"decode chain seed={seed} step {i}: fused H={H} B={B} T={T} RQ={RQ} FP32 pool")
+        kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]),
+                                    k=dev_bf16(win["k"]), v=dev_bf16(win["v"]),
+                                    raw_g=dev_bf16(win["raw_g"]),
+                                    raw_beta=dev_bf16(win["raw_beta"]), a_log=d["a_log"],
+                                    dt_bias=d["dt_bias"], lower_bound=W.LOWER_BOUND,
+                                    state=d["state"], state_slot_stride=page,
+                                    state_indices=d_slots, corr=d["corr"], kg=d["kg"],
+                                    record_tokens=RQ, record_rows=d_rows,
+                                    pending=d["pending"], out=out)
+        r_out = np.zeros((B * T, H * V), np.uint16)
+        oracle.fused_replay_verify(heads=H, tokens=T, batch=B, q=win["q"], k=win["k"],
+                                   v=win["v"], raw_g=win["raw_g"], raw_beta=win["raw_beta"],
+                                   a_log=a_log, dt_bias=dtb, lower_bound=W.LOWER_BOUND,
+                                   state=ref["state"], state_slot_stride=page,
+                                   state_indices=slots, corr=ref["corr"], kg=ref["kg"],
+                                   record_tokens=RQ, record_rows=rows, pending=ref["pending"],
+                                   out=r_out)
+        torch.cuda.synchronize()
+        assert_bf16_close(f"step {i} out", np_of(out), r_out)
+        compare(f"step {i} fused")
+
+        announce(f"decode chain seed={seed} step {i}: defer + eager commit")
+        d_lens = dev(accepted[i])
+        kda.kda_defer_commit(batch=B, state_indices=d_slots, commit_lens=d_lens,
+                             record_rows=d_rows, pending=d["pending"], eager=dev(eager[i]))
+        r_lens = accepted[i].copy()
+        oracle.defer(slots, r_lens, rows, ref["pending"], eager=eager[i])
+        torch.cuda.synchronize()
+        assert_exact(f"step {i} defer commit_lens", np_of(d_lens), r_lens)
+        eager_commits += sum(int(r_lens[b] > 0) for b in live)
+        kda.kda_commit(**_commit_args(kda, H, RQ, B, d, d_slots, d_lens, d_rows))
+        oracle.commit(heads=H, window=RQ, batch=B, state_bf16=False, state_layers=[ref["state"]],
+                      state_slot_strides=[page], corr_layers=[ref["corr"]],
+                      corr_row_strides=[H * RQ * V], kg_layers=[ref["kg"]],
+                      kg_row_strides=[H * RQ * 2 * K], a_log=a_log[None], dt_bias=dtb[None],
+                      sources=slots, commit_lens=r_lens, destinations=slots, record_rows=rows,
+                      lower_bound=W.LOWER_BOUND)
+        torch.cuda.synchronize()
+        compare(f"step {i} eager commit")
+
+    announce(f"decode chain seed={seed}: flush plan + commit")
+    fl = [torch.empty(B, dtype=torch.int32, device=DEV) for _ in range(4)]
+    kda.kda_flush_plan(batch=B, spec_query_len=T, state_indices=d_slots, record_rows=d_rows,
+                       pending=d["pending"], commit_lens=fl[0], final_indices=fl[1],
+                       boundaries=fl[2], boundary_lens=fl[3])
+    r_flush = oracle.flush_plan(slots, rows, ref["pending"], T)
+    torch.cuda.synchronize()
+    for name, got, want in zip(("commit_lens", "final", "boundaries", "boundary_lens"), fl,
+                               r_flush):
+        assert_exact(f"flush {name}", np_of(got), want)
+    kda.kda_commit(**_commit_args(kda, H, RQ, B, d, fl[1], fl[0], d_rows))
+    oracle.commit(heads=H, window=RQ, batch=B, state_bf16=False, state_layers=[ref["state"]],
+                  state_slot_strides=[page], corr_layers=[ref["corr"]],
+                  corr_row_strides=[H * RQ * V], kg_layers=[ref["kg"]],
+                  kg_row_strides=[H * RQ * 2 * K], a_log=a_log[None], dt_bias=dtb[None],
+                  sources=r_flush[1], commit_lens=r_flush[0], destinations=r_flush[1],
+                  record_rows=rows, lower_bound=W.LOWER_BOUND)
+    torch.cuda.synchronize()
+    compare("flush commit")
+
+    # The chain did what it is meant to exercise: replays in later steps, eager
+    # commits and a non-empty flush. A page moved iff its request had tokens to
+    # fold (pending at the start, or accepted in some step); the null slot's
+    # page and the pages of requests without a record row never change.
+    assert replayed > B and eager_commits > 0 and int(r_flush[0].sum()) > 0
+    final, start = np_of(d["state"]).reshape(S, page), first.reshape(S, page)
+    pend0, moved = c["pending"].numpy(), set()
+    for b in range(B):
+        if slots[b] > 0 and rows[b] >= 0 and (
+                pend0[rows[b]] > 0 or any(acc[b] > 0 for acc in accepted)):
+            moved.add(int(slots[b]))
+    assert len(moved) > B // 2
+    for s in range(S):
+        if s in moved:
+            assert not np.array_equal(final[s], start[s]), f"slot {s} did not move"
+        else:
+            assert_exact(f"slot {s} (nothing to fold)", final[s], start[s])

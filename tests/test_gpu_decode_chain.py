@@ -11,7 +11,10 @@ independently from the same seeded inputs: nothing the GPU produces is fed to
 the oracle. The pool is FP32, where the two chains stay within FP32 rounding
 of each other from step to step; a BF16 pool's legitimate one-ulp differences
 are scaled by the decays and can cancel in the next fold, so no per-step ulp
-bound holds over a chain of BF16 pages.
+bound holds over a chain of BF16 pages. With the convolution prologue the
+chain also carries each slot's window pool from step to step: a step reads its
+taps at the offset that the previous step's accepted count sets and writes the
+window back, so the next step's inputs depend on it.
 """
 import numpy as np
 import pytest
@@ -20,7 +23,8 @@ import torch
 import oracle
 import workloads as W
 from _compare import assert_bf16_close, assert_exact, assert_f32_close
-from _kda_cases import DEV, announce, dev, dev_bf16, np_of, window_np
+from _kda_cases import (DEV, announce, conv_pool_build, conv_pool_layout, dev, dev_bf16,
+                        np_of, window_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +41,7 @@ def _commit_args(kda, H, RQ, B, d, sources, lens, rows):
                 lower_bound=W.LOWER_BOUND)
 
 
-@pytest.mark.parametrize("seed", [11, 12])
-def test_decode_steps_chain_against_oracle(seed):
+def _run_chain(seed, conv_layout=None):
     import spec_decode_amd as kda
 
     H, B, T, RQ, S, STEPS = 4, 24, 8, 8, 32, 4
@@ -63,36 +66,55 @@ def test_decode_steps_chain_against_oracle(seed):
     d_slots, d_rows = dev(slots), dev(rows)
     out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=DEV)
     first = ref["state"].copy()
+    if conv_layout is not None:
+        cv = W.draw_conv_inputs(W._gen(seed + 7), B, T, H, RQ, S)
+        strides = conv_pool_layout(S, H, RQ + 2, layout=conv_layout)
+        ref["pool"] = conv_pool_build(W.bits(cv.window), strides, seed + 11)
+        d["pool"] = dev_bf16(ref["pool"])
+        conv_w, conv_b, pitch = W.bits(cv.weight), W.bits(cv.bias), cv.pitch
+        xs = [W.bits(cv.x)] + [W.bits(W.draw_conv_inputs(W._gen(seed + 200 + i), B, T, H, RQ,
+                                                         S).x) for i in range(1, STEPS)]
+        d_conv_w, d_conv_b = dev_bf16(conv_w), dev_bf16(conv_b)
+        pool0 = ref["pool"].copy()
 
     def compare(label):
         assert_f32_close(f"{label} state pool", np_of(d["state"]), ref["state"])
         assert_f32_close(f"{label} corrections", np_of(d["corr"]), ref["corr"])
         assert_exact(f"{label} key/gate records", np_of(d["kg"]), ref["kg"])
         assert_exact(f"{label} pending", np_of(d["pending"]), ref["pending"])
+        if conv_layout is not None:
+            assert_exact(f"{label} window pool", np_of(d["pool"]), ref["pool"])
 
     replayed = eager_commits = 0
     for i in range(STEPS):
         win = windows[i]
         live = [b for b in range(B) if slots[b] > 0 and rows[b] >= 0]
         replayed += sum(int(min(ref["pending"][rows[b]], RQ) > 0) for b in live)
-        announce(f"decode chain seed={seed} step {i}: fused H={H} B={B} T={T} RQ={RQ} FP32 pool")
-        kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]),
-                                    k=dev_bf16(win["k"]), v=dev_bf16(win["v"]),
-                                    raw_g=dev_bf16(win["raw_g"]),
-                                    raw_beta=dev_bf16(win["raw_beta"]), a_log=d["a_log"],
-                                    dt_bias=d["dt_bias"], lower_bound=W.LOWER_BOUND,
-                                    state=d["state"], state_slot_stride=page,
-                                    state_indices=d_slots, corr=d["corr"], kg=d["kg"],
-                                    record_tokens=RQ, record_rows=d_rows,
-                                    pending=d["pending"], out=out)
+        announce(f"decode chain seed={seed} step {i}: fused H={H} B={B} T={T} RQ={RQ} "
+                 f"FP32 pool, convolution prologue {conv_layout}")
+        common = dict(heads=H, tokens=T, batch=B, lower_bound=W.LOWER_BOUND,
+                      state_slot_stride=page, record_tokens=RQ)
+        g_io = dict(raw_g=dev_bf16(win["raw_g"]), raw_beta=dev_bf16(win["raw_beta"]),
+                    a_log=d["a_log"], dt_bias=d["dt_bias"], state=d["state"],
+                    state_indices=d_slots, corr=d["corr"], kg=d["kg"], record_rows=d_rows,
+                    pending=d["pending"], out=out)
         r_out = np.zeros((B * T, H * V), np.uint16)
-        oracle.fused_replay_verify(heads=H, tokens=T, batch=B, q=win["q"], k=win["k"],
-                                   v=win["v"], raw_g=win["raw_g"], raw_beta=win["raw_beta"],
-                                   a_log=a_log, dt_bias=dtb, lower_bound=W.LOWER_BOUND,
-                                   state=ref["state"], state_slot_stride=page,
-                                   state_indices=slots, corr=ref["corr"], kg=ref["kg"],
-                                   record_tokens=RQ, record_rows=rows, pending=ref["pending"],
-                                   out=r_out)
+        r_io = dict(raw_g=win["raw_g"], raw_beta=win["raw_beta"], a_log=a_log, dt_bias=dtb,
+                    state=ref["state"], state_indices=slots, corr=ref["corr"], kg=ref["kg"],
+                    record_rows=rows, pending=ref["pending"], out=r_out)
+        if conv_layout is None:
+            kda.kda_fused_replay_verify(q=dev_bf16(win["q"]), k=dev_bf16(win["k"]),
+                                        v=dev_bf16(win["v"]), **common, **g_io)
+            oracle.fused_replay_verify(q=win["q"], k=win["k"], v=win["v"], **common, **r_io)
+        else:
+            conv = dict(x_row_stride=pitch, conv_slot_stride=strides[0],
+                        conv_channel_stride=strides[1], conv_tap_stride=strides[2],
+                        q_scale=K ** -0.5)
+            kda.kda_fused_conv_replay_verify(x=dev_bf16(xs[i]), conv_weight=d_conv_w,
+                                             conv_bias=d_conv_b, conv_state=d["pool"],
+                                             **conv, **common, **g_io)
+            oracle.fused_conv_replay_verify(x=xs[i], conv_weight=conv_w, conv_bias=conv_b,
+                                            conv_state=ref["pool"], **conv, **common, **r_io)
         torch.cuda.synchronize()
         assert_bf16_close(f"step {i} out", np_of(out), r_out)
         compare(f"step {i} fused")
@@ -153,3 +175,21 @@ def test_decode_steps_chain_against_oracle(seed):
             assert not np.array_equal(final[s], start[s]), f"slot {s} did not move"
         else:
             assert_exact(f"slot {s} (nothing to fold)", final[s], start[s])
+    if conv_layout is not None:
+        # every step rewrote the windows of the live slots, and only theirs
+        rewritten = np_of(d["pool"]) != pool0
+        assert rewritten.any()
+        ss, cs, ts = strides
+        idx = np.arange(pool0.size)
+        slot_of = idx // ss
+        assert set(np.unique(slot_of[rewritten])) <= set(int(x) for x in slots if x > 0)
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_decode_steps_chain_against_oracle(seed):
+    _run_chain(seed)
+
+
+@pytest.mark.parametrize("layout", ["dim_first", "window_major"])
+def test_decode_steps_chain_convolution_prologue(layout):
+    _run_chain(21 if layout == "dim_first" else 22, conv_layout=layout)

@@ -348,6 +348,139 @@ def cpu_baseline(host, H, T, RQ, n_req, lb, bf16=False, min_seconds=10.0):
     }
 
 
+def sampled_cpu_baseline(run, n_items, state_bytes, seconds=2.0):
+    """The oracle on bounded random samples of a single-kernel workload's
+    (layer, request, head) items, on every core the process may use and on one
+    thread. run(items, threads) runs it on the given flattened item ids (host
+    inputs snapshotted before any GPU launch); state_bytes(items) gives their
+    algorithmic state bytes. Each sample doubles until it takes about
+    `seconds` of wall time; a sample that covers the whole workload sooner is
+    run again until that much time has passed."""
+    import numpy as np
+    import oracle
+
+    oracle._load()
+    rng = np.random.default_rng(0)
+    res = {}
+    for label, threads in (("all", oracle.default_threads()), ("one", 1)):
+        size = min(n_items, 64)
+        while True:
+            items = np.sort(rng.choice(n_items, size, replace=False)).astype(np.int64)
+            reps = 0
+            t0 = time.perf_counter()
+            while True:
+                run(items, threads)
+                reps += 1
+                dt = time.perf_counter() - t0
+                if dt >= seconds or size < n_items:
+                    break
+            if dt >= seconds or size == n_items:
+                break
+            size = min(n_items, max(2 * size, int(size * seconds / max(dt, 1e-3))))
+        res[label] = (threads, size, reps, dt, state_bytes(items))
+
+    def rates(r):
+        threads, size, reps, dt, sb = r
+        return reps * sb / dt / 1e9, reps * size / dt
+
+    (gbs, ips), (gbs1, ips1) = rates(res["all"]), rates(res["one"])
+    threads, size, reps, dt, _ = res["all"]
+    _, size1, reps1, dt1, _ = res["one"]
+    return {
+        "value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": (f"{size} of the workload's {n_items} items, drawn at random, FP64, "
+                   f"{reps} pass(es): {dt:.2f} s wall on {threads} threads; {size1} items, "
+                   f"{reps1} pass(es): {dt1:.2f} s on one thread"),
+        "items_per_s": round(ips, 1),
+        "single_thread": {"value": round(gbs1, 3), "unit": "GB/s", "items_per_s": round(ips1, 1)},
+    }
+
+
+def host_bits(t):
+    """Host copy of a device or host tensor: BF16 as uint16 bits, others as is."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16").copy()
+    return t.numpy().copy()
+
+
+def _commit_cpu_runner(H, B, Q, states, slot_strides, corrs, kgs, a_log, dt_bias, src, lens,
+                       dst, bnd, blen, lb):
+    """Host snapshots of a commit workload's BF16 pools and records and the
+    oracle over a subset of its items: (run, state_bytes) for
+    sampled_cpu_baseline."""
+    import oracle
+
+    L = len(states)
+    h_st = [host_bits(t) for t in states]
+    h_co = [host_bits(t) for t in corrs]
+    h_kg = [host_bits(t) for t in kgs]
+    h_al, h_db = host_bits(a_log), host_bits(dt_bias)
+    page_bytes = V * K * 2
+
+    def run(sel, threads):
+        oracle.commit(heads=H, window=Q, batch=B, state_bf16=True, state_layers=h_st,
+                      state_slot_strides=slot_strides, corr_layers=h_co,
+                      corr_row_strides=[H * Q * V] * L, kg_layers=h_kg,
+                      kg_row_strides=[H * Q * 2 * K] * L, a_log=h_al, dt_bias=h_db,
+                      sources=src, commit_lens=lens, destinations=dst, boundaries=bnd,
+                      boundary_lens=blen, lower_bound=lb, items=sel, threads=threads)
+
+    def state_bytes(sel):
+        tot = 0
+        for it in sel:
+            b = (int(it) // H) % B  # item id (l * B + b) * H + h
+            if min(int(lens[b]), Q) > 0 and src[b] > 0 and dst[b] > 0:
+                tot += 2 * page_bytes + (page_bytes if bnd is not None and bnd[b] > 0
+                                         and blen[b] > 0 else 0)
+        return tot
+
+    return run, state_bytes
+
+
+def _verify_cpu_runner(fused, H, B, T, RQ, state, slots, rows, pend_row, corr, kg, a_log,
+                       dt_bias, lb, win):
+    """Host snapshots of a stock-verify or fused workload's inputs and the oracle
+    over a subset of its items: (run, state_bytes) for sampled_cpu_baseline."""
+    import numpy as np
+    import oracle
+
+    h = {n: host_bits(getattr(win, n)) for n in ("q", "k", "v", "raw_g", "raw_beta")}
+    h.update(state=host_bits(state), corr=host_bits(corr), kg=host_bits(kg),
+             a_log=host_bits(a_log), dt_bias=host_bits(dt_bias),
+             slots=host_bits(slots).astype(np.int32), rows=host_bits(rows).astype(np.int32))
+    pend = None if pend_row is None else host_bits(pend_row).astype(np.int32)
+    out = np.zeros((B * T, H * V), np.uint16)
+    page = H * V * K
+    page_bytes = V * K * h["state"].itemsize
+
+    def run(sel, threads):
+        args = dict(heads=H, tokens=T, batch=B, q=h["q"], k=h["k"], v=h["v"], raw_g=h["raw_g"],
+                    raw_beta=h["raw_beta"], a_log=h["a_log"], dt_bias=h["dt_bias"],
+                    lower_bound=lb, state=h["state"], state_slot_stride=page,
+                    state_indices=h["slots"], corr=h["corr"], kg=h["kg"], record_tokens=RQ,
+                    record_rows=h["rows"], out=out, items=sel, threads=threads)
+        if fused:
+            oracle.fused_replay_verify(pending=pend, **args)
+        else:
+            oracle.verify(**args)
+
+    def state_bytes(sel):
+        tot = 0
+        for it in sel:
+            b = int(it) // H
+            if h["slots"][b] <= 0:
+                continue
+            tot += page_bytes  # the page read
+            r = h["rows"][b]
+            if fused and r >= 0 and min(int(pend[r]), RQ) > 0:
+                tot += page_bytes  # S_n written back
+        return tot
+
+    return run, state_bytes
+
+
 # ----------------------------------------------------------------- single-kernel workloads
 
 def bench_kernel_workload(args):
@@ -363,6 +496,7 @@ def bench_kernel_workload(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     i32 = lambda t: t.to(dev)
+    cpu_run = cpu_bytes = None  # the oracle on a sample of the workload (not for decay)
     if args.workload in ("commit", "align"):
         w = W.config1(device=dev) if args.workload == "commit" else W.config3(device=dev)
         a = w.arrays
@@ -396,6 +530,10 @@ def bench_kernel_workload(args):
             st += L * H * s_b
             tot += L * H * (s_b + n * (V * 4 + 2 * K * 2))
         items = L * B * H
+        if not args.no_cpu_baseline:
+            cpu_run, cpu_bytes = _commit_cpu_runner(
+                H, B, Q, states, list(w.slot_strides), corrs, kgs, a["a_log"], a["dt_bias"],
+                src, lens, dst, bn, bl, w.lower_bound)
         name = "kda_commit (BF16)" if L == 1 else "kda_commit (BF16, align, 8 layers)"
         workload = ("commit: L=1 H=32 B=64 window 4, BF16 pool of 256 slots, src -> dst"
                     if L == 1 else
@@ -434,6 +572,10 @@ def bench_kernel_workload(args):
         a_log, dt_bias = a["a_log"][0].contiguous().to(dev), a["dt_bias"][0].contiguous().to(dev)
         new = w.windows["new"].to(dev)
         out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=dev)
+        if not args.no_cpu_baseline:
+            cpu_run, cpu_bytes = _verify_cpu_runner(
+                False, H, B, T, RQ, state, a["state_indices"], a["record_rows"], None, corr, kg,
+                a_log, dt_bias, w.lower_bound, new)
         launch = lambda: kda.kda_verify(
             heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v, raw_g=new.raw_g,
             raw_beta=new.raw_beta, a_log=a_log, dt_bias=dt_bias, lower_bound=w.lower_bound,
@@ -462,6 +604,11 @@ def bench_kernel_workload(args):
         a_log, dt_bias = a["a_log"][0].contiguous().to(dev), a["dt_bias"][0].contiguous().to(dev)
         new, prior = w.windows["new"].to(dev), w.windows["prior"].to(dev)
         out = torch.empty((B * T, H * V), dtype=torch.bfloat16, device=dev)
+        if not args.no_cpu_baseline:
+            # the generator's records (before the prior-window verify rewrites them)
+            cpu_run, cpu_bytes = _verify_cpu_runner(
+                True, H, B, T, RQ, state, a["state_indices"], a["record_rows"], pend_row, corr,
+                kg, a_log, dt_bias, w.lower_bound, new)
         kda.kda_verify(heads=H, tokens=T, batch=B, q=prior.q, k=prior.k, v=prior.v,
                        raw_g=prior.raw_g, raw_beta=prior.raw_beta, a_log=a_log, dt_bias=dt_bias,
                        lower_bound=w.lower_bound, state=state, state_slot_stride=H * V * K,
@@ -508,7 +655,7 @@ def bench_kernel_workload(args):
     achieved = tot / (mean_ms * 1e-3) / 1e9
     # over the timed launches alone; a kernel with no state bytes reports its total rate
     value = (st if st else tot) / (mean_ms * 1e-3) / 1e9
-    print(json.dumps({
+    result = {
         "metric": "state GB/s (% of HBM peak) + (req,head) items/s, KDA commit & fused verify",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(mean_ms, 4),
@@ -525,7 +672,12 @@ def bench_kernel_workload(args):
         "roofline": {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": int(tot)},
-    }), flush=True)
+    }
+    if cpu_run is not None:
+        scratch = None
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = sampled_cpu_baseline(cpu_run, items, cpu_bytes)
+    print(json.dumps(result), flush=True)
 
 
 # ----------------------------------------------------------------- main

@@ -166,3 +166,74 @@ def test_source_digest_follows_code_not_comments(tmp_path, monkeypatch):
     # any code edit changes it, also one inside a string literal
     assert digest(src.replace("x + '/'", "x - '/'")) != base
     assert digest(src.replace("not/a", "not/b")) != base
+
+
+def test_sampled_cpu_baseline_runners_match_the_oracle():
+    """The single-kernel workloads' CPU-baseline runners pass the workload to the
+    oracle unchanged: on all items each equals a direct oracle call, and their
+    state-byte counts equal the bench's accounting."""
+    import torch
+    import oracle
+    import workloads as W
+    b = _bench()
+    H, B, T, RQ, S = 2, 5, 4, 4, 8
+    c = W.small_fused_case(3, H, B, T, RQ, S, null_rows=(1,), no_record_rows=(2,))
+    run, state_bytes = b._verify_cpu_runner(
+        True, H, B, T, RQ, c["state"], c["state_indices"], c["record_rows"], c["pending"],
+        c["corr"], c["kg"], c["a_log"][0], c["dt_bias"][0], W.LOWER_BOUND, c["window"])
+    run(np.arange(B * H, dtype=np.int64), 1)
+    state = c["state"].numpy().copy()
+    corr, kg = c["corr"].numpy().copy(), W.bits(c["kg"])
+    win = {n: W.bits(getattr(c["window"], n)) for n in ("q", "k", "v", "raw_g", "raw_beta")}
+    out = np.zeros((B * T, H * 128), np.uint16)
+    slots = c["state_indices"].numpy().astype(np.int32)
+    rows = c["record_rows"].numpy().astype(np.int32)
+    pend = c["pending"].numpy().astype(np.int32)
+    oracle.fused_replay_verify(heads=H, tokens=T, batch=B, a_log=c["a_log"][0].numpy(),
+                               dt_bias=c["dt_bias"][0].numpy(), lower_bound=W.LOWER_BOUND,
+                               state=state, state_slot_stride=H * 128 * 128,
+                               state_indices=slots, corr=corr, kg=kg, record_tokens=RQ,
+                               record_rows=rows, pending=pend, out=out, threads=1, **win)
+    rec = run.__closure__  # the runner's host copies, reached through its free variables
+    h = next(cell.cell_contents for cell in rec if isinstance(cell.cell_contents, dict))
+    assert np.array_equal(h["state"], state) and np.array_equal(h["corr"], corr)
+    assert np.array_equal(h["kg"], kg)
+    assert state_bytes(range(B * H)) == b.fused_bytes(slots, rows, pend, T, RQ, H)[0]
+    res = b.sampled_cpu_baseline(run, B * H, state_bytes, seconds=0.01)
+    assert res["kind"] == "oracle" and res["cores"] >= 1 and res["value"] > 0
+    assert res["single_thread"]["items_per_s"] > 0
+
+    # commit: two BF16 layers, src -> dst (disjoint), one boundary store
+    L, Q, S = 2, 4, 10
+    page = H * 128 * 128  # elements per slot
+    g = W._gen(5)
+    states = [W.bf16(W.normal(g, (S * page,), 0.1)) for _ in range(L)]
+    recs = [W.draw_records(g, B, H, Q) for _ in range(L)]
+    a_log, dt_bias = W.draw_gate_params(g, L, H)
+    src = np.array([1, 2, 0, 3, 4], np.int32)
+    dst = np.array([5, 6, 0, 7, 0], np.int32)
+    lens = np.array([2, 0, 3, 4, 1], np.int32)
+    bnd = np.array([8, 0, 0, 0, 0], np.int32)
+    blen = np.array([1, 0, 0, 0, 0], np.int32)
+    run, state_bytes = b._commit_cpu_runner(H, B, Q, states, [page] * L,
+                                            [r[0] for r in recs], [r[1] for r in recs], a_log,
+                                            dt_bias, src, lens, dst, bnd, blen, W.LOWER_BOUND)
+    run(np.arange(L * B * H, dtype=np.int64), 1)
+    want = [W.bits(t) for t in states]
+    oracle.commit(heads=H, window=Q, batch=B, state_bf16=True, state_layers=want,
+                  state_slot_strides=[page] * L,
+                  corr_layers=[r[0].numpy() for r in recs], corr_row_strides=[H * Q * 128] * L,
+                  kg_layers=[W.bits(r[1]) for r in recs], kg_row_strides=[H * Q * 256] * L,
+                  a_log=a_log.numpy(), dt_bias=dt_bias.numpy(), sources=src, commit_lens=lens,
+                  destinations=dst, boundaries=bnd, boundary_lens=blen,
+                  lower_bound=W.LOWER_BOUND, threads=1)
+    h_st = next(cell.cell_contents for cell in run.__closure__
+                if isinstance(cell.cell_contents, list)
+                and isinstance(cell.cell_contents[0], np.ndarray)
+                and cell.cell_contents[0].size == S * page)
+    for l in range(L):
+        assert np.array_equal(h_st[l], want[l]), l
+        assert not np.array_equal(h_st[l], W.bits(states[l])), l  # the pools moved
+    # live: requests 0 (with its boundary page) and 3; request 4 has a null destination
+    page_bytes = 128 * 128 * 2
+    assert state_bytes(range(L * B * H)) == L * H * (3 + 2) * page_bytes

@@ -1,7 +1,8 @@
 """GPU parity over seeded random combinations of the verify and fused options
 (window, record capacity, heads, batch, FP32/BF16 pool, gated output stage,
 variable-length windows, boundary stores, padded slot strides, null slots,
-missing record rows, edge pending counts), each against the FP64 oracle
+missing record rows, edge pending counts, key norms, the decay's lower
+bound), each against the FP64 oracle
 element by element. The single-option tests cover each option alone; these
 cover them together."""
 import numpy as np
@@ -23,6 +24,16 @@ def _lib():
 
     torch.cuda.init()
     yield
+
+
+# The decay's lower bound, drawn apart from the other draws (so they stay as
+# they were): the workloads' -5 half the time, else a degenerate end (0: no
+# decay; -60: decay products underflow) or a mild -0.5.
+LOWER_BOUNDS = (-5.0, -5.0, -5.0, 0.0, -0.5, -60.0)
+
+
+def _lower_bound(seed):
+    return float(np.random.default_rng(seed).choice(LOWER_BOUNDS))
 
 
 def _draw(seed):
@@ -90,11 +101,12 @@ def test_random_combination(seed):
                   norm_weight=weight.numpy(), norm_eps=eps)
     if align:
         kw.update(bounds=bounds, blens=blens)
+    lb = _lower_bound(2800 + seed)
     run_verify_case(fused=fused, H=H, B=B, T=T, RQ=RQ, state=state, slots=slots,
                     corr=corr.numpy().copy(), kg=W.bits(kg), a_log=a_log[0].numpy(),
                     dt_bias=dtb[0].numpy(), win=win, rows=rows,
                     pending=pending if fused else None, stride=stride, qsl=qsl,
-                    out_rows=out_rows, label=f"combination {seed}: {c}", **kw)
+                    out_rows=out_rows, lb=lb, label=f"combination {seed}: {c} lb={lb}", **kw)
 
 
 @pytest.mark.parametrize("seed", list(range(32)))
@@ -136,8 +148,9 @@ def test_random_conv_combination(seed):
                   raw_g=win["raw_g"], raw_beta=win["raw_beta"], x=W.bits(cv.x), pitch=cv.pitch,
                   conv_w=W.bits(cv.weight),
                   conv_b=W.bits(cv.bias) if r.integers(2) else None, pool=pool,
-                  strides=strides, rows=rows, pending=pending,
-                  label=f"conv combination {seed}: {c} {layout}", **kw)
+                  strides=strides, rows=rows, pending=pending, lb=_lower_bound(6800 + seed),
+                  label=f"conv combination {seed}: {c} {layout} lb={_lower_bound(6800 + seed)}",
+                  **kw)
 
 
 @pytest.mark.parametrize("seed", list(range(32)))
@@ -187,6 +200,6 @@ def test_random_commit_combination(seed):
     run_commit_case(H=H, B=B, Q=Q, bf16=bf16, layers_state=states, strides=strides,
                     corr_layers=corrs, kg_layers=kgs, a_log=a_log.numpy(), dt_bias=dtb.numpy(),
                     src=src, lens=lens, dst=dst, bnd=bnd if align else None,
-                    blen=blen if align else None, rows=rows,
+                    blen=blen if align else None, rows=rows, lb=_lower_bound(10800 + seed),
                     label=f"commit combination {seed}: L={L} H={H} B={B} Q={Q} bf16={bf16} "
-                          f"inplace={inplace} align={align}")
+                          f"inplace={inplace} align={align} lb={_lower_bound(10800 + seed)}")

@@ -214,6 +214,40 @@ def test_key_norm_edge(kind, bf16):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("lb", [0.0, -0.5, -60.0])
+@pytest.mark.parametrize("kind", ["verify", "fused", "commit", "fused_conv"])
+def test_lower_bound_edges(kind, lb, bf16):
+    """The decay's lower bound at its degenerate ends, through every kernel that
+    forms decays (fused page, KdaFused.decay; commit page, KdaCommit): lb = 0
+    gives d = 1 (the plain delta rule, nothing decays), lb = -60 drives d to
+    about e^-30 or below, so the decay products underflow within a window, and
+    -0.5 sits between. The workloads use -5 only."""
+    H, T, RQ = 3, 8, 8
+    if kind == "commit":
+        B, L, S = 6, 1, 16
+        states, strides, corrs, kgs, a_log, dtb = _commit_inputs(1400, L, H, B, RQ, bf16, S)
+        src = np.arange(1, B + 1, dtype=np.int32)
+        lens = np.array([8, 8, 5, 3, 1, 2], np.int32)
+        run_commit_case(H=H, B=B, Q=RQ, bf16=bf16, layers_state=states, strides=strides,
+                        corr_layers=corrs, kg_layers=kgs, a_log=a_log, dt_bias=dtb, src=src,
+                        lens=lens, dst=(src + B).astype(np.int32), lb=lb,
+                        label=f"commit lb={lb} bf16={bf16}")
+        return
+    B = 6
+    pending = np.array([0, 8, 3, 5, 1, 8], np.int32)
+    if kind == "fused_conv":
+        c = _conv_case(1410 + bf16, H, B, T, RQ, 10, bf16=bf16)
+        _run_conv(c, H, B, T, RQ, pending, f"fused conv lb={lb} bf16={bf16}", lb=lb)
+        return
+    c = _vf_case(1420 + bf16, H, B, T, RQ, 10, bf16=bf16)
+    run_verify_case(fused=kind == "fused", H=H, B=B, T=T, RQ=RQ, state=c["state"],
+                    slots=c["slots"], corr=c["corr"], kg=c["kg"], a_log=c["a_log"],
+                    dt_bias=c["dt_bias"], win=c["win"], rows=c["rows"],
+                    pending=pending if kind == "fused" else None, lb=lb,
+                    label=f"{kind} lb={lb} bf16={bf16}")
+
+
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_verify_windows(T, bf16):
     H, B = 3, 5

@@ -29,8 +29,9 @@ def _lib():
 
 # ---------------------------------------------------------------- plan steps
 
+@pytest.mark.parametrize("null_slot", [0, 2])
 @pytest.mark.parametrize("eager", [False, True])
-def test_plan_steps_bit_exact(eager):
+def test_plan_steps_bit_exact(eager, null_slot):
     import spec_decode_amd as kda
 
     rng = np.random.default_rng(3)
@@ -41,14 +42,14 @@ def test_plan_steps_bit_exact(eager):
     lens = rng.integers(-3, 12, B).astype(np.int32)
     pending = rng.integers(-5, 20, rows_n).astype(np.int32)
     eg = (rng.random(B) < 0.3).astype(np.int32) if eager else None
-    announce(f"plan: defer B={B} eager={eager}")
+    announce(f"plan: defer B={B} eager={eager} null_slot={null_slot}")
     d_lens, d_pend = dev(lens), dev(pending)
     kda.kda_defer_commit(batch=B, state_indices=dev(si), commit_lens=d_lens,
                          record_rows=dev(rows), pending=d_pend,
-                         eager=None if eg is None else dev(eg))
+                         eager=None if eg is None else dev(eg), null_slot=null_slot)
     torch.cuda.synchronize()
     r_lens, r_pend = lens.copy(), pending.copy()
-    oracle.defer(si, r_lens, rows, r_pend, eg)
+    oracle.defer(si, r_lens, rows, r_pend, eg, null_slot=null_slot)
     assert_exact("defer commit_lens", np_of(d_lens), r_lens)
     assert_exact("defer pending", np_of(d_pend), r_pend)
     for q in (1, 4, 8):
@@ -56,9 +57,10 @@ def test_plan_steps_bit_exact(eager):
         outs = [torch.full((B,), -99, dtype=torch.int32, device=DEV) for _ in range(4)]
         kda.kda_flush_plan(batch=B, spec_query_len=q, state_indices=dev(si),
                            record_rows=dev(rows), pending=dev(r_pend), commit_lens=outs[0],
-                           final_indices=outs[1], boundaries=outs[2], boundary_lens=outs[3])
+                           final_indices=outs[1], boundaries=outs[2], boundary_lens=outs[3],
+                           null_slot=null_slot)
         torch.cuda.synchronize()
-        ref = oracle.flush_plan(si, rows, r_pend, q)
+        ref = oracle.flush_plan(si, rows, r_pend, q, null_slot=null_slot)
         for name, g, r in zip(("commit_lens", "final", "boundaries", "boundary_lens"), outs, ref):
             assert_exact(f"flush {name} q={q}", np_of(g), r)
 
@@ -245,6 +247,72 @@ def test_lower_bound_edges(kind, lb, bf16):
                     dt_bias=c["dt_bias"], win=c["win"], rows=c["rows"],
                     pending=pending if kind == "fused" else None, lb=lb,
                     label=f"{kind} lb={lb} bf16={bf16}")
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("kind", ["verify", "fused", "commit", "fused_conv"])
+def test_nonzero_null_slot(kind, bf16):
+    """The null slot is an argument (the kernels page's plan steps and the
+    verify/commit operands compare slots against it): with null_slot = 3,
+    every slot 1..3 marks padding just as 0 does, so those items write zeros
+    to o (verify, fused) or nothing at all (commit), and their pages, records
+    and windows stay untouched."""
+    H, T, RQ, NULL = 3, 8, 8, 3
+    if kind == "commit":
+        B, L, S = 8, 1, 20
+        states, strides, corrs, kgs, a_log, dtb = _commit_inputs(1500, L, H, B, RQ, bf16, S)
+        src = np.array([1, 4, 3, 5, 6, 7, 2, 8], np.int32)   # 1, 3, 2: null sources
+        dst = np.array([9, 10, 11, 2, 12, 13, 14, 15], np.int32)  # 2: a null destination
+        bnd = np.array([16, 3, 17, 18, 19, 0, 1, 16], np.int32)
+        blen = np.array([2, 3, 1, 2, 4, 1, 1, 0], np.int32)
+        lens = np.array([4, 5, 3, 6, 8, 2, 7, 3], np.int32)
+        bnd[7] = 0  # (16 is request 0's boundary)
+        run_commit_case(H=H, B=B, Q=RQ, bf16=bf16, layers_state=states, strides=strides,
+                        corr_layers=corrs, kg_layers=kgs, a_log=a_log, dt_bias=dtb, src=src,
+                        lens=lens, dst=dst, bnd=bnd, blen=blen, null_slot=NULL,
+                        label=f"commit null_slot={NULL} bf16={bf16}")
+        return
+    B = 8
+    pending = np.array([0, 8, 3, 5, 1, 8, 2, 6], np.int32)
+    if kind == "fused_conv":
+        c = _conv_case(1510 + bf16, H, B, T, RQ, 12, bf16=bf16)
+        assert (c["slots"] <= NULL).any() and (c["slots"] > NULL).sum() >= 4
+        _run_conv(c, H, B, T, RQ, pending, f"fused conv null_slot={NULL} bf16={bf16}",
+                  null_slot=NULL)
+        return
+    c = _vf_case(1520 + bf16, H, B, T, RQ, 12, bf16=bf16)
+    assert (c["slots"] <= NULL).any() and (c["slots"] > NULL).sum() >= 4
+    run_verify_case(fused=kind == "fused", H=H, B=B, T=T, RQ=RQ, state=c["state"],
+                    slots=c["slots"], corr=c["corr"], kg=c["kg"], a_log=c["a_log"],
+                    dt_bias=c["dt_bias"], win=c["win"], rows=c["rows"],
+                    pending=pending if kind == "fused" else None, null_slot=NULL,
+                    label=f"{kind} null_slot={NULL} bf16={bf16}")
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 0.05])
+def test_fused_conv_q_scale(q_scale):
+    """The query scale of the convolution prologue is an argument (fused page,
+    KdaFused.kernel: q is normalised, then scaled); the workloads pass 128^-1/2."""
+    H, B, T, RQ = 3, 5, 8, 8
+    c = _conv_case(1530, H, B, T, RQ, 9, null_rows=(2,), norec_rows=(4,))
+    pending = np.array([0, 8, 3, 5, 1], np.int32)
+    _run_conv(c, H, B, T, RQ, pending, f"fused conv q_scale={q_scale}", q_scale=q_scale)
+
+
+@pytest.mark.parametrize("norm_eps", [0.0, 1e-3, 1.0])
+@pytest.mark.parametrize("fused", [False, True])
+def test_gated_output_norm_eps(fused, norm_eps):
+    """The gated RMSNorm's eps is an argument (fused page, KdaFused.kernel,
+    output stage: rstd = (mean(o^2) + eps)^-1/2); the workloads pass 1e-5."""
+    H, B, T, RQ = 3, 5, 8, 8
+    c = _vf_case(1540, H, B, T, RQ, 9, null_rows=(1,), norec_rows=(3,))
+    gate, weight, _ = W.draw_output_stage(W._gen(1541), B, T, H)
+    pending = np.array([0, 8, 3, 5, 1], np.int32)
+    run_verify_case(fused=fused, H=H, B=B, T=T, RQ=RQ, state=c["state"], slots=c["slots"],
+                    corr=c["corr"], kg=c["kg"], a_log=c["a_log"], dt_bias=c["dt_bias"],
+                    win=c["win"], rows=c["rows"], pending=pending if fused else None,
+                    gate=W.bits(gate), norm_weight=weight.numpy(), norm_eps=norm_eps,
+                    label=f"gated output fused={fused} eps={norm_eps}")
 
 
 @pytest.mark.parametrize("bf16", [False, True])

@@ -68,11 +68,27 @@ def commit_written(layers, H, B, Q, lens, src, dst, bnd, blen, rows, null_slot=0
     return out
 
 
+def pad_record_rows(records, pad, fill):
+    """Flat copy of records [rows, ...] with `pad` extra elements after each
+    row, set to `fill` (a value no correct read may see); returns (flat, row
+    stride in elements)."""
+    rows = records.shape[0]
+    n = int(np.prod(records.shape[1:]))
+    flat = np.full((rows, n + pad), fill, dtype=records.dtype)
+    flat[:, :n] = records.reshape(rows, n)
+    return flat.reshape(-1), n + pad
+
+
 def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_layers, a_log,
                     dt_bias, src, lens, dst, bnd=None, blen=None, rows=None,
-                    lb=W.LOWER_BOUND, null_slot=0, label="commit"):
-    """layers_state: per-layer flat host pools (uint16 bits or float32)."""
+                    lb=W.LOWER_BOUND, null_slot=0, label="commit", corr_strides=None,
+                    kg_strides=None):
+    """layers_state: per-layer flat host pools (uint16 bits or float32).
+    corr_strides / kg_strides: per-layer record row strides in elements
+    (default dense, H*Q*128 and H*Q*256)."""
     L = len(layers_state)
+    corr_strides = [H * Q * V] * L if corr_strides is None else list(corr_strides)
+    kg_strides = [H * Q * 2 * K] * L if kg_strides is None else list(kg_strides)
     announce(f"{label}: L={L} H={H} B={B} Q={Q} bf16={bf16} align={bnd is not None}")
     d_state = [to_dev(s) for s in layers_state]
     d_corr = [to_dev(c) for c in corr_layers]
@@ -83,9 +99,9 @@ def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_lay
                    state_dtype=kda.KDA_STATE_BF16 if bf16 else kda.KDA_STATE_F32,
                    state_addrs=[t.data_ptr() for t in d_state], state_slot_strides=strides,
                    corr_addrs=[t.data_ptr() for t in d_corr],
-                   corr_row_strides=[H * Q * V] * L,
+                   corr_row_strides=corr_strides,
                    kg_addrs=[t.data_ptr() for t in d_kg],
-                   kg_row_strides=[H * Q * 2 * K] * L,
+                   kg_row_strides=kg_strides,
                    a_log=dev(np.asarray(a_log, np.float32)),
                    dt_bias=dev(np.asarray(dt_bias, np.float32)), sources=i32(src),
                    commit_lens=i32(lens), destinations=i32(dst), boundaries=i32(bnd),
@@ -96,8 +112,8 @@ def run_commit_case(*, H, B, Q, bf16, layers_state, strides, corr_layers, kg_lay
     ref = [s.copy() for s in layers_state]
     oracle.commit(heads=H, window=Q, batch=B, state_bf16=bf16, state_layers=ref,
                   state_slot_strides=strides, corr_layers=corr_layers,
-                  corr_row_strides=[H * Q * V] * L, kg_layers=kg_layers,
-                  kg_row_strides=[H * Q * 2 * K] * L, a_log=a_log, dt_bias=dt_bias,
+                  corr_row_strides=corr_strides, kg_layers=kg_layers,
+                  kg_row_strides=kg_strides, a_log=a_log, dt_bias=dt_bias,
                   sources=src, commit_lens=lens, destinations=dst, boundaries=bnd,
                   boundary_lens=blen, record_rows=rows, lower_bound=lb, null_slot=null_slot)
     written = commit_written(L, H, B, Q, lens, src, dst, bnd, blen, rows, null_slot)

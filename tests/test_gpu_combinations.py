@@ -156,9 +156,10 @@ def test_random_conv_combination(seed):
 @pytest.mark.parametrize("seed", list(range(32)))
 def test_random_commit_combination(seed):
     """kda_commit over random layer counts (up to 18, more than one launch),
-    windows, pool types, padded per-layer strides, in-place or src -> dst,
-    boundaries, record rows and lengths (0, negative, above the window)."""
-    from _kda_cases import run_commit_case
+    windows, pool types, padded per-layer strides, padded record rows, in-place
+    or src -> dst, boundaries, record rows and lengths (0, negative, above the
+    window)."""
+    from _kda_cases import pad_record_rows, run_commit_case
     r = np.random.default_rng(10000 + seed)
     L = int(r.choice([1, 1, 2, 3, 5, 17, 18]))
     H = int(r.integers(1, 4))
@@ -197,8 +198,20 @@ def test_random_commit_combination(seed):
         for b in range(B):
             if r.random() < 0.15:
                 rows[b] = -1
+    # Half the combinations pad the record rows (drawn apart, so the other draws
+    # stay); the padding holds NaN, which no correct read may see.
+    r2 = np.random.default_rng(10900 + seed)
+    corr_strides = kg_strides = None
+    if r2.integers(2):
+        padded = [pad_record_rows(corrs[l], 4 * int(r2.integers(1, 9)), np.float32(np.nan))
+                  for l in range(L)]
+        corrs, corr_strides = [x[0] for x in padded], [x[1] for x in padded]
+        padded = [pad_record_rows(kgs[l], 8 * int(r2.integers(1, 9)), np.uint16(0x7FC0))
+                  for l in range(L)]
+        kgs, kg_strides = [x[0] for x in padded], [x[1] for x in padded]
     run_commit_case(H=H, B=B, Q=Q, bf16=bf16, layers_state=states, strides=strides,
                     corr_layers=corrs, kg_layers=kgs, a_log=a_log.numpy(), dt_bias=dtb.numpy(),
+                    corr_strides=corr_strides, kg_strides=kg_strides,
                     src=src, lens=lens, dst=dst, bnd=bnd if align else None,
                     blen=blen if align else None, rows=rows, lb=_lower_bound(10800 + seed),
                     label=f"commit combination {seed}: L={L} H={H} B={B} Q={Q} bf16={bf16} "

@@ -71,8 +71,9 @@ int kda_decay(const uint16_t* raw_g, int64_t tokens, int heads, const float* a_l
   KDA_REQUIRE(raw_g && a_log && dt_bias && out, "kda_decay: null pointer argument");
   KDA_REQUIRE(aligned16(raw_g) && aligned16(out) && aligned16(dt_bias),
               "kda_decay: raw_g, dt_bias and out must be 16-byte aligned");
-  const int64_t chunks = tokens * heads * (kda::K / 4);  // the kernel's threads: 4 channels each
-  KDA_REQUIRE((chunks + 255) / 256 < (int64_t)1 << 31, "kda_decay: tensor too large");
+  // The kernel strides over 4-channel chunks with a capped grid; the only
+  // limit is the element count's 64-bit range.
+  KDA_REQUIRE(tokens <= INT64_MAX / kda::K / heads, "kda_decay: tensor too large");
   return launched(kda::launch_decay(raw_g, tokens, heads, a_log, dt_bias, lower_bound, out,
                                     reinterpret_cast<hipStream_t>(stream)),
                   "kda_decay");

@@ -104,9 +104,8 @@ def test_rejects_bad_arguments_without_launch(lib):
     assert lib.kda_decay(fake, ctypes.c_int64(3), ctypes.c_int(2), fake, fake,
                          ctypes.c_float(float("nan")), fake, P(None)) == 1
     assert "finite" in _err(lib)
-    # a grid beyond 2^31 - 1 workgroups: one thread per 4 channels, 256 per workgroup
-    # (2^28 tokens x 64 heads x 32 threads = 2^31 workgroups)
-    assert lib.kda_decay(fake, ctypes.c_int64(1 << 28), ctypes.c_int(64), fake, fake,
+    # an element count beyond the 64-bit range (2^56 tokens x 64 heads x 128 channels)
+    assert lib.kda_decay(fake, ctypes.c_int64(1 << 56), ctypes.c_int(64), fake, fake,
                          ctypes.c_float(-5.0), fake, P(None)) == 1
     assert "too large" in _err(lib)
 

@@ -170,7 +170,8 @@ FUSED_SOURCES = ["spec_decode_amd/csrc/fused.hip", "spec_decode_amd/csrc/verify_
                  "spec_decode_amd/csrc/kda_device.h"]
 COMMIT_SOURCES = ["spec_decode_amd/csrc/commit.hip", "spec_decode_amd/csrc/kda_device.h"]
 CONV_SOURCES = FUSED_SOURCES + ["spec_decode_amd/csrc/fused_conv.hip",
-                                "spec_decode_amd/csrc/fused_conv_packed.hip"]
+                                "spec_decode_amd/csrc/fused_conv_packed.hip",
+                                "spec_decode_amd/csrc/fused_conv_window_major.hip"]
 
 
 def fused_variant(args):

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["abi.hip", "plan.hip", "decay.hip", "commit.hip", "fused.hip", "fused_conv.hip",
-           "fused_conv_packed.hip", "gate_proj.hip", "probe.hip"]
+           "fused_conv_packed.hip", "fused_conv_window_major.hip", "gate_proj.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

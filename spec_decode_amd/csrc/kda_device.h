@@ -325,6 +325,8 @@ hipError_t launch_verify_conv(const VerifyParams& p, int tokens, bool bf16, int 
                               hipStream_t stream);
 hipError_t launch_verify_conv_packed(const VerifyParams& p, int tokens, bool bf16, int batch,
                                      hipStream_t stream);
+hipError_t launch_verify_conv_window_major(const VerifyParams& p, int tokens, bool bf16,
+                                           int batch, hipStream_t stream);
 hipError_t launch_gate_projection(const uint16_t* f_a, int64_t sa, const uint16_t* f_b,
                                   uint16_t* out, int64_t tokens, int heads, hipStream_t stream);
 hipError_t launch_page_rw(float* state, int64_t slot_stride, const int32_t* slots, int batch,

@@ -1,7 +1,7 @@
 // The verify kernel template: fused replay+verify and the stock verify over
 // FP32 or BF16 state pages, with the optional convolution prologue and gated
-// RMSNorm output stage. Instantiated by fused.hip, fused_conv.hip and
-// fused_conv_packed.hip.
+// RMSNorm output stage. Instantiated by fused.hip, fused_conv.hip,
+// fused_conv_packed.hip and fused_conv_window_major.hip.
 //
 // Method (the vLLM page "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.
 // kda.fused", module docstring and KdaFused): per (request, head) item,
@@ -47,7 +47,9 @@
 //
 // Convolution prologue (fused page, KdaFused.kernel; template argument CONV, 0
 // without it, 1 for window pools of any strides, 2 for packed dim-first pools
-// whose per-wave window blocks move as 16-byte chunks through LDS): q, k
+// whose per-wave window blocks move as 16-byte chunks through LDS, 3 for
+// window-major pools whose taps, inputs and new entries move as 16-byte
+// chunks through a per-wave LDS stage): q, k
 // and v are computed in the kernel from a packed row x of pre-activations, each
 // channel's 4-tap causal convolution over its window in the conv pool followed
 // by SiLU. The window holds the previous step's [2 history values, its T
@@ -224,18 +226,29 @@ __device__ __forceinline__ void conv_silu(const float (&seq)[3 + T], const float
 // multiple of 8 elements, 16-byte aligned base). In the packed layout the
 // windows of a wave's 64 channels are one contiguous block of 128 W bytes,
 // which the wave moves with 16-byte accesses through LDS.
-constexpr int CONV_NONE = 0, CONV_STRIDED = 1, CONV_PACKED = 2;
+constexpr int CONV_NONE = 0, CONV_STRIDED = 1, CONV_PACKED = 2, CONV_WINDOW_MAJOR = 3;
 constexpr int CONV_BLOCK = 64 * (MAX_T + 2) * 2;  // LDS bytes of one wave's block, W <= MAX_T + 2
+// Window-major pools (channel stride 1, tap and slot strides and the input
+// rows 16-byte aligned): a wave stages its 64 channels' 3 taps and T inputs as
+// rows of 128 bytes, [tap 0, tap 1, tap 2, x_0 .. x_{T-1}], moved in and out
+// with 16-byte accesses. The new window [tap 1, tap 2, x_0 .. x_{T-1}] is rows
+// 1 .. T + 2 of the stage.
+constexpr int CONV_STAGE = 64 * (MAX_T + 3) * 2;  // LDS bytes of one wave's stage
+template <int MODE>
+constexpr int conv_area() { return MODE == CONV_WINDOW_MAJOR ? CONV_STAGE : CONV_BLOCK; }
 
 // One channel's convolution operands as raw BF16 bits: the T inputs, the 4
 // weights and the bias; strided layout: the 3 window taps at the item's
 // offset; packed layout: the wave's window block, 16-byte chunks lane and
-// lane + 64 (clamped to the last chunk).
+// lane + 64 (clamped to the last chunk); window-major layout: instead of the
+// inputs and taps, the lane's 16-byte chunk of the wave's input rows (row
+// lane / 8, channels 8 (lane % 8) .. +7) and of its tap rows.
 template <int T>
 struct ConvIn {
   uint32_t tap[3];
   u32x4 blk[2];
   uint32_t x[T];
+  u32x4 xv, tv;
   uint32_t w[4];
   uint32_t bias;
 };
@@ -244,12 +257,23 @@ struct ConvIn {
 // taps start at the wave-uniform offset off = max(n - 1, 0) <= RQ - 1, so the
 // last one, off + 2 <= RQ + 1, lies inside the window of RQ + 2 entries. The
 // inputs, weights and bias do not depend on n and are issued first.
-template <int T, int MODE>
+template <int T, int MODE, bool NT = false>
 __device__ __forceinline__ void conv_load(const VerifyParams& p, ConvIn<T>& ci, int slot,
                                           int64_t col, int64_t head_row, int part,
                                           int64_t dim, int64_t tok0, int off) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  if constexpr (MODE == CONV_WINDOW_MAJOR) {
+    // Row lane / 8 (clamped: lanes past the last row load it again), channels
+    // 8 (lane % 8) .. +7 of the wave's 64 (col - lane .. col - lane + 63).
+    const int r = lane >> 3;
+    const int64_t ch = col - lane + 8 * (lane & 7);
+    const u32x4* const xp =
+        reinterpret_cast<const u32x4*>(p.x + (tok0 + (r < T ? r : T - 1)) * p.x_stride + ch);
+    ci.xv = NT ? __builtin_nontemporal_load(xp) : *xp;
+  } else {
 #pragma unroll
-  for (int t = 0; t < T; ++t) ci.x[t] = p.x[(tok0 + t) * p.x_stride + col];
+    for (int t = 0; t < T; ++t) ci.x[t] = p.x[(tok0 + t) * p.x_stride + col];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) ci.w[i] = p.conv_w[(part * 4 + i) * dim + head_row];
   // Unconditional (without a bias, from the weights, col < 3HK <= 12HK, then
@@ -257,12 +281,18 @@ __device__ __forceinline__ void conv_load(const VerifyParams& p, ConvIn<T>& ci, 
   const bool has_bias = p.conv_b != nullptr;
   const uint32_t braw = (has_bias ? p.conv_b : p.conv_w)[col];
   ci.bias = has_bias ? braw : 0u;
-  if constexpr (MODE == CONV_PACKED) {
+  if constexpr (MODE == CONV_WINDOW_MAJOR) {
+    // Tap row off + lane / 8 (lanes 0..23; the others load the last one again).
+    const int r = lane >> 3;
+    const int64_t ch = col - lane + 8 * (lane & 7);
+    const u32x4* const tp = reinterpret_cast<const u32x4*>(
+        p.conv + (int64_t)slot * p.conv_ss + (int64_t)(off + (r < 3 ? r : 2)) * p.conv_ts + ch);
+    ci.tv = NT ? __builtin_nontemporal_load(tp) : *tp;
+  } else if constexpr (MODE == CONV_PACKED) {
     // The block of channels col0 .. col0 + 63 (col0 = col rounded down to 64:
     // a wave's channels), 8 W chunks of 16 bytes.
     const int W = p.rq + 2;
     const int nchunk = 8 * W;
-    const int lane = threadIdx.x & (WAVE - 1);
     const u32x4* bp = reinterpret_cast<const u32x4*>(
         p.conv + (int64_t)slot * p.conv_ss + (col & ~(int64_t)63) * W);
     ci.blk[0] = bp[lane < nchunk ? lane : nchunk - 1];
@@ -281,12 +311,40 @@ __device__ __forceinline__ void conv_load(const VerifyParams& p, ConvIn<T>& ci, 
 // bits die as they are converted. Packed layout: the block goes to the wave's
 // LDS area blk_s (CONV_BLOCK bytes), each lane reads its taps there and writes
 // its new entries back, and the wave stores the whole block.
-template <int T, int MODE>
+template <int T, int MODE, bool NT = false>
 __device__ __forceinline__ void conv_part(const VerifyParams& p, const ConvIn<T>& ci, int slot,
                                           int64_t col, int off, uint8_t* blk_s,
                                           uint32_t (&y)[T]) {
   uint32_t tap[3];
-  if constexpr (MODE == CONV_PACKED) {
+  uint32_t xin[T];
+  if constexpr (MODE == CONV_WINDOW_MAJOR) {
+    // Stage rows [tap 0..2, x_0 .. x_{T-1}] of 8 chunks each, read the lane's
+    // channel back, then store rows 1 .. T + 2 as window entries 0 .. T + 1.
+    const int lane = threadIdx.x & (WAVE - 1);
+    u32x4* const sv = reinterpret_cast<u32x4*>(blk_s);
+    const uint16_t* const sh = reinterpret_cast<const uint16_t*>(blk_s);
+    if (lane < 24) sv[lane] = ci.tv;
+    if (lane < 8 * T) sv[24 + lane] = ci.xv;
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 3; ++i) tap[i] = sh[i * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xin[t] = sh[(3 + t) * 64 + lane];
+    uint16_t* const wp = p.conv + (int64_t)slot * p.conv_ss + (col - lane);
+    constexpr int NCH = 8 * (T + 2);
+#pragma unroll
+    for (int q0 = 0; q0 < NCH; q0 += WAVE) {
+      const int q = q0 + lane;
+      if (q < NCH) {
+        u32x4* const dp =
+            reinterpret_cast<u32x4*>(wp + (int64_t)(q >> 3) * p.conv_ts + 8 * (q & 7));
+        if constexpr (NT)
+          __builtin_nontemporal_store(sv[8 + q], dp);
+        else
+          *dp = sv[8 + q];
+      }
+    }
+  } else if constexpr (MODE == CONV_PACKED) {
     const int W = p.rq + 2;
     const int nchunk = 8 * W;
     const int lane = threadIdx.x & (WAVE - 1);
@@ -301,6 +359,8 @@ __device__ __forceinline__ void conv_part(const VerifyParams& p, const ConvIn<T>
     mine[1] = (uint16_t)tap[2];
 #pragma unroll
     for (int t = 0; t < T; ++t) mine[2 + t] = (uint16_t)ci.x[t];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xin[t] = ci.x[t];
     wave_lds_sync();
     u32x4* const bp = reinterpret_cast<u32x4*>(
         p.conv + (int64_t)slot * p.conv_ss + (col & ~(int64_t)63) * W);
@@ -314,13 +374,15 @@ __device__ __forceinline__ void conv_part(const VerifyParams& p, const ConvIn<T>
     wp[p.conv_ts] = (uint16_t)tap[2];
 #pragma unroll
     for (int t = 0; t < T; ++t) wp[(int64_t)(2 + t) * p.conv_ts] = (uint16_t)ci.x[t];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xin[t] = ci.x[t];
   }
   float seq[3 + T];
   float w[4];
 #pragma unroll
   for (int i = 0; i < 3; ++i) seq[i] = bf16_bits_to_f32(tap[i]);
 #pragma unroll
-  for (int t = 0; t < T; ++t) seq[3 + t] = bf16_bits_to_f32(ci.x[t]);
+  for (int t = 0; t < T; ++t) seq[3 + t] = bf16_bits_to_f32(xin[t]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = bf16_bits_to_f32(ci.w[i]);
   conv_silu<T>(seq, w, bf16_bits_to_f32(ci.bias), y);
@@ -471,11 +533,12 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   ConvIn<T> cin0, cin1;  // lower: q part, k part; upper: v part in cin0
   const int64_t dim = (int64_t)H * K;
   const int conv_off = n > 0 ? n - 1 : 0;
-  // Packed window blocks stage through x_s, which is first written after the
-  // prologue's part one: areas 2w, 2w + 1 (q, k) of lower wave w, w + 2 (v) of
-  // upper wave w, 6 * CONV_BLOCK <= sizeof x_s.
+  // Packed window blocks and window-major stages go through x_s, which is
+  // first written after the prologue's part one: areas 2w, 2w + 1 (q, k) of
+  // lower wave w, w + 2 (v) of upper wave w, 6 areas <= sizeof x_s.
   uint8_t* const blk_s = reinterpret_cast<uint8_t*>(&x_s[0][0]);
-  static_assert(6 * CONV_BLOCK <= 16 * XP * sizeof(float), "window blocks fit in x_s");
+  constexpr int CA = conv_area<CONV>();
+  static_assert(6 * CA <= 16 * XP * sizeof(float), "window blocks fit in x_s");
   uint32_t okb[MAX_T], ogb[MAX_T];
   float ou[MAX_T];
   uint32_t rbb = 0;
@@ -508,8 +571,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   // loaded values at once.
   if (lower) {
     if constexpr (CONV) {
-      conv_load<T, CONV>(p, cin0, slot, 0 * dim + head_row, head_row, 0, dim, tok0, conv_off);
-      conv_load<T, CONV>(p, cin1, slot, 1 * dim + head_row, head_row, 1, dim, tok0, conv_off);
+      conv_load<T, CONV, STREAM>(p, cin0, slot, 0 * dim + head_row, head_row, 0, dim, tok0,
+                                 conv_off);
+      conv_load<T, CONV, STREAM>(p, cin1, slot, 1 * dim + head_row, head_row, 1, dim, tok0,
+                                 conv_off);
 #pragma unroll
       for (int t = 0; t < T; ++t) gb[t] = p.g[(tok0 + (t < L ? t : last)) * H * K + head_row];
     } else {
@@ -538,10 +603,10 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     __builtin_amdgcn_sched_barrier(0);
     const float ea = __expf(a_log_h);
     if constexpr (CONV) {
-      conv_part<T, CONV>(p, cin0, slot, 0 * dim + head_row, conv_off,
-                         blk_s + 2 * wave * CONV_BLOCK, qb);
-      conv_part<T, CONV>(p, cin1, slot, 1 * dim + head_row, conv_off,
-                         blk_s + (2 * wave + 1) * CONV_BLOCK, kb);
+      conv_part<T, CONV, STREAM>(p, cin0, slot, 0 * dim + head_row, conv_off,
+                                 blk_s + 2 * wave * CA, qb);
+      conv_part<T, CONV, STREAM>(p, cin1, slot, 1 * dim + head_row, conv_off,
+                                 blk_s + (2 * wave + 1) * CA, kb);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -560,7 +625,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
     // The v part's convolution operands go before the page, so that its
     // convolution runs while the page streams in.
     if constexpr (CONV) {
-      conv_load<T, CONV>(p, cin0, slot, 2 * dim + head_row, head_row, 2, dim, tok0, conv_off);
+      conv_load<T, CONV, STREAM>(p, cin0, slot, 2 * dim + head_row, head_row, 2, dim, tok0,
+                                 conv_off);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kContig) {
@@ -588,8 +654,8 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
       // Before the record loads: their count depends on n, so a wait placed
       // after them could not tell the convolution's operands from the page.
       __builtin_amdgcn_sched_barrier(0);
-      conv_part<T, CONV>(p, cin0, slot, 2 * dim + head_row, conv_off, blk_s + (wave + 2) * CONV_BLOCK,
-                         vb);
+      conv_part<T, CONV, STREAM>(p, cin0, slot, 2 * dim + head_row, conv_off,
+                                 blk_s + (wave + 2) * CA, vb);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (FUSED) {

@@ -251,7 +251,8 @@ def window_np(win: "W.Window"):
 
 # ---------------------------------------------------------------- fused + convolution
 
-CONV_LAYOUTS = ("dim_first", "window_major", "dim_first_padded", "dim_first_slot_pad")
+CONV_LAYOUTS = ("dim_first", "window_major", "dim_first_padded", "dim_first_slot_pad",
+                "window_major_padded", "window_major_odd")
 
 
 def conv_pool_layout(S, H, W, dim_first=True, layout=None):
@@ -259,12 +260,16 @@ def conv_pool_layout(S, H, W, dim_first=True, layout=None):
     (dim-first, the packed layout) or [S, W, 3HK] (window-major); layout, when
     given, also names 'dim_first_padded' (channel stride W + 1) and
     'dim_first_slot_pad' (slot stride 3HK*W + 4, not a multiple of 8), which the
-    library serves with its strided code."""
+    library serves with its strided code, 'window_major_padded' (rows of 3HK + 8
+    elements, still 16-byte aligned: the window-major code) and
+    'window_major_odd' (rows of 3HK + 3 elements: the strided code)."""
     hk3 = 3 * H * K
     layout = layout or ("dim_first" if dim_first else "window_major")
     return {"dim_first": (hk3 * W, W, 1), "window_major": (hk3 * W, 1, hk3),
             "dim_first_padded": (hk3 * (W + 1), W + 1, 1),
-            "dim_first_slot_pad": (hk3 * W + 4, W, 1)}[layout]
+            "dim_first_slot_pad": (hk3 * W + 4, W, 1),
+            "window_major_padded": ((hk3 + 8) * W, 1, hk3 + 8),
+            "window_major_odd": ((hk3 + 3) * W, 1, hk3 + 3)}[layout]
 
 
 def conv_pool_build(win, strides, seed):

@@ -501,6 +501,20 @@ def test_fused_conv_pool_layouts(layout, T, RQ, bf16):
     _run_conv(c, H, B, T, RQ, pending, f"fused conv {layout} T={T} RQ={RQ}")
 
 
+@pytest.mark.parametrize("layout", ["window_major", "window_major_padded"])
+def test_fused_conv_unaligned_input_rows(layout):
+    """Input rows whose pitch is not a multiple of 8 elements: a window-major
+    pool then goes through the strided code instead of the 16-byte stage."""
+    H, B, T, RQ = 3, 6, 8, 8
+    c = _conv_case(960, H, B, T, RQ, 9, null_rows=(2,), norec_rows=(4,), layout=layout)
+    pitch2 = c["pitch"] + 3
+    x2 = np.zeros((B * T, pitch2), np.uint16)
+    x2[:, :c["pitch"]] = c["x"].reshape(B * T, c["pitch"])
+    c.update(x=x2, pitch=pitch2)
+    pending = np.array([0, 8, 3, 5, 1, 7], np.int32)
+    _run_conv(c, H, B, T, RQ, pending, f"fused conv {layout} pitch={pitch2}")
+
+
 @pytest.mark.parametrize("T,bf16", [(3, False), (8, False), (4, True)])
 def test_fused_conv_gated_output(T, bf16):
     H, B, RQ = 3, 5, 8

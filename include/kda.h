@@ -269,8 +269,13 @@ int kda_fused_replay_verify(int heads, int tokens, int batch, const uint16_t* q,
  *                        W = record_tokens + 2 (tap stride 1, channel stride W),
  *                        a slot stride that is a multiple of 8 and a 16-byte
  *                        aligned base is moved in 16-byte chunks, each wave's
- *                        64 windows as one block; other pools use 2-byte
- *                        accesses
+ *                        64 windows as one block. A window-major pool (channel
+ *                        stride 1) whose tap and slot strides are multiples
+ *                        of 8 and whose base is 16-byte aligned, with x 16-byte
+ *                        aligned and x_row_stride a multiple of 8, moves its
+ *                        taps, inputs and new entries in 16-byte chunks through
+ *                        a per-wave LDS stage. Other pools use 2-byte accesses
+ *                        (the results are the same bits)
  *   q_scale              finite (the pages use 128^-1/2)
  *   raw_g, raw_beta, a_log, dt_bias, lower_bound, state_dtype, state,
  *   state_slot_stride, state_indices, null_slot, corr, kg, record_tokens,

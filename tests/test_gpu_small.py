@@ -515,6 +515,27 @@ def test_fused_conv_unaligned_input_rows(layout):
     _run_conv(c, H, B, T, RQ, pending, f"fused conv {layout} pitch={pitch2}")
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_fused_conv_window_major_matches_strided(bf16):
+    """The window-major 16-byte stage and the strided code give the same bits:
+    the same inputs through a window-major pool (rows of 3HK) and through one
+    with rows of 3HK + 3 (the strided code), every output compared exactly,
+    the windows by their logical entries."""
+    H, B, T, RQ, S = 3, 6, 8, 8, 9
+    pending = np.array([0, 8, 3, 5, 1, 7], np.int32)
+    res = []
+    for layout in ("window_major", "window_major_odd"):
+        c = _conv_case(970 + bf16, H, B, T, RQ, S, bf16=bf16, null_rows=(2,), norec_rows=(4,),
+                       layout=layout)
+        gpu, _ = _run_conv(c, H, B, T, RQ, pending, f"fused conv {layout} bf16={bf16}")
+        ss, cs, ts = c["strides"]
+        idx = (np.arange(S)[:, None, None] * ss + np.arange(3 * H * K)[None, :, None] * cs +
+               np.arange(RQ + 2)[None, None, :] * ts)
+        res.append(dict(gpu, pool=gpu["pool"][idx]))
+    for name in ("out", "state", "corr", "kg", "pool"):
+        assert_exact(f"window-major stage vs strided code: {name}", res[0][name], res[1][name])
+
+
 @pytest.mark.parametrize("T,bf16", [(3, False), (8, False), (4, True)])
 def test_fused_conv_gated_output(T, bf16):
     H, B, RQ = 3, 5, 8

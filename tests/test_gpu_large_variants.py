@@ -1,7 +1,7 @@
 """The step's variants at the large decode batch's size (H=64, B=512, q=8, a
 2 GiB FP32 pool), in the launch configuration the benchmark times: the gated
 RMSNorm output stage, and the convolution prologue over a packed dim-first
-window pool. Sampled requests (null slots, a missing record row, every pending
+and over a window-major window pool. Sampled requests (null slots, a missing record row, every pending
 count) are recomputed by the oracle on compact copies; pages nobody writes are
 compared bit for bit over the whole pool."""
 import numpy as np
@@ -135,8 +135,11 @@ def test_large_decode_gated_output_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("layout", ["dim_first", "window_major"])
 @pytest.mark.parametrize("bf16", [False, True])
-def test_large_decode_conv_prologue_packed_pool_sampled(bf16):
+def test_large_decode_conv_prologue_sampled(bf16, layout):
+    """The benchmark's --conv step takes the window-major pool by default; the
+    packed dim-first pool runs the packed code."""
     import spec_decode_amd as kda
     g, slots, rows, pending_row, a_log, dtb, corr, kg = _plan(940)
     page = H * V * K
@@ -144,12 +147,14 @@ def test_large_decode_conv_prologue_packed_pool_sampled(bf16):
     cv = W.draw_conv_inputs(W._gen(941), B, T, H, RQ, S)
     x, w_bits, b_bits = W.bits(cv.x), W.bits(cv.weight), W.bits(cv.bias)
     pool = W.bits(cv.window)  # [S, 3HK, RQ + 2]: the packed dim-first layout
-    strides = conv_pool_layout(S, H, RQ + 2)
+    strides = conv_pool_layout(S, H, RQ + 2, layout=layout)
+    # The pool as the GPU holds it: [S, 3HK, RQ + 2] or [S, RQ + 2, 3HK].
+    g_in = pool if layout == "dim_first" else np.ascontiguousarray(pool.transpose(0, 2, 1))
     d_state = W.draw_state(942, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
     before = d_state.clone()
-    d_corr, d_kg, d_pool = dev(corr), dev_bf16(kg), dev_bf16(pool.reshape(-1))
+    d_corr, d_kg, d_pool = dev(corr), dev_bf16(kg), dev_bf16(g_in.reshape(-1))
     out = torch.zeros((B * T, H * V), dtype=torch.bfloat16, device=DEV)
-    announce(f"large decode, convolution prologue, packed dim-first window pool, "
+    announce(f"large decode, convolution prologue, {layout} window pool, "
              f"{'BF16' if bf16 else 'FP32'} state pool")
     kda.kda_fused_conv_replay_verify(
         heads=H, tokens=T, batch=B, x=dev_bf16(x), x_row_stride=cv.pitch,
@@ -161,7 +166,9 @@ def test_large_decode_conv_prologue_packed_pool_sampled(bf16):
         record_tokens=RQ, record_rows=dev(rows), pending=dev(pending_row), out=out)
     torch.cuda.synchronize()
     _untouched("conv", d_state, before, slots, rows, pending_row)
-    g_pool = np_of(d_pool).reshape(S, 3 * H * K, RQ + 2)
+    g_pool = np_of(d_pool).reshape(g_in.shape)
+    if layout == "window_major":
+        g_pool = np.ascontiguousarray(g_pool.transpose(0, 2, 1))
     live_slots = set(int(s) for s in slots if s > 0)
     for s in range(S):
         if s not in live_slots:
@@ -175,7 +182,7 @@ def test_large_decode_conv_prologue_packed_pool_sampled(bf16):
     for j, b in enumerate(R):
         if slots[b] > 0:
             m_pool[j + 1] = pool[int(slots[b])]
-    m_strides = conv_pool_layout(nR + 1, H, RQ + 2)
+    m_strides = conv_pool_layout(nR + 1, H, RQ + 2)  # the oracle's copy stays dim-first
     m_out = np.zeros((nR * T, H * V), np.uint16)
     announce(f"large decode conv: oracle on {nR} sampled requests")
     flat = m_pool.reshape(-1)
@@ -196,7 +203,7 @@ def test_large_decode_conv_prologue_packed_pool_sampled(bf16):
             assert_exact(f"conv windows request {b}", g_pool[int(slots[b])], m_pool[j + 1])
     # The recorded keys against the plain FP64 convolution and SiLU.
     share = check_conv_keys_plain("conv", np_of(d_kg), H=H, T=T, RQ=RQ, x=x, pitch=cv.pitch,
-                                  conv_w=w_bits, conv_b=b_bits, pool=pool, strides=strides,
+                                  conv_w=w_bits, conv_b=b_bits, pool=g_in, strides=strides,
                                   slots=slots[R], rows=rows[R], pending=pending_row,
                                   tok_of=lambda j: R[j] * T)
     announce(f"large decode conv: keys match the plain SiLU ({100 * share:.3f}% near a tie)")

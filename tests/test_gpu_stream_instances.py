@@ -6,13 +6,18 @@ runs the plain one. Items are independent, so the same requests run as one
 launch (streaming) and as two launches of half the batch (plain) must leave
 the pool, the records and the outputs bit for bit equal. Neither side is the
 oracle: the oracle pins both through the other GPU tests; this one pins that
-the instance choice changes nothing but the cache policy.
+the instance choice changes nothing but the cache policy. The one exception
+is the commit of FP32 pages, whose streaming kernel folds on the matrix cores
+and the plain one on the vector ALU: there the two agree within the FP32
+tolerance, and the streaming result is checked against the oracle here.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
+from _compare import assert_f32_close
 from _kda_cases import DEV, announce
 
 pytestmark = pytest.mark.gpu
@@ -85,20 +90,31 @@ def test_fused_streaming_instance_matches_plain(gated, T, pool):
     _assert_same(one, two, ("state", "corr", "kg", "out"))
 
 
-@pytest.mark.parametrize("pool", ["f32", "bf16"])
-def test_commit_streaming_instance_matches_plain(pool):
+@pytest.mark.parametrize("pool,Q,align", [("f32", 8, False), ("bf16", 8, False),
+                                          ("f32", 3, False), ("f32", 8, True), ("f32", 5, True)])
+def test_commit_streaming_instance_matches_plain(pool, Q, align):
+    """Windows of 3, 5 and 8 tokens, with and without boundary stores (the
+    boundary pages beyond every source page, two of them null). BF16 pools:
+    the same bits. FP32 pools: the two within the FP32 tolerance, and 10
+    sampled requests of the streaming launch against the oracle."""
     import spec_decode_amd as kda
     bf16 = pool == "bf16"
     es = 2 if bf16 else 4
-    B, Q = (160 if bf16 else 80), 8
+    B = 160 if bf16 else 80
     page = H * V * K
     assert B * page * es > MALL >= (B // 2) * page * es
-    S = B + 5
-    g = W._gen(960 + bf16)
-    src = (W.permutation(g, S - 1) + 1)[:B].to(torch.int32)
+    S = B + 5 + (B if align else 0)
+    g = W._gen(960 + bf16 + 2 * Q + 20 * align)
+    src = (W.permutation(g, B + 4) + 1)[:B].to(torch.int32)
     src[[3, 50]] = 0
     rows = W.permutation(g, B).to(torch.int32)
     lens = W.uniform_int(g, 0, Q, B).to(torch.int32)
+    bounds = blens = None
+    if align:
+        # Boundary pages of their own, beyond every source page; some null.
+        bounds = (B + 5 + W.permutation(g, B)).to(torch.int32)
+        bounds[[7, 61]] = 0
+        blens = W.uniform_int(g, 0, Q + 1, B).to(torch.int32)
     corr, kg = W.draw_records(g, B, H, Q)
     a_log, dtb = W.draw_gate_params(g, 1, H)
     state0 = W.draw_state(962 + bf16, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
@@ -113,16 +129,57 @@ def test_commit_streaming_instance_matches_plain(pool):
                        kg_addrs=[d_kg.data_ptr()], kg_row_strides=[H * Q * 2 * K],
                        a_log=a_log.to(DEV), dt_bias=dtb.to(DEV), sources=s,
                        commit_lens=lens[lo:hi].to(DEV), destinations=s,
+                       boundaries=None if bounds is None else bounds[lo:hi].to(DEV),
+                       boundary_lens=None if blens is None else blens[lo:hi].to(DEV),
                        record_rows=rows[lo:hi].to(DEV), lower_bound=W.LOWER_BOUND)
 
-    announce(f"commit, streaming vs plain instance, H={H} B={B} window {Q}, {pool} pool")
+    announce(f"commit, streaming vs plain instance, H={H} B={B} window {Q}, {pool} pool, "
+             f"align {align}")
     one, two = state0.clone(), state0.clone()
     call(one, 0, B)
     call(two, 0, B // 2)
     call(two, B // 2, B)
     torch.cuda.synchronize()
     assert not torch.equal(one, state0)
-    assert np.array_equal(_bits(one), _bits(two))
+    if align:
+        assert not torch.equal(one[(B + 5) * page:], state0[(B + 5) * page:])
+    if bf16:
+        assert np.array_equal(_bits(one), _bits(two))
+        return
+    g_one, g_two = one.cpu().numpy(), two.cpu().numpy()
+    assert_f32_close("streaming vs plain FP32 commit", g_one, g_two)
+    # Sampled requests of the streaming launch against the oracle on a compact
+    # pool: slot 1+3j source, 2+3j destination (a copy of the source: the
+    # commit runs in place), 3+3j boundary.
+    live = [b for b in range(B) if src[b] > 0 and lens[b] > 0]
+    R = np.random.default_rng(61 + Q).choice(live, 10, replace=False)
+    nR = len(R)
+    m_src = (1 + 3 * np.arange(nR)).astype(np.int32)
+    m_bnd = np.where((blens[R] > 0) & (bounds[R] > 0), m_src + 2, 0).astype(np.int32) \
+        if align else None
+    s0 = state0.cpu().numpy()
+    mini = np.zeros((1 + 3 * nR) * page, np.float32)
+    for j, b in enumerate(R):
+        sl = int(src[b])
+        mini[m_src[j] * page:(m_src[j] + 1) * page] = s0[sl * page:(sl + 1) * page]
+    r_of = rows.numpy()[R]
+    announce(f"commit FP32 streaming launch: oracle on {nR} sampled requests x {H} heads")
+    oracle.commit(heads=H, window=Q, batch=nR, state_bf16=False, state_layers=[mini],
+                  state_slot_strides=[page], corr_layers=[corr.numpy()[r_of]],
+                  corr_row_strides=[H * Q * V], kg_layers=[W.bits(kg)[r_of]],
+                  kg_row_strides=[H * Q * 2 * K], a_log=a_log.numpy(), dt_bias=dtb.numpy(),
+                  sources=m_src, commit_lens=lens.numpy()[R], destinations=m_src,
+                  boundaries=m_bnd, boundary_lens=None if blens is None else blens.numpy()[R],
+                  lower_bound=W.LOWER_BOUND)
+    for j, b in enumerate(R):
+        sl = int(src[b])
+        assert_f32_close(f"streaming commit request {b}", g_one[sl * page:(sl + 1) * page],
+                         mini[m_src[j] * page:(m_src[j] + 1) * page])
+        if align and m_bnd[j] > 0:
+            bs = int(bounds[b])
+            assert_f32_close(f"streaming commit request {b} boundary",
+                             g_one[bs * page:(bs + 1) * page],
+                             mini[m_bnd[j] * page:(m_bnd[j] + 1) * page])
 
 
 @pytest.mark.parametrize("layout", ["dim_first", "window_major"])

@@ -10,7 +10,11 @@
 // - commit_kernel (BF16 pages, and FP32 pools that fit in the MALL): the page
 //   goes HBM -> VGPRs -> HBM; each thread issues all of its 16-byte loads
 //   before the coefficients are built and owns a fixed 16-byte column group
-//   of every pass' rows, folded on the vector ALU.
+//   of every pass' rows, folded on the vector ALU. The LDS path below, run on
+//   BF16 pages (32 KiB area, the same tiles in the fused kernel's BF16
+//   channel order), lost: 8-layer align commit 1.13 against 0.974 ms, the
+//   1 GiB pool's flush 0.398 against 0.355 ms; a BF16 page carries half the
+//   bytes, so the path's per-item latency weighs twice as much.
 // - commit_f32_stream_kernel (FP32 pages of launches larger than the MALL):
 //   the page goes HBM -> LDS -> VGPRs -> HBM. Each wave loads its 32 rows
 //   straight into LDS as contiguous 1 KiB pieces, reads them back as 16x16

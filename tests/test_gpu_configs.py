@@ -235,24 +235,40 @@ def test_large_decode_gate_projection_general_factors():
     assert not bf16_mismatch(got, oracle.round_bf16(prod)).any()
 
 
-def test_config3_align_commit_full_size_sampled():
+@pytest.mark.parametrize("pool", ["bf16", "f32"])
+def test_config3_align_commit_full_size_sampled(pool):
+    """The prefix-cache align commit at full size: 8 layers of BF16 pools (the
+    workload), and the same plan over 3 layers of FP32 pools, 1.5 GiB of source
+    pages per launch (the streaming FP32 kernel: pages through LDS, folded on
+    the matrix cores). Whole-pool property: every slot nobody writes is
+    bit-identical; 12 sampled requests (6 with a boundary store) of every
+    layer and head against the oracle."""
     import spec_decode_amd as kda
 
-    w = W.config3(device=DEV)
+    bf16 = pool == "bf16"
+    w = W.config3(device=DEV, layers=8 if bf16 else 3)
     a = w.arrays
     L, H, B, Q = w.layers, w.heads, w.batch, w.tokens
     strides = w.slot_strides
     page = H * V * K
     src, dst = a["sources"].numpy(), a["destinations"].numpy()
     bnd, blen, lens = a["boundaries"].numpy(), a["boundary_lens"].numpy(), a["commit_lens"].numpy()
-    pools = [a[f"state{l}"] for l in range(L)]
+    if bf16:
+        pools = [a[f"state{l}"] for l in range(L)]
+    else:
+        pools = [W.draw_state(3000 + 17 + l, w.slots * strides[l], torch.float32, DEV)
+                 for l in range(L)]
+        for l in range(L):
+            del a[f"state{l}"]
+        torch.cuda.empty_cache()
     before = [p.clone() for p in pools]
     corrs = [a[f"corr{l}"].numpy().copy() for l in range(L)]
     kgs = [W.bits(a[f"kg{l}"]) for l in range(L)]
     d_corr = [dev(c) for c in corrs]
     d_kg = [dev_bf16(k) for k in kgs]
-    announce(f"config3: full-size align commit L={L} H={H} B={B} Q={Q}")
-    kda.kda_commit(heads=H, window=Q, batch=B, state_dtype=kda.KDA_STATE_BF16,
+    announce(f"config3: full-size align commit L={L} H={H} B={B} Q={Q}, {pool} pools")
+    kda.kda_commit(heads=H, window=Q, batch=B,
+                   state_dtype=kda.KDA_STATE_BF16 if bf16 else kda.KDA_STATE_F32,
                    state_addrs=[p.data_ptr() for p in pools], state_slot_strides=strides,
                    corr_addrs=[c.data_ptr() for c in d_corr], corr_row_strides=[H * Q * V] * L,
                    kg_addrs=[k.data_ptr() for k in d_kg], kg_row_strides=[H * Q * 2 * K] * L,
@@ -260,6 +276,9 @@ def test_config3_align_commit_full_size_sampled():
                    sources=dev(src), commit_lens=dev(lens), destinations=dev(dst),
                    boundaries=dev(bnd), boundary_lens=dev(blen), lower_bound=w.lower_bound)
     torch.cuda.synchronize()
+
+    def bits(t):
+        return t.view(torch.int16) if bf16 else t.view(torch.int32)
 
     # Property over the whole pools: every slot nobody writes is bit-identical.
     for l in range(L):
@@ -271,12 +290,11 @@ def test_config3_align_commit_full_size_sampled():
         view_now = pools[l].view(w.slots, strides[l])
         view_then = before[l].view(w.slots, strides[l])
         idx = torch.tensor(keep, device=DEV)
-        assert torch.equal(view_now.index_select(0, idx).view(torch.int16),
-                           view_then.index_select(0, idx).view(torch.int16)), f"layer {l}"
+        assert torch.equal(bits(view_now.index_select(0, idx)),
+                           bits(view_then.index_select(0, idx))), f"layer {l}"
         # the padding between pages of odd layers is never written either
         if strides[l] > page:
-            assert torch.equal(view_now[:, page:].view(torch.int16),
-                               view_then[:, page:].view(torch.int16))
+            assert torch.equal(bits(view_now[:, page:]), bits(view_then[:, page:]))
 
     # Sampled requests: 6 with a boundary store and 6 without, all layers and heads.
     rng = np.random.default_rng(33)
@@ -288,13 +306,15 @@ def test_config3_align_commit_full_size_sampled():
     m_src = (1 + 3 * np.arange(nR)).astype(np.int32)
     m_dst = m_src + 1
     m_bnd = np.where(blen[R] > 0, m_src + 2, 0).astype(np.int32)
+    host = W.bits if bf16 else (lambda t: t.cpu().numpy())
+    close = assert_bf16_close if bf16 else assert_f32_close
     announce(f"config3: oracle on {nR} sampled requests x {L} layers x {H} heads")
     for l in range(L):
         pool_then = before[l].view(w.slots, strides[l])[:, :page]
-        mini = np.zeros((1 + 3 * nR) * page, np.uint16)
+        mini = np.zeros((1 + 3 * nR) * page, np.uint16 if bf16 else np.float32)
         for j, b in enumerate(R):
-            mini[m_src[j] * page:(m_src[j] + 1) * page] = W.bits(pool_then[int(src[b])])
-        oracle.commit(heads=H, window=Q, batch=nR, state_bf16=True, state_layers=[mini],
+            mini[m_src[j] * page:(m_src[j] + 1) * page] = host(pool_then[int(src[b])])
+        oracle.commit(heads=H, window=Q, batch=nR, state_bf16=bf16, state_layers=[mini],
                       state_slot_strides=[m_stride], corr_layers=[corrs[l][R]],
                       corr_row_strides=[H * Q * V], kg_layers=[kgs[l][R]],
                       kg_row_strides=[H * Q * 2 * K], a_log=a["a_log"][l:l + 1].numpy(),
@@ -303,13 +323,11 @@ def test_config3_align_commit_full_size_sampled():
                       boundary_lens=blen[R], lower_bound=w.lower_bound)
         pool_now = pools[l].view(w.slots, strides[l])[:, :page]
         for j, b in enumerate(R):
-            assert_bf16_close(f"config3 layer {l} request {b} destination",
-                              W.bits(pool_now[int(dst[b])]),
-                              mini[m_dst[j] * page:(m_dst[j] + 1) * page])
+            close(f"config3 layer {l} request {b} destination", host(pool_now[int(dst[b])]),
+                  mini[m_dst[j] * page:(m_dst[j] + 1) * page])
             if blen[b] > 0:
-                assert_bf16_close(f"config3 layer {l} request {b} boundary",
-                                  W.bits(pool_now[int(bnd[b])]),
-                                  mini[m_bnd[j] * page:(m_bnd[j] + 1) * page])
+                close(f"config3 layer {l} request {b} boundary", host(pool_now[int(bnd[b])]),
+                      mini[m_bnd[j] * page:(m_bnd[j] + 1) * page])
     del pools, before
     torch.cuda.empty_cache()
 

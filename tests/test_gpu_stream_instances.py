@@ -91,9 +91,10 @@ def test_fused_streaming_instance_matches_plain(gated, T, pool):
 
 
 @pytest.mark.parametrize("pool,Q,align", [("f32", 8, False), ("bf16", 8, False),
-                                          ("f32", 3, False), ("f32", 8, True), ("f32", 5, True)])
+                                          ("f32", 3, False), ("f32", 8, True), ("f32", 5, True),
+                                          ("f32", 1, False), ("f32", 4, True), ("f32", 7, True)])
 def test_commit_streaming_instance_matches_plain(pool, Q, align):
-    """Windows of 3, 5 and 8 tokens, with and without boundary stores (the
+    """Windows of 1, 3, 4, 5, 7 and 8 tokens, with and without boundary stores (the
     boundary pages beyond every source page, two of them null). BF16 pools:
     the same bits. FP32 pools: the two within the FP32 tolerance, and 10
     sampled requests of the streaming launch against the oracle."""

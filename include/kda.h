@@ -43,9 +43,13 @@
  *    (kda_commit: batch x heads x layers pages; kda_fused_replay_verify and
  *    kda_fused_conv_replay_verify on FP32 pools: batch x heads pages) write
  *    their pages with write-through, no-reuse stores, at two workgroups per
- *    CU (extra dynamic LDS, sized on the first such launch of each kernel
- *    from its static LDS; this is the library's only retained host data).
- *    The results are bit-identical to those of smaller launches.
+ *    CU (where a kernel's own LDS would allow more, extra dynamic LDS, sized
+ *    on the first such launch of each kernel from its static LDS; this is the
+ *    library's only retained host data). The results are bit-identical to
+ *    those of smaller launches, except for kda_commit on FP32 pools: its
+ *    streaming launches fold on the matrix cores (the products of up to four
+ *    tokens summed in one instruction) where smaller ones add one token at a
+ *    time, so the two can differ by FP32 rounding of the fold.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -17,7 +17,10 @@ All inputs are synthetic (seeded generators in ``workloads``) and resident in
 HBM before timing; the records the first step replays come from a verify of a
 prior window. W untimed warm-up steps, then K timed steps between device
 synchronisations. Kernel durations come from HIP events recorded on the stream
-the kernels are launched on.
+the kernels are launched on: around the fused launch on the even timed steps
+and around the commit on the odd ones (both on every step when K = 1). Each
+pair of events costs the step the overlap of one kernel's drain with the next
+one's start, about 4 us, so the step carries one pair, not one per kernel.
 
 Printed: one JSON line. ``value`` is the step's state bandwidth: algorithmic
 state bytes (pages read + pages written, from the actual plan) per second.
@@ -796,15 +799,29 @@ def main():
     total = args.warmup + args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
 
+    # Timed step j brackets the fused launch (and the gate projection) with
+    # events when j is even, the commit when j is odd; both when only one step
+    # is timed. Warm-up steps record none.
+    def times_fused(i):
+        j = i - args.warmup
+        return j >= 0 and (j % 2 == 0 or args.steps == 1)
+
+    def times_commit(i):
+        j = i - args.warmup
+        return j >= 0 and (j % 2 == 1 or args.steps == 1)
+
     def step(i):
         e = ev[i]
+        tf, tc = times_fused(i), times_commit(i)
         commit_lens.copy_(accepted)
-        e[4].record()
         if gp is not None:
+            if tf:
+                e[4].record()
             kda.kda_gate_projection(tokens=B * T, heads=H, f_a=gp["f_a"],
                                     f_a_row_stride=gp["pitch"], f_b=gp["f_b"],
                                     raw_g=gp["raw_g"])
-        e[0].record()
+        if tf:
+            e[0].record()
         if conv is None:
             kda.kda_fused_replay_verify(heads=H, tokens=T, batch=B, q=new.q, k=new.k, v=new.v,
                                         raw_g=raw_g, raw_beta=new.raw_beta, a_log=a_log,
@@ -823,15 +840,18 @@ def main():
                 dt_bias=dt_bias, lower_bound=lb, state=state, state_slot_stride=state_stride,
                 state_indices=slots, corr=corr, kg=kg, record_tokens=RQ, record_rows=rows,
                 pending=pending, out=out, gate=gate, norm_weight=norm_w, norm_eps=norm_eps)
-        e[1].record()
+        if tf:
+            e[1].record()
         kda.kda_defer_commit(batch=B, state_indices=slots, commit_lens=commit_lens,
                              record_rows=rows, pending=pending)
         kda.kda_flush_plan(batch=B, spec_query_len=T, state_indices=slots, record_rows=rows,
                            pending=pending, commit_lens=flush[0], final_indices=flush[1],
                            boundaries=flush[2], boundary_lens=flush[3])
-        e[2].record()
+        if tc:
+            e[2].record()
         kda.kda_commit(**commit_args)
-        e[3].record()
+        if tc:
+            e[3].record()
 
     for i in range(args.warmup):
         step(i)
@@ -844,11 +864,11 @@ def main():
     if not bool(torch.isfinite(state[: 64 * page]).all()):
         sys.exit("non-finite state after the run")
 
-    timed = ev[args.warmup:]
-    fused_ms = [e[0].elapsed_time(e[1]) for e in timed]
-    commit_ms = [e[2].elapsed_time(e[3]) for e in timed]
-    step_ms = [e[4].elapsed_time(e[3]) for e in timed]
-    gp_ms = [e[4].elapsed_time(e[0]) for e in timed]
+    f_idx = [i for i in range(args.warmup, total) if times_fused(i)]
+    c_idx = [i for i in range(args.warmup, total) if times_commit(i)]
+    fused_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in f_idx]
+    commit_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in c_idx]
+    gp_ms = [ev[i][4].elapsed_time(ev[i][0]) for i in f_idx] if gp is not None else []
 
     # Algorithmic bytes from the plan of each step.
     sl_h, rr_h = slots.cpu().numpy(), rows.cpu().numpy()
@@ -863,10 +883,13 @@ def main():
     items = B * H
     fused_mean_ms = sum(fused_ms) / len(fused_ms)
     commit_mean_ms = sum(commit_ms) / len(commit_ms)
-    fused_total = sum(f[1] for f in fb) / len(fb)
-    fused_state = sum(f[0] for f in fb) / len(fb)
-    commit_total = sum(c[1] for c in cb) / len(cb)
-    commit_state = sum(c[0] for c in cb) / len(cb)
+    # Per-launch bytes of the steps whose launches the events timed.
+    fb_t = [fb[i - args.warmup] for i in f_idx]
+    cb_t = [cb[i - args.warmup] for i in c_idx]
+    fused_total = sum(f[1] for f in fb_t) / len(fb_t)
+    fused_state = sum(f[0] for f in fb_t) / len(fb_t)
+    commit_total = sum(c[1] for c in cb_t) / len(cb_t)
+    commit_state = sum(c[0] for c in cb_t) / len(cb_t)
     achieved = fused_total / (fused_mean_ms * 1e-3) / 1e9
     tkey, tsrc = fused_variant(args)
     traffic = measured_traffic(tkey, source_digest(tsrc))
@@ -914,7 +937,6 @@ def main():
                 "state_gbs": round(commit_state / (commit_mean_ms * 1e-3) / 1e9, 1),
                 "total_gbs": round(commit_total / (commit_mean_ms * 1e-3) / 1e9, 1),
                 "items_per_s": round(items / (commit_mean_ms * 1e-3), 1)},
-            "step_event_ms": round(sum(step_ms) / len(step_ms), 4),
             **({"gate_projection": {
                 "mean_ms": round(sum(gp_ms) / len(gp_ms), 4),
                 "total_gbs": round((B * T * (256 + H * K * 2) + H * K * 256)

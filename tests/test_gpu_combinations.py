@@ -216,3 +216,65 @@ def test_random_commit_combination(seed):
                     blen=blen if align else None, rows=rows, lb=_lower_bound(10800 + seed),
                     label=f"commit combination {seed}: L={L} H={H} B={B} Q={Q} bf16={bf16} "
                           f"inplace={inplace} align={align} lb={_lower_bound(10800 + seed)}")
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_random_commit_combination_streaming(seed):
+    """The same draws at a size whose FP32 source pages exceed the 256 MB MALL
+    (H=64, B=66: 264 MiB per layer), so kda_commit runs its streaming FP32
+    kernel (pages through LDS, folded on the matrix cores), against the full
+    oracle: one or two layers, any window, in place or not, boundaries, record
+    rows, padded record rows holding NaN, lengths 0, negative and above the
+    window."""
+    from _kda_cases import pad_record_rows, run_commit_case
+    r = np.random.default_rng(13000 + seed)
+    L = int(r.choice([1, 2]))
+    H, B = 64, 66
+    Q = int(r.integers(1, 9))
+    inplace = bool(r.integers(2))
+    align = bool(r.integers(2))
+    S = 3 * B + 2
+    page = H * V * K
+    assert B * page * 4 > 256 << 20
+    g = W._gen(13100 + seed)
+    strides = [page + 8 * int(r.integers(0, 20)) for _ in range(L)]
+    states, corrs, kgs = [], [], []
+    for l in range(L):
+        states.append(W.draw_state(13200 + seed * 4 + l, S * strides[l], torch.float32).numpy())
+        c, k = W.draw_records(g, B, H, Q)
+        corrs.append(c.numpy().copy())
+        kgs.append(W.bits(k))
+    a_log, dtb = W.draw_gate_params(g, L, H)
+    perm = r.permutation(np.arange(1, S)).astype(np.int32)
+    src = perm[:B].copy()
+    dst = src.copy() if inplace else perm[B:2 * B].copy()
+    bnd = perm[2 * B:3 * B].copy()
+    for b in range(B):
+        if r.random() < 0.15:
+            src[b] = 0
+        if r.random() < 0.25:
+            bnd[b] = 0
+    lens = r.integers(-1, Q + 3, B).astype(np.int32)
+    blen = r.integers(-1, Q + 3, B).astype(np.int32)
+    rows = None
+    if r.integers(2):
+        rows = r.permutation(B).astype(np.int32)
+        for b in range(B):
+            if r.random() < 0.15:
+                rows[b] = -1
+    corr_strides = kg_strides = None
+    if r.integers(2):
+        padded = [pad_record_rows(corrs[l], 4 * int(r.integers(1, 9)), np.float32(np.nan))
+                  for l in range(L)]
+        corrs, corr_strides = [x[0] for x in padded], [x[1] for x in padded]
+        padded = [pad_record_rows(kgs[l], 8 * int(r.integers(1, 9)), np.uint16(0x7FC0))
+                  for l in range(L)]
+        kgs, kg_strides = [x[0] for x in padded], [x[1] for x in padded]
+    lb = _lower_bound(13300 + seed)
+    run_commit_case(H=H, B=B, Q=Q, bf16=False, layers_state=states, strides=strides,
+                    corr_layers=corrs, kg_layers=kgs, a_log=a_log.numpy(), dt_bias=dtb.numpy(),
+                    corr_strides=corr_strides, kg_strides=kg_strides,
+                    src=src, lens=lens, dst=dst, bnd=bnd if align else None,
+                    blen=blen if align else None, rows=rows, lb=lb,
+                    label=f"streaming commit combination {seed}: L={L} Q={Q} inplace={inplace} "
+                          f"align={align} lb={lb}")

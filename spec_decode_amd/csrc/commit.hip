@@ -16,9 +16,10 @@
 //   1 GiB pool's flush 0.398 against 0.355 ms; a BF16 page carries half the
 //   bytes, so the path's per-item latency weighs twice as much.
 // - commit_f32_stream_kernel (FP32 pages of launches larger than the MALL):
-//   the page goes HBM -> LDS -> VGPRs -> HBM. Each wave loads its 32 rows
-//   straight into LDS as contiguous 1 KiB pieces, reads them back as 16x16
-//   tiles in the accumulator layout of V_MFMA_F32_16X16X4_F32, folds each tile
+//   each wave loads its 32 rows as contiguous 1 KiB pieces, the first half
+//   straight into its LDS area and the second half into registers, turns
+//   both into 16x16 tiles in the accumulator layout of V_MFMA_F32_16X16X4_F32
+//   through that area (as the stock verify loads its page), folds each tile
 //   on the matrix cores (S^T <- diag(D) S^T + KP U^T, K = the replayed tokens)
 //   and stores the tiles 16 rows per instruction, the access order that moves
 //   the most on an in-place pass over a pool larger than the MALL.
@@ -109,38 +110,6 @@ __device__ __forceinline__ void commit_suffix_products(const float (&kn)[Q], con
 
 // ------------------------------------------------------------ FP32 pages
 
-// Wave w's 32 rows of an FP32 page straight into its 16 KiB LDS area (buffer
-// loads to LDS): piece j, lane l fetches row rho = 2j + l/32, chunk
-// g = (l % 32) ^ (rho % 16), so each piece is 1 KiB of contiguous page and
-// chunk g of row rho lands at slot g ^ (rho % 16) of that row.
-template <int CPOL>
-__device__ __forceinline__ void load_page_lds(const float* page, int wave, int lane,
-                                              u32x4* area) {
-  const __amdgpu_buffer_rsrc_t rs = page_rsrc(const_cast<float*>(page), PAGE * 4);
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int rho = 2 * j + (lane >> 5);
-    const int g = (lane & 31) ^ (rho & 15);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(area + 64 * j), 16,
-                                             ((32 * wave + rho) * K) * 4 + g * 16, 0, 0, CPOL);
-  }
-}
-
-// The wave's tiles from its area once its loads have landed. Lane l of tile
-// (r, cb) holds row 32w + 16r + l%16, channels 16cb + 4(l/16) .. +3: chunk
-// 4cb + l/16 of the row. Within a group of 16 lanes the rows differ and so do
-// their slots, so no two of them meet on one bank group.
-__device__ __forceinline__ void read_tiles(const u32x4* area, int lane, u32x4 (&st)[2][8]) {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (gfx9 encoding; expcnt, lgkmcnt not waited)
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int rl = lane & 15;
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-      st[r][cb] = area[(16 * r + rl) * 32 + ((4 * cb + (lane >> 4)) ^ rl)];
-}
-
 // One stage of the fold over tokens t0 <= t < t1 on the tiles:
 // S^T <- diag(D) S^T + KP U^T. In V_MFMA_F32_16X16X4_F32 terms the tile is the
 // accumulator (M = key channel, N = state row), A = kp_t[c] (lane l: channel
@@ -187,17 +156,19 @@ __device__ __forceinline__ void store_tiles(const u32x4 (&st)[2][8], float* page
       store_page16<CPOL>(st[r][cb], rs, off0 + (16 * r * K + 16 * cb) * 4);
 }
 
-// FP32 pages of launches larger than the MALL. The 64 KiB page area holds
-// the kernel at two workgroups per CU, the occupancy its write-through stores
-// want. The key norms are formed within each of waves 0 and 1 (each lane also
-// loads the channel of the other wave), so the kernel's one barrier is the
-// one before the fold, which waits for the page, needed next anyway. On the
-// large decode flush (2 GiB pool, in place) it took 0.630-0.635 ms against
-// 0.650-0.652 ms for commit_kernel, and 0.644 ms with the same tiles folded
-// on the vector ALU. For pools that fit in the MALL commit_kernel is the
-// faster one (24.6 against 28.8 us on 68 MiB, 64 against 69 us on 196 MiB):
-// at its four workgroups per CU latency hides better, and the LDS area or
-// tile-order register loads (28.0 and 69 us) cost more than they save there.
+// FP32 pages of launches larger than the MALL, at two workgroups per CU (the
+// occupancy its write-through stores want; its 41 KiB of LDS would allow
+// three, which was slower). The key norms are formed within each of waves 0
+// and 1 (each lane also loads the channel of the other wave), so the kernel's
+// one barrier is the one before the fold, which waits for the page, needed
+// next anyway. On the large decode flush (2 GiB pool, in place) it takes
+// 0.622-0.624 ms, against 0.629-0.633 ms with the whole page straight into a
+// 64 KiB LDS area, 0.644 ms with the tiles folded on the vector ALU, and
+// 0.650-0.652 ms for commit_kernel. For pools that fit in the MALL
+// commit_kernel is the faster one (24.6 against 28.8 us on 68 MiB, 64 against
+// 69 us on 196 MiB, measured with the 64 KiB area): at its four workgroups per
+// CU latency hides better, and the LDS area or tile-order register loads
+// (28.0 and 69 us) cost more than they save there.
 template <int Q, bool ALIGN>
 __global__ __launch_bounds__(256) void commit_f32_stream_kernel(const CommitParams p) {
   CommitItem it;
@@ -207,7 +178,7 @@ __global__ __launch_bounds__(256) void commit_f32_stream_kernel(const CommitPara
   const CommitLayer L = p.layer[l];
   const int H = p.heads;
 
-  __shared__ __attribute__((aligned(16))) u32x4 pg_s[4][32 * 32];
+  __shared__ __attribute__((aligned(16))) u32x4 xt_s[4][16 * 32];  // per-wave transpose areas
   __shared__ float u_s[Q][V];
   __shared__ __attribute__((aligned(16))) float kp_s[Q][K];
   __shared__ __attribute__((aligned(16))) float dn_s[K];
@@ -243,7 +214,8 @@ __global__ __launch_bounds__(256) void commit_f32_stream_kernel(const CommitPara
   __builtin_amdgcn_sched_barrier(0);
   const float* srcp = reinterpret_cast<const float*>(L.state) + (int64_t)it.src * L.state_stride +
                       (int64_t)it.h * PAGE;
-  load_page_lds<CPOL_NT>(srcp, wave, lane, &pg_s[wave][0]);
+  u32x4 cont[8];
+  load_page_halves(srcp, wave, lane, &xt_s[wave][0], cont);
   __builtin_amdgcn_sched_barrier(0);
 
   if (lower) {
@@ -270,7 +242,7 @@ __global__ __launch_bounds__(256) void commit_f32_stream_kernel(const CommitPara
   __syncthreads();
 
   u32x4 st[2][8];
-  read_tiles(&pg_s[wave][0], lane, st);
+  transpose_page_halves(cont, &xt_s[wave][0], lane, st);
   float ub[2][2];
   {
     const int lq = lane >> 4;
@@ -496,7 +468,8 @@ static hipError_t launch_q(const CommitParams& p, int window, dim3 grid, hipStre
 #define KDA_COMMIT_CASE(QQ)                                                                   \
   case QQ: {                                                                                 \
     if constexpr (STREAM && !BF16) {                                                         \
-      hipLaunchKernelGGL((commit_f32_stream_kernel<QQ, ALIGN>), grid, dim3(256), 0, stream,  \
+      static const size_t pad = two_per_cu_lds(&commit_f32_stream_kernel<QQ, ALIGN>);       \
+      hipLaunchKernelGGL((commit_f32_stream_kernel<QQ, ALIGN>), grid, dim3(256), pad, stream, \
                          p);                                                                 \
     } else {                                                                                 \
       static const size_t pad =                                                              \

@@ -1,7 +1,7 @@
 """The step's variants at the large decode batch's size (H=64, B=512, q=8, a
 2 GiB FP32 pool), in the launch configuration the benchmark times: the gated
-RMSNorm output stage, and the convolution prologue over a packed dim-first
-and over a window-major window pool. Sampled requests (null slots, a missing record row, every pending
+RMSNorm output stage, the convolution prologue over a packed dim-first and
+over a window-major window pool, and the stock verify. Sampled requests (null slots, a missing record row, every pending
 count) are recomputed by the oracle on compact copies; pages nobody writes are
 compared bit for bit over the whole pool."""
 import numpy as np
@@ -131,6 +131,49 @@ def test_large_decode_gated_output_sampled():
                                norm_weight=weight.numpy(), norm_eps=eps, o_raw=o_raw)
     _check("gated", R, m, m_out, np_of(out), lambda sl: np_of(d_state[sl * page:(sl + 1) * page]),
            np_of(d_corr), np_of(d_kg), slots, rows, o_raw)
+    del d_state, before
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_large_decode_stock_verify_sampled(bf16):
+    """kda_verify at the large decode batch's size, as the benchmark's
+    --workload verify launches it (the streaming instance: half of each page
+    straight into LDS on FP32 pools): o and the records of sampled requests
+    against the oracle, and the pool never written."""
+    import spec_decode_amd as kda
+    g, slots, rows, pending_row, a_log, dtb, corr, kg = _plan(950)
+    page = H * V * K
+    win = window_np(W.draw_window(g, B, T, H))
+    d_state = W.draw_state(952, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
+    before = d_state.clone()
+    d_corr, d_kg = dev(corr), dev_bf16(kg)
+    out = torch.zeros((B * T, H * V), dtype=torch.bfloat16, device=DEV)
+    announce(f"large decode, stock verify, {'BF16' if bf16 else 'FP32'} pool")
+    kda.kda_verify(heads=H, tokens=T, batch=B, q=dev_bf16(win["q"]), k=dev_bf16(win["k"]),
+                   v=dev_bf16(win["v"]), raw_g=dev_bf16(win["raw_g"]),
+                   raw_beta=dev_bf16(win["raw_beta"]), a_log=dev(a_log), dt_bias=dev(dtb),
+                   lower_bound=W.LOWER_BOUND, state=d_state, state_slot_stride=page,
+                   state_indices=dev(slots), corr=d_corr, kg=d_kg, record_tokens=RQ,
+                   record_rows=dev(rows), out=out)
+    torch.cuda.synchronize()
+    bits = torch.int16 if bf16 else torch.int32
+    assert torch.equal(d_state.view(bits), before.view(bits)), "the stock verify wrote the pool"
+    R = _sample(953, slots, rows, pending_row)
+    m = _compact(R, slots, rows, pending_row, corr, kg,
+                 lambda sl: np_of(before[sl * page:(sl + 1) * page]),
+                 np.uint16 if bf16 else np.float32)
+    m_win = {k: np.ascontiguousarray(v[m["tok"]]) for k, v in win.items()}
+    m_out = np.zeros((len(R) * T, H * V), np.uint16)
+    announce(f"large decode stock verify: oracle on {len(R)} sampled requests")
+    oracle.verify(heads=H, tokens=T, batch=len(R), q=m_win["q"], k=m_win["k"], v=m_win["v"],
+                  raw_g=m_win["raw_g"], raw_beta=m_win["raw_beta"], a_log=a_log, dt_bias=dtb,
+                  lower_bound=W.LOWER_BOUND, state=m["state"], state_slot_stride=page,
+                  state_indices=m["slots"], corr=m["corr"], kg=m["kg"], record_tokens=RQ,
+                  record_rows=m["rows"], out=m_out)
+    _check("stock verify", R, m, m_out, np_of(out),
+           lambda sl: np_of(d_state[sl * page:(sl + 1) * page]), np_of(d_corr), np_of(d_kg),
+           slots, rows, bf16=bf16)
     del d_state, before
     torch.cuda.empty_cache()
 

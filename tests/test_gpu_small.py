@@ -86,6 +86,27 @@ def test_decay(lb):
         assert np.all(np_of(out) == 1.0)
 
 
+@pytest.mark.parametrize("N", [4096, 4099])
+def test_decay_full_size(N):
+    """The large decode batch's raw gates (4096 tokens x 64 heads x 128, as the
+    benchmark's decay workload), and 3 tokens more: more 8-byte chunks than the
+    capped grid has threads, so every thread takes a second chunk, the last
+    pass ragged. Every element against the oracle."""
+    import spec_decode_amd as kda
+
+    g = W._gen(6)
+    H = 64
+    assert N * H * K // 4 > 256 * 64 * 256
+    raw = W.bf16(W.normal(g, (N, H, K)) * 3.0)
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    announce(f"decay N={N} H={H} (grid-stride)")
+    out = torch.full((N, H, K), float("nan"), dtype=torch.float32, device=DEV)
+    kda.kda_decay(raw.to(DEV), a_log[0].to(DEV), dtb[0].to(DEV), W.LOWER_BOUND, out)
+    torch.cuda.synchronize()
+    ref = oracle.decay_buf(W.bits(raw), a_log[0].numpy(), dtb[0].numpy(), W.LOWER_BOUND)
+    assert_f32_close("decay full size", np_of(out), ref)
+
+
 # ---------------------------------------------------------------- commit
 
 def _commit_inputs(seed, L, H, B, Q, bf16, slots, pad=(0,)):

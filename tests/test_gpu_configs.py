@@ -554,6 +554,94 @@ def test_maximum_batch_grid_fused_sampled():
 
 
 @pytest.mark.parametrize("pool", ["bf16", "f32"])
+def test_maximum_batch_grid_commit_sampled(pool):
+    """kda_commit at 65535 requests (the largest grid the kernels take), one
+    head, in place, with boundary pages of their own (two pools of 65536
+    slots: 8 GiB FP32, 4 GiB BF16, so both take their streaming kernels);
+    null sources, missing record
+    rows, lengths 0..window+1 and boundary lengths drawn; 24 sampled requests
+    against the oracle, and every page the call must not write compared bit
+    for bit."""
+    import spec_decode_amd as kda
+    bf16 = pool == "bf16"
+    H, B, Q = 1, 65535, 4
+    S = 2 * 65536
+    page = H * V * K
+    g = W._gen(910 + bf16)
+    src = (W.permutation(g, 65535) + 1).numpy().astype(np.int32)
+    src[::997] = 0
+    bnd = (65536 + W.permutation(g, 65536)[:B]).numpy().astype(np.int32)
+    bnd[3::5] = 0
+    rows = W.permutation(g, B).numpy().astype(np.int32)
+    rows[5::1009] = -1
+    lens = W.uniform_int(g, 0, Q + 1, B).numpy()
+    blen = W.uniform_int(g, 0, Q + 1, B).numpy()
+    a_log, dtb = W.draw_gate_params(g, 1, H)
+    corr, kg = W.draw_records(g, B, H, Q)
+    corr, kg = corr.numpy(), W.bits(kg)
+    d_state = W.draw_state(911 + bf16, S * page, torch.bfloat16 if bf16 else torch.float32, DEV)
+    before = d_state.clone()
+    d_corr, d_kg = dev(corr), dev_bf16(kg)
+    announce(f"max batch: commit H=1 B=65535 window {Q}, {pool} pool with boundaries")
+    kda.kda_commit(heads=H, window=Q, batch=B,
+                   state_dtype=kda.KDA_STATE_BF16 if bf16 else kda.KDA_STATE_F32,
+                   state_addrs=[d_state.data_ptr()], state_slot_strides=[page],
+                   corr_addrs=[d_corr.data_ptr()], corr_row_strides=[H * Q * V],
+                   kg_addrs=[d_kg.data_ptr()], kg_row_strides=[H * Q * 2 * K],
+                   a_log=a_log.to(DEV), dt_bias=dtb.to(DEV), sources=dev(src),
+                   commit_lens=dev(lens), destinations=dev(src), boundaries=dev(bnd),
+                   boundary_lens=dev(blen), record_rows=dev(rows), lower_bound=W.LOWER_BOUND)
+    torch.cuda.synchronize()
+    live = (lens > 0) & (src > 0) & (rows >= 0)
+    touched = torch.zeros(S, dtype=torch.bool)
+    touched[torch.from_numpy(src[live]).long()] = True
+    bl = live & (blen > 0) & (bnd > 0)
+    touched[torch.from_numpy(bnd[bl]).long()] = True
+    keep = (~touched).nonzero().flatten().to(DEV)
+    bits = torch.int16 if bf16 else torch.int32
+    for part in torch.split(keep, 16384):
+        assert torch.equal(d_state.view(S, page).index_select(0, part).view(bits),
+                           before.view(S, page).index_select(0, part).view(bits))
+    rng = np.random.default_rng(912)
+    cand = np.flatnonzero(live)
+    R = [int(x) for x in np.concatenate([np.flatnonzero(bl)[:6], [B - 1, 0, 5, 997],
+                                         rng.choice(cand, 14, replace=False)])]
+    R = list(dict.fromkeys(R))
+    nR = len(R)
+    host = (lambda t: W.bits(t)) if bf16 else (lambda t: t.cpu().numpy())
+    m_src = (1 + 2 * np.arange(nR)).astype(np.int32)  # slot 1+2j the page, 2+2j its boundary
+    m_bnd = np.where(bl[R], m_src + 1, 0).astype(np.int32)
+    mini = np.zeros((1 + 2 * nR) * page, np.uint16 if bf16 else np.float32)
+    for j, b in enumerate(R):
+        if src[b] > 0:
+            mini[m_src[j] * page:(m_src[j] + 1) * page] = host(before[int(src[b]) * page:
+                                                                  (int(src[b]) + 1) * page])
+    r_of = np.where(rows[R] >= 0, rows[R], 0)
+    announce(f"max batch commit: oracle on {nR} sampled requests")
+    oracle.commit(heads=H, window=Q, batch=nR, state_bf16=bf16, state_layers=[mini],
+                  state_slot_strides=[page], corr_layers=[corr[r_of]],
+                  corr_row_strides=[H * Q * V], kg_layers=[kg[r_of]],
+                  kg_row_strides=[H * Q * 2 * K], a_log=a_log.numpy(), dt_bias=dtb.numpy(),
+                  sources=np.where(src[R] > 0, m_src, 0).astype(np.int32),
+                  commit_lens=lens[R], destinations=np.where(src[R] > 0, m_src, 0).astype(np.int32),
+                  boundaries=m_bnd, boundary_lens=blen[R],
+                  record_rows=np.where(rows[R] >= 0, np.arange(nR), -1).astype(np.int32),
+                  lower_bound=W.LOWER_BOUND)
+    close = assert_bf16_close if bf16 else assert_f32_close
+    for j, b in enumerate(R):
+        if src[b] > 0:
+            close(f"max batch commit request {b}",
+                  host(d_state[int(src[b]) * page:(int(src[b]) + 1) * page]),
+                  mini[m_src[j] * page:(m_src[j] + 1) * page])
+        if m_bnd[j] > 0:
+            close(f"max batch commit request {b} boundary",
+                  host(d_state[int(bnd[b]) * page:(int(bnd[b]) + 1) * page]),
+                  mini[m_bnd[j] * page:(m_bnd[j] + 1) * page])
+    del d_state, before
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("pool", ["bf16", "f32"])
 def test_large_decode_ragged_windows_and_boundaries_sampled(pool):
     """The large decode shape (H=64, B=512, q=8) on a pool of 1040 slots (2 GiB
     BF16, 4 GiB FP32: the FP32 launch takes the streaming instance, whose S_n

@@ -48,6 +48,8 @@ def _run(cmd, verbose):
 VARIANTS = {
     # the verify kernel's row dots on plain FP32 FMAs instead of MFMA
     "valu_dots": ["-DKDA_VALU_DOTS=1"],
+    # the streaming FP32 commit's fold on plain FP32 FMAs instead of MFMA
+    "valu_fold": ["-DKDA_VALU_FOLD=1"],
 }
 
 

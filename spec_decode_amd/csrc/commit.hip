@@ -45,7 +45,18 @@
 // the MALL are about 5% slower with them.
 #include "kda_device.h"
 
+// A measurement variant, never built by default: with -DKDA_VALU_FOLD=1 the
+// streaming FP32 commit folds its tiles with plain FP32 FMAs, one token at a
+// time in the order of commit_kernel's fold (so its pages equal that kernel's
+// bit for bit), instead of on the matrix cores. It exists to time the MFMA
+// choice for this fold against the vector ALU on the same kernel.
+#ifndef KDA_VALU_FOLD
+#define KDA_VALU_FOLD 0
+#endif
+
 namespace kda {
+
+constexpr bool kValuFold = KDA_VALU_FOLD != 0;
 
 // Item of a workgroup and its admission (both kernels).
 struct CommitItem {
@@ -140,6 +151,36 @@ __device__ __forceinline__ void fold_tiles(u32x4 (&st)[2][8], const float (&ub)[
       if (mf1) s = __builtin_amdgcn_mfma_f32_16x16x4f32(ka1, ub[r][1], s, 0, 0, 0);
       st[r][cb] = __builtin_bit_cast(u32x4, s);
     }
+  }
+}
+
+// The measurement variant's fold of the same tiles on the vector ALU:
+// s <- s D + sum_{t0 <= t < t1} u_t kp_t element by element, one FMA per
+// token. uu[r][t] holds u_t at the lane's row of tile row r (zero past the
+// last folded token); the lane's 4 channels of tile cb are 16cb + 4(l/16)...
+template <int Q>
+__device__ __forceinline__ void fold_tiles_valu(u32x4 (&st)[2][8], const float (&uu)[2][Q],
+                                                const float* D, const float (*kp)[K], int t0,
+                                                int t1, int lane) {
+  const int c4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    const floatx4 dd = *reinterpret_cast<const floatx4*>(D + 16 * cb + c4);
+    floatx4 s0 = __builtin_bit_cast(floatx4, st[0][cb]) * dd;
+    floatx4 s1 = __builtin_bit_cast(floatx4, st[1][cb]) * dd;
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      if (t >= t0 && t < t1) {
+        const floatx4 k = *reinterpret_cast<const floatx4*>(&kp[t][16 * cb + c4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s0[e] = fmaf(uu[0][t], k[e], s0[e]);
+          s1[e] = fmaf(uu[1][t], k[e], s1[e]);
+        }
+      }
+    }
+    st[0][cb] = __builtin_bit_cast(u32x4, s0);
+    st[1][cb] = __builtin_bit_cast(u32x4, s1);
   }
 }
 
@@ -255,15 +296,29 @@ __global__ __launch_bounds__(256) void commit_f32_stream_kernel(const CommitPara
       ub[r][1] = 4 + lq < ne ? u_s[k1][vrow] : 0.f;
     }
   }
+  float uu[kValuFold ? 2 : 1][kValuFold ? Q : 1];
+  if constexpr (kValuFold) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int t = 0; t < Q; ++t)
+        uu[r][t] = t < ne ? u_s[t][32 * wave + 16 * r + (lane & 15)] : 0.f;
+  }
+  auto fold = [&](const float* D, const float (*kp)[K], int t0, int t1) {
+    if constexpr (kValuFold)
+      fold_tiles_valu<Q>(st, uu, D, kp, t0, t1, lane);
+    else
+      fold_tiles<Q>(st, ub, D, kp, t0, t1, lane);
+  };
   float* base = reinterpret_cast<float*>(L.state);
   if constexpr (ALIGN) {
     if (mm > 0) {
-      fold_tiles<Q>(st, ub, &dm_s[0], kpm_s, 0, mm, lane);
+      fold(&dm_s[0], kpm_s, 0, mm);
       store_tiles<CPOL_NT | CPOL_SC1>(
           st, base + (int64_t)it.bnd * L.state_stride + (int64_t)it.h * PAGE, wave, lane);
     }
   }
-  fold_tiles<Q>(st, ub, &dn_s[0], kp_s, mm, ne, lane);
+  fold(&dn_s[0], kp_s, mm, ne);
   store_tiles<CPOL_NT | CPOL_SC1>(
       st, base + (int64_t)it.dst * L.state_stride + (int64_t)it.h * PAGE, wave, lane);
 }

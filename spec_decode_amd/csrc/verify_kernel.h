@@ -398,11 +398,9 @@ __device__ __forceinline__ constexpr int chan0(int cb, int g) {
 template <int T, bool FUSED, bool GATED, bool SB16, int CONV, bool STREAM = false>
 __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   static_assert(FUSED || !CONV, "the convolution prologue is a fused-step prologue");
-  // Write-through stores (STREAM): the stock verify's o and records on either
-  // pool; the fused step's S_n, o and records on FP32 pools only (on BF16
-  // pools its streaming instance keeps plain stores and only loads with the
-  // no-reuse hint).
-  constexpr bool kWriteThrough = STREAM && !(FUSED && SB16);
+  // Write-through stores (STREAM): the stock verify's o and records, and the
+  // fused step's S_n, o and records, on either pool.
+  constexpr bool kWriteThrough = STREAM;
   // Contiguous no-reuse page loads through an LDS transpose: the streaming
   // instances over FP32 pages (fused step 0.812 -> 0.785 ms, stock verify
   // 0.507 -> 0.487 ms on the large decode batch).
@@ -1028,14 +1026,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 }
 
 // Launch of one fused instance: the streaming one when the grid's pages (batch
-// x heads pages of 64 or 32 KiB) exceed the MALL. Over FP32 pages it writes
-// through at two workgroups per CU: on the 2 GiB pool of the large decode
-// batch the step is 2.4% faster (the commit after it finds no dirty lines to
-// write back), while pages that fit in the MALL are best kept there. BF16
-// pages gain nothing from the write-through stores (the fused launch loses
-// what the commit gains, and at two workgroups per CU the step is 9% slower):
-// their streaming instance keeps plain stores at its natural occupancy and
-// only loads its inputs and old records with the no-reuse hint (1% faster).
+// x heads pages of 64 or 32 KiB) exceed the MALL. It writes through: on the
+// 2 GiB FP32 pool of the large decode batch the step is 2.4% faster (the
+// commit after it finds no dirty lines to write back), while pages that fit
+// in the MALL are best kept there. Over FP32 pages it runs at two workgroups
+// per CU; over BF16 pages at its natural four (two per CU made the step 9%
+// slower), where the write-through stores took the 1 GiB pool's step from
+// 0.879-0.885 to 0.858-0.861 ms (the fused launch 0.510-0.515 -> 0.497-0.500
+// ms, the commit after it 0.358-0.362 -> 0.352-0.353 ms).
 template <int TT, bool G, bool B, int MODE>
 hipError_t launch_fused_instance(const VerifyParams& p, dim3 grid, hipStream_t stream) {
   if (stream_pages((int64_t)grid.x * grid.y * PAGE * (B ? 2 : 4))) {

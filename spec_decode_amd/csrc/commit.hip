@@ -386,15 +386,17 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitParams p) {
   constexpr int PASSES = V / RPP;
 
   // Item order. Workgroups are dealt to the 8 XCDs round-robin by linear
-  // index; the streaming instances remap that index so that XCD x takes the
-  // x-th eighth of the layer's (head, request) items, i.e. whole requests'
-  // pages in turn, instead of every eighth head of the requests in flight
-  // (8-layer BF16 align 1.050 -> 0.975 ms, the FP32 large decode flush on
-  // this kernel 0.662 -> 0.650 ms; the 1 GiB BF16 in-place commit 0.347 ->
-  // 0.357 ms). Unsigned: heads x batch reaches 65535^2, above INT_MAX but
-  // below 2^32.
+  // index; the streaming align instances remap that index so that XCD x
+  // takes the x-th eighth of the layer's (head, request) items, i.e. whole
+  // requests' pages in turn, instead of every eighth head of the requests in
+  // flight: the 8-layer BF16 align commit 1.050 -> 0.975 ms (1.045 against
+  // 0.975 ms when re-measured). Commits without boundaries keep the launch
+  // order, as the fused step does: the 1 GiB BF16 in-place flush after the
+  // fused step took 0.351-0.352 ms with the remap against 0.337-0.339 ms
+  // without. Unsigned: heads x batch reaches 65535^2, above INT_MAX but below
+  // 2^32.
   uint32_t lin = blockIdx.x + blockIdx.y * gridDim.x;
-  if constexpr (STREAM) {
+  if constexpr (STREAM && ALIGN) {
     const uint32_t per_layer = gridDim.x * gridDim.y;
     if ((per_layer & 7u) == 0) lin = (lin & 7u) * (per_layer >> 3) + (lin >> 3);
   }
